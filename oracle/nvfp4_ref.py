@@ -1,0 +1,261 @@
+"""CPU oracle for NVFP4 W4A4: quantize, dequantize, block-scaled GEMM, fused segments.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The GPU library
+(``nvfp4_w4a4_block_amd``) never imports it, shares no code, tables or constants with it,
+and must fail loudly rather than fall back to it.
+
+It is written for being checked by eye, not for speed: plain numpy steps in the order the
+format defines them, float32 where the format's arithmetic is binary32, float64 for the
+GEMM.
+
+Sources (the pages this follows):
+  * "NVFP4 W4A4 Quantization Compresses 27B Hybrid Models" (thevalue.engineering), section
+    "Challenging the Recurrence Fragility Assumption": NVFP4 = E2M1 4-bit element values
+    with one E4M3 scale per 16-element block.
+  * "Why Gated DeltaNet Survives 4-Bit Quantization" (kipquest paper page), "The deep dive":
+    four-bit storage with one shared scale per sixteen-element block; W4A4 (weights and
+    activations both four-bit) on every linear layer; block scaling confines an outlier to
+    its own block of sixteen.
+  * The paper abstract (Lattice and kipquest pages): the global-scale mismatch that appears
+    when per-module-calibrated NVFP4 checkpoints are served by kernels that fuse modules
+    into one GEMM, which the authors repair.  A per-module global scale is therefore part
+    of the format; each fused segment keeps its own.
+
+Readings where the pages are silent (each is listed with its justification in the design
+notes of this repository):
+  R1 E2M1 magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}; code = sign<<3 | magnitude index.
+  R2 E4M3 is the OCP E4M3FN byte (bias 7, no infinities, 0x7F/0xFF NaN, max 448).
+  R3 Global scale s_g = fl32(amax / 2688), 2688 = 6 * 448 (largest E2M1 times largest E4M3),
+     applied as a multiplier on dequantization.  Modes: one per tensor, one per row, or
+     given by the caller.
+  R4 Block scale byte s_j = E4M3_RNE_SAT(fl32(a_j / fl32(6 * s_g))), a_j = block max |x|.
+  R5 Element: d_j = fl32(E4M3(s_j) * s_g); magnitude = E2M1_RNE_SAT(fl32(|x| / d_j)), or 0
+     when d_j == 0; the sign bit is copied from x (so -0 and small negatives give code 8).
+  R6 Ties go to the even code/byte (round to nearest even) in both E2M1 and E4M3; anything
+     above the largest value saturates to it (6 for E2M1, 448 for E4M3).
+  R7 Packing: two codes per byte, even column in the low nibble; scales one byte per block,
+     row-major; both GEMM operands K-major (Y = A . W^T).
+  R8 Dequantized value = E2M1(code) * E4M3(s_j) * s_g (exact in float64).
+  R9 A tensor (per-tensor mode) or row (per-row mode) holding a NaN or an infinity has a
+     non-finite global scale; its codes and scales are unspecified and not compared.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+F32 = np.float32
+F64 = np.float64
+
+BLOCK = 16                         # elements per E4M3 block scale (R7, deep dive)
+E2M1_MAX = 6.0                     # largest E2M1 magnitude (R1)
+E4M3_MAX = 448.0                   # largest finite E4M3FN value (R2)
+GLOBAL_DIVISOR = F32(E2M1_MAX * E4M3_MAX)   # 2688 (R3)
+
+PER_TENSOR = "per_tensor"
+PER_ROW = "per_row"
+GIVEN = "given"
+
+# R1: the eight E2M1 magnitudes, indexed by the 3-bit magnitude field.
+E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=F64)
+
+_CHUNK = 1 << 22
+
+
+# ------------------------------------------------------------------------------ E2M1
+
+def e2m1_decode(codes) -> np.ndarray:
+    """Value of each 4-bit code (float64): sign bit 3, magnitude index bits 0..2 (R1)."""
+    c = np.asarray(codes).astype(np.int64)
+    mag = E2M1_MAGNITUDES[c & 7]
+    return np.where((c & 8) != 0, -mag, mag)
+
+
+def e2m1_rne_sat(v) -> np.ndarray:
+    """Magnitude index (0..7) of the E2M1 value nearest to v >= 0; ties to the even index,
+    values above 6 saturate to 6 (R6).  v is float32 (or anything exactly float64)."""
+    v = np.asarray(v, dtype=F64)
+    flat = v.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.int64)
+    for s in range(0, flat.size, _CHUNK):
+        c = flat[s:s + _CHUNK]
+        dist = np.abs(c[:, None] - E2M1_MAGNITUDES[None, :])   # exact for float32 inputs
+        best = dist.min(axis=1, keepdims=True)
+        at_min = dist == best
+        first = np.argmax(at_min, axis=1)                      # lowest nearest index
+        nxt = np.minimum(first + 1, 7)
+        tie = at_min[np.arange(c.size), nxt] & (nxt != first)
+        # A tie is between two neighbouring indices; keep the even one.
+        idx = np.where(tie & (first % 2 == 1), nxt, first)
+        idx = np.where(c >= E2M1_MAX, 7, idx)                  # includes +inf
+        out[s:s + c.size] = idx
+    return out.reshape(v.shape)
+
+
+# ------------------------------------------------------------------------------ E4M3
+
+def e4m3_decode(b) -> np.ndarray:
+    """Value of each E4M3FN byte (float64): sign bit 7, exponent bits 3..6 (bias 7),
+    mantissa bits 0..2; exponent 0 is subnormal (m * 2^-9); 0x7F and 0xFF are NaN (R2)."""
+    b = np.asarray(b).astype(np.int64)
+    e = (b >> 3) & 15
+    m = b & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2((e - 7).astype(F64)))
+    mag = np.where((b & 0x7F) == 0x7F, np.nan, mag)
+    return np.where((b & 0x80) != 0, -mag, mag)
+
+
+# Non-negative finite E4M3 values; position in this table equals the byte (0x00..0x7E),
+# and the table is increasing.
+E4M3_TABLE = e4m3_decode(np.arange(0x7F))
+
+
+def e4m3_rne_sat(t) -> np.ndarray:
+    """Byte of the E4M3 value nearest to t >= 0; ties to the even byte (even mantissa);
+    t above 448 (including +inf) saturates to 448 = 0x7E (R4, R6)."""
+    t = np.asarray(t, dtype=F64)
+    flat = t.reshape(-1)
+    i = np.searchsorted(E4M3_TABLE, flat, side="right") - 1     # largest value <= t
+    i = np.clip(i, 0, 0x7E)
+    j = np.minimum(i + 1, 0x7E)
+    lo = E4M3_TABLE[i]
+    hi = E4M3_TABLE[j]
+    d_lo = flat - lo        # exact: lo <= t and t, lo are within a factor of two or lo = 0
+    d_hi = hi - flat
+    up = (j != i) & ((d_hi < d_lo) | ((d_hi == d_lo) & (j % 2 == 0)))
+    out = np.where(up, j, i)
+    out = np.where(flat >= E4M3_MAX, 0x7E, out)
+    return out.reshape(t.shape).astype(np.uint8)
+
+
+# ------------------------------------------------------------------------------ tensors
+
+@dataclass
+class NVFP4:
+    """An NVFP4 tensor: codes [R, C/2] (two per byte, even column low), E4M3 block scales
+    [R, C/16], float32 global scale of shape (1,) or (R,), logical shape (R, C)."""
+    codes: np.ndarray
+    scales: np.ndarray
+    global_scale: np.ndarray
+    rows: int
+    cols: int
+    nonfinite: bool = False
+
+    def global_per_row(self) -> np.ndarray:
+        g = np.asarray(self.global_scale, dtype=F32).reshape(-1)
+        return np.broadcast_to(g if g.size == self.rows else g[:1], (self.rows,))
+
+
+def unpack_codes(codes: np.ndarray) -> np.ndarray:
+    """[R, C/2] bytes -> [R, C] 4-bit codes (R7: even column from the low nibble)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    out = np.empty((codes.shape[0], codes.shape[1] * 2), dtype=np.uint8)
+    out[:, 0::2] = codes & 0x0F
+    out[:, 1::2] = codes >> 4
+    return out
+
+
+def pack_codes(code: np.ndarray) -> np.ndarray:
+    """[R, C] 4-bit codes -> [R, C/2] bytes (R7)."""
+    code = np.asarray(code, dtype=np.uint8)
+    return (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+
+
+def global_scale(x: np.ndarray, mode: str, given: float | None = None) -> np.ndarray:
+    """R3: s_g = fl32(amax / 2688) over the tensor or each row, or the caller's value."""
+    ax = np.abs(np.asarray(x, dtype=F32))
+    if mode == PER_TENSOR:
+        amax = ax.max() if ax.size else F32(0)
+        return (np.asarray([amax], dtype=F32) / GLOBAL_DIVISOR).astype(F32)
+    if mode == PER_ROW:
+        amax = ax.max(axis=1) if ax.shape[1] else np.zeros(ax.shape[0], F32)
+        return (amax.astype(F32) / GLOBAL_DIVISOR).astype(F32)
+    if mode == GIVEN:
+        return np.asarray([given], dtype=F32)
+    raise ValueError(f"unknown mode {mode!r}")
+
+
+def quantize(x, mode: str = PER_TENSOR, given: float | None = None) -> NVFP4:
+    """Quantize X[R, C] (float32 values; bf16 inputs widened exactly) to NVFP4.
+
+    Steps R3-R7 in order; all element arithmetic is binary32 with round-to-nearest-even.
+    """
+    x = np.ascontiguousarray(x, dtype=F32)
+    if x.ndim != 2:
+        raise ValueError("x must be 2-D")
+    R, C = x.shape
+    if C % BLOCK:
+        raise ValueError("cols must be a multiple of 16")
+    nonfinite = not bool(np.isfinite(x).all())
+    sg = global_scale(x, mode, given)                                   # (1,) or (R,)
+    sg_row = np.broadcast_to(sg if sg.size == R else sg[:1], (R,)).astype(F32)[:, None]
+
+    ax = np.abs(x).reshape(R, C // BLOCK, BLOCK)
+    a = ax.max(axis=2) if C else np.zeros((R, 0), F32)                  # block max |x|
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore", under="ignore"):
+        den = (F32(E2M1_MAX) * sg_row).astype(F32)                      # fl32(6 * s_g)
+        t = (a / den).astype(F32)                                       # fl32(a_j / den)
+        s = e4m3_rne_sat(np.where(np.isnan(t), 0.0, t))
+        s = np.where(sg_row == 0, 0, s).astype(np.uint8)                # zero tensor/row
+        d = (e4m3_decode(s).astype(F32) * sg_row).astype(F32)           # fl32(E4M3(s) * s_g)
+        q = (ax / d[:, :, None]).astype(F32)                            # fl32(|x| / d_j)
+    mag = e2m1_rne_sat(np.where(np.isnan(q), 0.0, q))
+    mag = np.where(d[:, :, None] == 0, 0, mag).reshape(R, C)
+    sign = np.signbit(x).astype(np.int64)
+    code = ((sign << 3) | mag).astype(np.uint8)
+    return NVFP4(pack_codes(code), s, sg.astype(F32), R, C, nonfinite)
+
+
+def dequantize(t: NVFP4, rows=None) -> np.ndarray:
+    """R8: float64 values E2M1(code) * E4M3(scale) * s_g (exact), optionally for a subset
+    of rows."""
+    codes, scales, g = t.codes, t.scales, t.global_per_row()
+    if rows is not None:
+        rows = np.asarray(rows)
+        codes, scales, g = codes[rows], scales[rows], g[rows]
+    v = e2m1_decode(unpack_codes(codes))
+    s = np.repeat(e4m3_decode(scales), BLOCK, axis=1)
+    return v * s * g.astype(F64)[:, None]
+
+
+def dequantize_f32(t: NVFP4) -> np.ndarray:
+    """Binary32 dequantization fl32(E2M1 * fl32(E4M3 * s_g)), used to re-quantize."""
+    v = e2m1_decode(unpack_codes(t.codes)).astype(F32)
+    g = t.global_per_row().astype(F32)[:, None]
+    d = (e4m3_decode(t.scales).astype(F32) * g).astype(F32)
+    return (v * np.repeat(d, BLOCK, axis=1)).astype(F32)
+
+
+# ------------------------------------------------------------------------------ GEMM
+
+def gemm(a: NVFP4, w: NVFP4, a_rows=None):
+    """Y[m, n] = sum_k A^[m, k] * W^[n, k] in float64 (Y = A^ . W^T), and the tolerance scale
+    T[m, n] = sum_k |A^[m, k] * W^[n, k]|.  A^ and W^ are the exact dequantized operands
+    (global scales included).  ``a_rows`` restricts to a subset of output rows."""
+    if a.cols != w.cols:
+        raise ValueError("K mismatch")
+    A = dequantize(a, a_rows)
+    W = dequantize(w)
+    return A @ W.T, np.abs(A) @ np.abs(W).T
+
+
+def fused_segments(a: NVFP4, segments: list[NVFP4], a_rows=None):
+    """The repaired fused GEMM: output columns of segment i are A^ . W_i^T with W_i
+    dequantized under its own global scale; segments are concatenated along N."""
+    ys, ts = zip(*(gemm(a, w, a_rows) for w in segments))
+    return np.concatenate(ys, axis=1), np.concatenate(ts, axis=1)
+
+
+def fused_shared_scale(a: NVFP4, segments: list[NVFP4], shared: float, a_rows=None):
+    """The global-scale mismatch (negative control): the fused launch dequantizes every
+    segment's codes and block scales with one shared global scale instead of its own."""
+    relabeled = [NVFP4(w.codes, w.scales, np.asarray([shared], F32), w.rows, w.cols)
+                 for w in segments]
+    return fused_segments(a, relabeled, a_rows)
+
+
+def nvfp4_bytes(rows: int, cols: int, global_scales: int = 1) -> int:
+    """Storage of one NVFP4 tensor: 4-bit codes + one byte per 16 elements + fp32 scales."""
+    return rows * cols // 2 + rows * cols // BLOCK + 4 * global_scales
