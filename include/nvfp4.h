@@ -1,0 +1,145 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 W4A4 library.
+ *
+ * The library implements the data-parallel hot path of NVFP4 W4A4 inference of linear
+ * layers:
+ *   1. activation quantization: per 16-element block a max-abs, an E4M3 block scale under
+ *      an FP32 global scale, round-to-nearest-even to E2M1 codes packed two per byte;
+ *   2. the block-scaled 4-bit x 4-bit GEMM Y = A . W^T with FP32 accumulation;
+ *   3. the fused-module GEMM in which several separately calibrated modules share one
+ *      launch and each column segment keeps its own weight global scale (the repair of the
+ *      global-scale mismatch).
+ *
+ * Sources: the element format (E2M1 values, one E4M3 scale per 16-element block) is from
+ * "NVFP4 W4A4 Quantization Compresses 27B Hybrid Models" (thevalue.engineering), section
+ * "Challenging the Recurrence Fragility Assumption"; W4A4 on every linear layer and the
+ * 16-element block from "Why Gated DeltaNet Survives 4-Bit Quantization" (kipquest),
+ * "The deep dive"; the global-scale mismatch between per-module-calibrated checkpoints and
+ * fused-module GEMM kernels, and its repair, from the paper's abstract (Lattice and
+ * kipquest pages).
+ *
+ * Data format (identical for activations and weights):
+ *   codes [rows, cols/2]  uint8, row-major, contiguous; two 4-bit E2M1 codes per byte, the
+ *                         even column in the low nibble.  Code = sign<<3 | magnitude index,
+ *                         magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+ *   scales [rows, cols/16] uint8, row-major, contiguous; OCP E4M3FN bytes (bias 7,
+ *                         max 448, never NaN), one per 16 consecutive elements of a row.
+ *   global scale          float32 on the device: one per tensor, or one per row.
+ *   value = E2M1(code) * E4M3(scale) * global_scale.
+ *   The dynamic global scale is s_g = fl32(max|x| / 2688), 2688 = 6 * 448.
+ *
+ * Conventions of every entry point:
+ *   * Pointers are DEVICE pointers unless marked (host).  The caller owns all memory; the
+ *     library never allocates device memory, never synchronises and keeps no state.
+ *   * Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = default stream)
+ *     and is stream-ordered; the global scales never travel to the host.
+ *   * Return value: an nvfp4_status.  Argument errors are detected on the host before any
+ *     launch and leave every output untouched.  A failed launch returns NVFP4_ERR_HIP.
+ *   * Non-finite input is reported in band: the affected global scale (of the tensor, or of
+ *     the row in per-row mode) becomes NaN or infinite and the codes and scales it governs
+ *     are unspecified.
+ *   * Calls on different streams may run concurrently if their outputs and workspaces do
+ *     not overlap.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad enum */
+  NVFP4_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. too many segments) */
+  NVFP4_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace_size */
+  NVFP4_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} nvfp4_status;
+
+typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype;
+
+typedef enum {
+  NVFP4_SCALE_PER_TENSOR = 0, /* s_g = max|x| over the tensor / 2688, written to [1]    */
+  NVFP4_SCALE_PER_ROW = 1,    /* s_g[r] = max|x[r,:]| / 2688, written to [rows]         */
+  NVFP4_SCALE_GIVEN = 2       /* s_g read from global_scale[0] (a calibrated scale)     */
+} nvfp4_scale_mode;
+
+#define NVFP4_MAX_SEGMENTS 64
+
+/*
+ * Quantize X[rows, cols] to NVFP4 (format above).
+ *   x             [rows, ldx] of x_dtype (NVFP4_BF16 or NVFP4_F32); 16-byte aligned, and
+ *                 ldx * element size a multiple of 16 bytes; ldx >= cols.
+ *   rows >= 0     rows == 0 is a no-op except that PER_TENSOR writes s_g = 0.
+ *   cols > 0      multiple of 16.
+ *   codes         out [rows, cols/2], 8-byte aligned.
+ *   scales        out [rows, cols/16].
+ *   global_scale  PER_TENSOR: out [1]; PER_ROW: out [rows]; GIVEN: in [1].  A given scale
+ *                 must be finite and > 0 (otherwise the output is unspecified); a zero
+ *                 scale (all-zero input) gives all-zero scale bytes and sign-only codes.
+ *   workspace     device scratch of nvfp4_quantize_workspace_size() bytes (may be NULL if
+ *                 that is 0); contents need no initialisation and are clobbered.
+ * Follows: block max -> E4M3 scale -> E2M1 round-to-nearest-even, two codes per byte.
+ */
+int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                   uint8_t* codes, uint8_t* scales, float* global_scale, int mode,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols, int mode);
+
+/*
+ * Y[M, N] = A . W^T with A = NVFP4 [M, K] activations and W = NVFP4 [N, K] weights, both
+ * K-major; FP32 accumulation of the exactly dequantized operands, then
+ * y = (acc * a_global[m or 0]) * w_global[0], stored as y_dtype (bf16: round to nearest
+ * even).
+ *   M >= 0, N >= 0 (zero is a no-op), K > 0 and a multiple of 16.
+ *   a_codes/w_codes 16-byte aligned.
+ *   a_global      device [1] (a_global_per_row == 0) or [M] (== 1).
+ *   w_global      device [1].
+ *   y             [M, ldy] of y_dtype, ldy >= N.
+ *   workspace     nvfp4_gemm_workspace_size(M, N, K) bytes (may be NULL if 0).
+ */
+int nvfp4_gemm(int64_t M, int64_t N, int64_t K,
+               const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+               int a_global_per_row,
+               const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+               void* y, int y_dtype, int64_t ldy,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The fused-module GEMM: W is the concatenation along N of num_segments separately
+ * quantized modules (codes [sum N_i, K/2], scales [sum N_i, K/16]); output column n of
+ * segment i is scaled by that module's own global scale w_globals[i]:
+ *   Y[:, off_i : off_i + N_i] = A . W_i^T,  off_i = N_0 + ... + N_{i-1}.
+ * One launch; one shared activation quantization.  This is the repair of the global-scale
+ * mismatch: a kernel that applied one scale to every segment would mis-scale segment i by
+ * w_globals[0] / w_globals[i].
+ *   1 <= num_segments <= NVFP4_MAX_SEGMENTS; seg_n (host) widths, each > 0.
+ *   w_globals     device [num_segments].
+ *   Other arguments as in nvfp4_gemm, with N = sum of seg_n.
+ */
+int nvfp4_gemm_fused_segments(int64_t M, int64_t K,
+                              const uint8_t* a_codes, const uint8_t* a_scales,
+                              const float* a_global, int a_global_per_row,
+                              int num_segments, const int64_t* seg_n,
+                              const uint8_t* w_codes, const uint8_t* w_scales,
+                              const float* w_globals,
+                              void* y, int y_dtype, int64_t ldy,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* Static description of a status code. */
+const char* nvfp4_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int nvfp4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

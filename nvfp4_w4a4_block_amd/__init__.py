@@ -1,0 +1,198 @@
+"""Python binding of the MI355X NVFP4 W4A4 library (``libnvfp4.so``, C ABI in
+``include/nvfp4.h``).
+
+Argument marshalling only: every step of quantization and GEMM runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream.  If the library is not
+built this module raises ImportError; there is no fallback implementation.
+
+Entry points (same names as the C ABI):
+  quantize(x, mode)                      -> NVFP4Tensor (codes, scales, global_scale)
+  gemm(a, w, out_dtype)                  -> Y = A . W^T
+  gemm_fused_segments(a, w, widths, w_globals, out_dtype)
+                                         -> Y with one weight global scale per segment
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Sequence
+
+import torch
+
+__all__ = [
+    "NVFP4Tensor", "NVFP4Error", "quantize", "gemm", "gemm_fused_segments", "library_path", "lib",
+    "PER_TENSOR", "PER_ROW", "GIVEN", "MAX_SEGMENTS", "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+PER_TENSOR, PER_ROW, GIVEN = 0, 1, 2
+_MODES = {"per_tensor": PER_TENSOR, "per_row": PER_ROW, "given": GIVEN}
+_F32, _BF16 = 0, 1
+MAX_SEGMENTS = 64
+EXPORTED_SYMBOLS = (
+    "nvfp4_quantize", "nvfp4_quantize_workspace_size", "nvfp4_gemm", "nvfp4_gemm_fused_segments",
+    "nvfp4_gemm_workspace_size", "nvfp4_status_string", "nvfp4_version",
+)
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run `python -m nvfp4_w4a4_block_amd.build`")
+    L = ctypes.CDLL(_LIB_PATH)
+    p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.nvfp4_quantize.argtypes = [p, i32, i64, i64, i64, p, p, p, i32, p, sz, p]
+    L.nvfp4_quantize.restype = i32
+    L.nvfp4_quantize_workspace_size.argtypes = [i64, i64, i32]
+    L.nvfp4_quantize_workspace_size.restype = sz
+    L.nvfp4_gemm.argtypes = [i64, i64, i64, p, p, p, i32, p, p, p, p, i32, i64, p, sz, p]
+    L.nvfp4_gemm.restype = i32
+    L.nvfp4_gemm_fused_segments.argtypes = [i64, i64, p, p, p, i32, i32, p, p, p, p, p, i32, i64, p, sz, p]
+    L.nvfp4_gemm_fused_segments.restype = i32
+    L.nvfp4_gemm_workspace_size.argtypes = [i64, i64, i64]
+    L.nvfp4_gemm_workspace_size.restype = sz
+    L.nvfp4_status_string.argtypes = [i32]
+    L.nvfp4_status_string.restype = ctypes.c_char_p
+    L.nvfp4_version.argtypes = []
+    L.nvfp4_version.restype = i32
+    return L
+
+
+lib = _load()
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lib.nvfp4_status_string(status).decode()} (status {status})")
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise NVFP4Error(status, what)
+
+
+@dataclass
+class NVFP4Tensor:
+    """codes uint8 [rows, cols/2], scales uint8 [rows, cols/16], global_scale float32 [1] or
+    [rows], all on one GPU."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    global_scale: torch.Tensor
+
+    @property
+    def rows(self) -> int:
+        return self.codes.shape[0]
+
+    @property
+    def cols(self) -> int:
+        return self.codes.shape[1] * 2
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _require(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def quantize(x: torch.Tensor, mode: str = "per_tensor", global_scale: torch.Tensor | None = None,
+             out: NVFP4Tensor | None = None) -> NVFP4Tensor:
+    """Quantize a 2-D bf16/fp32 CUDA tensor (row stride may exceed its width) to NVFP4.
+
+    mode: "per_tensor" | "per_row" | "given" (then ``global_scale`` is a float32 CUDA tensor
+    of one element)."""
+    _require(x.is_cuda and x.dim() == 2, "x must be a 2-D GPU tensor")
+    _require(x.dtype in (torch.bfloat16, torch.float32), "x must be bf16 or fp32")
+    _require(x.stride(1) == 1, "x must be row-contiguous")
+    m = _MODES[mode]
+    rows, cols = x.shape
+    dev = x.device
+    if out is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+        if m == GIVEN:
+            _require(global_scale is not None, "given mode needs global_scale")
+            g = global_scale
+        else:
+            g = torch.empty((rows if m == PER_ROW else 1,), dtype=torch.float32, device=dev)
+        out = NVFP4Tensor(codes, scales, g)
+    elif m == GIVEN and global_scale is not None:
+        out.global_scale = global_scale
+    _require(out.global_scale.dtype == torch.float32 and out.global_scale.is_cuda, "global scale: fp32 GPU")
+    ws_bytes = lib.nvfp4_quantize_workspace_size(rows, cols, m)
+    ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev) if ws_bytes else None
+    ldx = x.stride(0) if rows > 1 else max(x.stride(0), cols)
+    st = lib.nvfp4_quantize(_ptr(x), _BF16 if x.dtype == torch.bfloat16 else _F32, rows, cols, ldx,
+                            _ptr(out.codes), _ptr(out.scales), _ptr(out.global_scale), m,
+                            _ptr(ws), ws_bytes, _stream(dev))
+    _check(st, "nvfp4_quantize")
+    return out
+
+
+def _out_tensor(M: int, N: int, dtype: torch.dtype, dev, out: torch.Tensor | None) -> torch.Tensor:
+    if out is None:
+        return torch.empty((M, N), dtype=dtype, device=dev)
+    _require(out.shape == (M, N) and out.dtype == dtype and out.stride(1) == 1, "bad out tensor")
+    return out
+
+
+def _y_dtype(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return _BF16
+    _require(dtype == torch.float32, "out_dtype must be bfloat16 or float32")
+    return _F32
+
+
+def gemm(a: NVFP4Tensor, w: NVFP4Tensor, out_dtype: torch.dtype = torch.bfloat16,
+         out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y[M, N] = A . W^T for NVFP4 A [M, K] and W [N, K]."""
+    _require(a.cols == w.cols, "K mismatch")
+    _require(w.global_scale.numel() == 1, "W must have one global scale")
+    M, N, K = a.rows, w.rows, a.cols
+    dev = a.codes.device
+    y = _out_tensor(M, N, out_dtype, dev, out)
+    per_row = int(a.global_scale.numel() == M and M != 1)
+    ws_bytes = lib.nvfp4_gemm_workspace_size(M, N, K)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev) if ws_bytes else None
+    st = lib.nvfp4_gemm(M, N, K, _ptr(a.codes), _ptr(a.scales), _ptr(a.global_scale), per_row,
+                        _ptr(w.codes), _ptr(w.scales), _ptr(w.global_scale), _ptr(y), _y_dtype(out_dtype),
+                        y.stride(0) if M > 0 else N, _ptr(ws), ws_bytes, _stream(dev))
+    _check(st, "nvfp4_gemm")
+    return y
+
+
+def gemm_fused_segments(a: NVFP4Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
+                        seg_widths: Sequence[int], w_globals: torch.Tensor,
+                        out_dtype: torch.dtype = torch.bfloat16,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """Fused-module GEMM: W = concatenation (along N) of len(seg_widths) modules, each with its
+    own global scale w_globals[i] (fp32 GPU tensor)."""
+    M, K = a.rows, a.cols
+    N = int(sum(seg_widths))
+    _require(w_codes.shape == (N, K // 2) and w_scales.shape == (N, K // 16), "bad fused weight shapes")
+    dev = a.codes.device
+    y = _out_tensor(M, N, out_dtype, dev, out)
+    per_row = int(a.global_scale.numel() == M and M != 1)
+    widths = (ctypes.c_int64 * len(seg_widths))(*[int(v) for v in seg_widths])
+    ws_bytes = lib.nvfp4_gemm_workspace_size(M, N, K)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev) if ws_bytes else None
+    st = lib.nvfp4_gemm_fused_segments(M, K, _ptr(a.codes), _ptr(a.scales), _ptr(a.global_scale), per_row,
+                                       len(seg_widths), ctypes.cast(widths, ctypes.c_void_p),
+                                       _ptr(w_codes), _ptr(w_scales), _ptr(w_globals), _ptr(y),
+                                       _y_dtype(out_dtype), y.stride(0) if M > 0 else N, _ptr(ws), ws_bytes,
+                                       _stream(dev))
+    _check(st, "nvfp4_gemm_fused_segments")
+    return y

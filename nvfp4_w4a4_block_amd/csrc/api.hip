@@ -1,0 +1,121 @@
+// C ABI of the NVFP4 W4A4 library: argument validation and dispatch to the kernels.
+// Every argument error is detected here, on the host, before anything is enqueued.
+#include <stdint.h>
+
+#include "nvfp4_internal.h"
+
+using namespace nvfp4;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_gemm_common(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+                      const float* a_global, int a_global_per_row, const uint8_t* w_codes,
+                      const uint8_t* w_scales, const void* y, int y_dtype, int64_t ldy) {
+  if (M < 0 || N < 0 || K <= 0 || K % 16 != 0) return NVFP4_ERR_INVALID_ARG;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return NVFP4_ERR_UNSUPPORTED;
+  if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_ERR_INVALID_ARG;
+  if (a_global_per_row != 0 && a_global_per_row != 1) return NVFP4_ERR_INVALID_ARG;
+  if (ldy < N) return NVFP4_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (!a_codes || !a_scales || !a_global || !w_codes || !w_scales || !y) return NVFP4_ERR_INVALID_ARG;
+  if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_global, 4)) return NVFP4_ERR_INVALID_ARG;
+  if (!aligned(y, y_dtype == NVFP4_F32 ? 4 : 2)) return NVFP4_ERR_INVALID_ARG;
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_INVALID_ARG: return "invalid argument";
+    case NVFP4_ERR_UNSUPPORTED: return "unsupported configuration";
+    case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
+    case NVFP4_ERR_HIP: return "HIP runtime or launch failure";
+    default: return "unknown status";
+  }
+}
+
+int nvfp4_version(void) { return 100; }
+
+size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols, int mode) {
+  if (rows < 0 || cols <= 0) return 0;
+  return quantize_workspace_bytes(rows, cols, mode);
+}
+
+int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, uint8_t* codes,
+                   uint8_t* scales, float* global_scale, int mode, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  if (x_dtype != NVFP4_BF16 && x_dtype != NVFP4_F32) return NVFP4_ERR_INVALID_ARG;
+  if (mode != NVFP4_SCALE_PER_TENSOR && mode != NVFP4_SCALE_PER_ROW && mode != NVFP4_SCALE_GIVEN)
+    return NVFP4_ERR_INVALID_ARG;
+  if (rows < 0 || cols <= 0 || cols % 16 != 0 || ldx < cols) return NVFP4_ERR_INVALID_ARG;
+  if ((uint64_t)rows * (uint64_t)(cols / 16) >= (1ull << 31)) return NVFP4_ERR_UNSUPPORTED;
+  if ((rows > 0 || mode == NVFP4_SCALE_PER_TENSOR) && (!global_scale || !aligned(global_scale, 4)))
+    return NVFP4_ERR_INVALID_ARG;
+  const int64_t esize = x_dtype == NVFP4_BF16 ? 2 : 4;
+  if (rows > 0) {
+    if (!x || !codes || !scales) return NVFP4_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || (ldx * esize) % 16 != 0 || !aligned(codes, 8)) return NVFP4_ERR_INVALID_ARG;
+  }
+  const size_t need = quantize_workspace_bytes(rows, cols, mode);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 4))) return NVFP4_ERR_WORKSPACE;
+  return launch_quantize(x, x_dtype, rows, cols, ldx, codes, scales, global_scale, mode, workspace,
+                         static_cast<hipStream_t>(stream));
+}
+
+size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K <= 0) return 0;
+  return gemm_workspace_bytes(M, N, K);
+}
+
+int nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+               const float* a_global, int a_global_per_row, const uint8_t* w_codes, const uint8_t* w_scales,
+               const float* w_global, void* y, int y_dtype, int64_t ldy, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  int st = check_gemm_common(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales, y,
+                             y_dtype, ldy);
+  if (st != NVFP4_OK || M == 0 || N == 0) return st;
+  if (!w_global || !aligned(w_global, 4)) return NVFP4_ERR_INVALID_ARG;
+  const size_t need = gemm_workspace_bytes(M, N, K);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_ERR_WORKSPACE;
+  SegmentTable seg{};
+  seg.count = 1;
+  seg.bound[0] = 0;
+  seg.bound[1] = (int32_t)N;
+  return launch_gemm(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales, w_global, seg,
+                     y, y_dtype, ldy, workspace, static_cast<hipStream_t>(stream));
+}
+
+int nvfp4_gemm_fused_segments(int64_t M, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+                              const float* a_global, int a_global_per_row, int num_segments,
+                              const int64_t* seg_n, const uint8_t* w_codes, const uint8_t* w_scales,
+                              const float* w_globals, void* y, int y_dtype, int64_t ldy, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (num_segments < 1 || !seg_n) return NVFP4_ERR_INVALID_ARG;
+  if (num_segments > NVFP4_MAX_SEGMENTS) return NVFP4_ERR_UNSUPPORTED;
+  SegmentTable seg{};
+  seg.count = num_segments;
+  int64_t N = 0;
+  for (int i = 0; i < num_segments; ++i) {
+    if (seg_n[i] <= 0) return NVFP4_ERR_INVALID_ARG;
+    seg.bound[i] = (int32_t)N;
+    N += seg_n[i];
+    if (N > INT32_MAX) return NVFP4_ERR_UNSUPPORTED;
+  }
+  seg.bound[num_segments] = (int32_t)N;
+  int st = check_gemm_common(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales, y,
+                             y_dtype, ldy);
+  if (st != NVFP4_OK || M == 0) return st;
+  if (!w_globals || !aligned(w_globals, 4)) return NVFP4_ERR_INVALID_ARG;
+  const size_t need = gemm_workspace_bytes(M, N, K);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_ERR_WORKSPACE;
+  return launch_gemm(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales, w_globals, seg,
+                     y, y_dtype, ldy, workspace, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,357 @@
+// Block-scaled NVFP4 x NVFP4 GEMM for gfx950: Y[M, N] = A . W^T, FP32 accumulation.
+//
+// What is computed (W4A4, "Why Gated DeltaNet Survives 4-Bit Quantization", "The deep
+// dive"; the fused-module global-scale repair, paper abstract):
+//   Y[m, n] = s_gA[m or 0] * s_gW[seg(n)] * sum_k (E2M1(a_mk) E4M3(sa_m,k/16)) (E2M1(w_nk) E4M3(sw_n,k/16))
+// where seg(n) is the fused segment holding column n.
+//
+// Design (gfx950):
+//  * Each E2M1 x E4M3 product has at most 6 significant bits and lies in [2^-10, 2688], so
+//    it is exact in fp16; operands are dequantized exactly in registers and fed to the fp16
+//    MFMA, whose products are exact in fp32.  Only the fp32 accumulation rounds.  The
+//    global scales stay out of the operands and are applied in the epilogue, per row of A
+//    and per column segment of W.
+//  * Prefill kernel: 256 x 256 output tile per 256-thread workgroup (4 wavefronts, each a
+//    128 x 128 sub-tile of 4 x 4 MFMA 32x32x16 tiles), K step 128.  Packed codes (64 B per
+//    row per step) and scale bytes are staged in LDS, double-buffered; each lane reads 16 B
+//    of codes (32 elements of one row) per 64-wide K chunk and uses one dword per MFMA.  The
+//    K order inside a chunk is permuted identically for A and W, which leaves every dot
+//    product unchanged.  Tiles are mapped to XCDs so that each XCD's L2 serves a compact
+//    block of output tiles.
+//  * Decode kernel (M <= 16): memory-bound streaming of W.  A 512-thread workgroup owns 16
+//    rows of W; its 8 wavefronts split K, accumulate 16x16 MFMA tiles and reduce them in
+//    LDS in a fixed order (deterministic).
+//  * A plain kernel (one thread per output, fp32 FMA) serves shapes the fast kernels do not
+//    take (K not a multiple of 128).
+#include "nvfp4_device.h"
+#include "nvfp4_internal.h"
+
+namespace nvfp4 {
+
+namespace {
+
+struct GemmArgs {
+  int32_t M, N, K;
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const float* a_global;
+  int32_t a_per_row;
+  const uint8_t* w_codes;
+  const uint8_t* w_scales;
+  const float* w_globals;
+  void* y;
+  int32_t y_bf16;
+  int64_t ldy;
+  SegmentTable seg;
+};
+
+__device__ __forceinline__ int segment_of(int n, const SegmentTable& seg) {
+  int s = 0;
+  for (int i = 1; i < seg.count; ++i) s += n >= seg.bound[i];
+  return s;
+}
+
+__device__ __forceinline__ void store_out(const GemmArgs& g, int m, int n, float v) {
+  if (g.y_bf16)
+    static_cast<uint16_t*>(g.y)[(int64_t)m * g.ldy + n] = f32_to_bf16_rne(v);
+  else
+    static_cast<float*>(g.y)[(int64_t)m * g.ldy + n] = v;
+}
+
+// Byte k of a dword as an fp16 scale pair (E4M3 * 2^-8 in both halves).
+__device__ __forceinline__ half2_t pair_of_byte(uint32_t dw, int k) {
+  return scale_pair_f16((dw >> (8 * k)) & 0xFFu);
+}
+
+// ------------------------------------------------------------------ prefill kernel
+
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int kRowBytes = BK / 2;           // 64 B of codes per row per K step
+constexpr int kRowStride = kRowBytes + 16;  // padded LDS row: conflict-free 16 B reads
+constexpr int kCodeTile = BM * kRowStride;  // bytes per operand per stage
+constexpr int kScaleTile = BM * 8;          // 8 scale bytes per row per K step
+constexpr int kStageBytes = 2 * kCodeTile + 2 * kScaleTile;
+constexpr int kPrefillThreads = 256;
+
+struct StageRegs {
+  uint4 a[4], b[4];
+  uint2 sa, sb;
+};
+
+// Scale bytes of one row for one K step [b0..b7] reordered to [b0 b1 b4 b5 | b2 b3 b6 b7]
+// so that lane half h reads its four bytes (blocks 2h, 2h+1 of both 64-wide chunks) as one
+// dword.
+__device__ __forceinline__ uint2 permute_scales(uint2 s) {
+  return make_uint2(__builtin_amdgcn_perm(s.y, s.x, 0x05040100u), __builtin_amdgcn_perm(s.y, s.x, 0x07060302u));
+}
+
+__device__ __forceinline__ void load_stage(const GemmArgs& g, int m0, int n0, int kt, StageRegs& r) {
+  const int t = threadIdx.x;
+  const int64_t kb = (int64_t)g.K / 2, ks = (int64_t)g.K / 16;
+  const int seg16 = t & 3;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (t >> 2) + 64 * j;
+    const int am = min(m0 + row, g.M - 1), wn = min(n0 + row, g.N - 1);
+    r.a[j] = *reinterpret_cast<const uint4*>(g.a_codes + am * kb + kt * kRowBytes + seg16 * 16);
+    r.b[j] = *reinterpret_cast<const uint4*>(g.w_codes + wn * kb + kt * kRowBytes + seg16 * 16);
+  }
+  const int am = min(m0 + t, g.M - 1), wn = min(n0 + t, g.N - 1);
+  r.sa = *reinterpret_cast<const uint2*>(g.a_scales + am * ks + kt * 8);
+  r.sb = *reinterpret_cast<const uint2*>(g.w_scales + wn * ks + kt * 8);
+}
+
+__device__ __forceinline__ void store_stage(uint8_t* lds, const StageRegs& r) {
+  const int t = threadIdx.x;
+  uint8_t* ca = lds;
+  uint8_t* cb = lds + kCodeTile;
+  uint8_t* sa = lds + 2 * kCodeTile;
+  uint8_t* sb = sa + kScaleTile;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (t >> 2) + 64 * j;
+    *reinterpret_cast<uint4*>(ca + row * kRowStride + (t & 3) * 16) = r.a[j];
+    *reinterpret_cast<uint4*>(cb + row * kRowStride + (t & 3) * 16) = r.b[j];
+  }
+  *reinterpret_cast<uint2*>(sa + t * 8) = permute_scales(r.sa);
+  *reinterpret_cast<uint2*>(sb + t * 8) = permute_scales(r.sb);
+}
+
+// Tile index -> (tile_m, tile_n).  Workgroups are dispatched round-robin over the 8 XCDs;
+// workgroup i is given logical tile start(i % 8) + i / 8, so each XCD owns a contiguous
+// range of logical tiles, ordered in groups of 8 tile rows (column-major inside a group)
+// so that concurrently resident tiles share rows of A and W in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int i, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int T = tiles_m * tiles_n;
+  const int x = i & 7, j = i >> 3;
+  const int per = T >> 3, rem = T & 7;
+  const int t = x * per + min(x, rem) + j;
+  const int G = 8;
+  const int group = t / (G * tiles_n);
+  const int first = group * G;
+  const int gsize = min(tiles_m - first, G);
+  const int in = t - group * G * tiles_n;
+  tm = first + in % gsize;
+  tn = in / gsize;
+}
+
+__global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(GemmArgs g) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const int r = lane & 31, h = lane >> 5;
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+
+  const int nk = g.K / BK;
+  StageRegs regs;
+  load_stage(g, m0, n0, 0, regs);
+  store_stage(lds, regs);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) load_stage(g, m0, n0, kt + 1, regs);
+    const uint8_t* buf = lds + (kt & 1) * kStageBytes;
+    const uint8_t* ca = buf;
+    const uint8_t* cb = buf + kCodeTile;
+    const uint8_t* sa_t = buf + 2 * kCodeTile;
+    const uint8_t* sb_t = sa_t + kScaleTile;
+    uint32_t sa[4], sb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sa[i] = *reinterpret_cast<const uint32_t*>(sa_t + (wm + 32 * i + r) * 8 + 4 * h);
+      sb[i] = *reinterpret_cast<const uint32_t*>(sb_t + (wn + 32 * i + r) * 8 + 4 * h);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      uint4 qa[4], qb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qa[i] = *reinterpret_cast<const uint4*>(ca + (wm + 32 * i + r) * kRowStride + c * 32 + h * 16);
+        qb[i] = *reinterpret_cast<const uint4*>(cb + (wn + 32 * i + r) * kRowStride + c * 32 + h * 16);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        half8_t fa[4], fb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t wa = s == 0 ? qa[i].x : s == 1 ? qa[i].y : s == 2 ? qa[i].z : qa[i].w;
+          const uint32_t wb = s == 0 ? qb[i].x : s == 1 ? qb[i].y : s == 2 ? qb[i].z : qb[i].w;
+          fa[i] = dequant8_f16(wa, pair_of_byte(sa[i], 2 * c + (s >> 1)));
+          fb[i] = dequant8_f16(wb, pair_of_byte(sb[i], 2 * c + (s >> 1)));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    if (kt + 1 < nk) store_stage(lds + ((kt + 1) & 1) * kStageBytes, regs);
+    __syncthreads();
+  }
+
+  // Epilogue: y = (acc * s_gA[m]) * s_gW[seg(n)].
+  float sw[4];
+  int ncol[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ncol[j] = n0 + wn + 32 * j + r;
+    sw[j] = g.w_globals[segment_of(min(ncol[j], g.N - 1), g.seg)];
+  }
+  const float sa0 = g.a_global[0];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int m = m0 + wm + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+      if (m >= g.M) continue;
+      const float sam = g.a_per_row ? g.a_global[m] : sa0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (ncol[j] < g.N) store_out(g, m, ncol[j], (acc[i][j][q] * sam) * sw[j]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ decode kernel
+
+constexpr int kDecodeWaves = 8;
+constexpr int kDecodeThreads = 64 * kDecodeWaves;
+
+__global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(GemmArgs g) {
+  __shared__ float red[kDecodeWaves][64][4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rr = lane & 15, grp = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  const int64_t kb = (int64_t)g.K / 2, ks = (int64_t)g.K / 16;
+  const int nchunks = g.K / 128;
+  const int c0 = wave * nchunks / kDecodeWaves, c1 = (wave + 1) * nchunks / kDecodeWaves;
+
+  const int wrow = min(n0 + rr, g.N - 1);
+  const bool arow_ok = rr < g.M;
+  const uint8_t* wc = g.w_codes + wrow * kb + grp * 16;
+  const uint8_t* wsc = g.w_scales + wrow * ks + grp * 2;
+  const uint8_t* ac = g.a_codes + (arow_ok ? rr : 0) * kb + grp * 16;
+  const uint8_t* asc = g.a_scales + (arow_ok ? rr : 0) * ks + grp * 2;
+
+  f32x4_t acc = f32x4_t{};
+#pragma unroll 4
+  for (int c = c0; c < c1; ++c) {
+    const uint4 w = *reinterpret_cast<const uint4*>(wc + c * 64);
+    const uint32_t ws = *reinterpret_cast<const uint16_t*>(wsc + c * 8);
+    uint4 a = make_uint4(0, 0, 0, 0);
+    uint32_t as = 0;
+    if (arow_ok) {
+      a = *reinterpret_cast<const uint4*>(ac + c * 64);
+      as = *reinterpret_cast<const uint16_t*>(asc + c * 8);
+    }
+    const half2_t pw0 = pair_of_byte(ws, 0), pw1 = pair_of_byte(ws, 1);
+    const half2_t pa0 = pair_of_byte(as, 0), pa1 = pair_of_byte(as, 1);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(a.x, pa0), dequant8_f16(w.x, pw0), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(a.y, pa0), dequant8_f16(w.y, pw0), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(a.z, pa1), dequant8_f16(w.z, pw1), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(a.w, pa1), dequant8_f16(w.w, pw1), acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) red[wave][lane][q] = acc[q];
+  __syncthreads();
+  if (wave == 0) {
+    f32x4_t s = f32x4_t{};
+    for (int w = 0; w < kDecodeWaves; ++w)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s[q] += red[w][lane][q];
+    const int n = n0 + rr;
+    if (n < g.N) {
+      const float swn = g.w_globals[segment_of(n, g.seg)];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = 4 * grp + q;
+        if (m < g.M) store_out(g, m, n, (s[q] * g.a_global[g.a_per_row ? m : 0]) * swn);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ plain kernel
+
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+  const float v = mag[c & 7u];
+  return (c & 8u) ? -v : v;
+}
+
+__global__ __launch_bounds__(256) void gemm_plain_kernel(GemmArgs g) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)g.M * g.N) return;
+  const int m = (int)(idx / g.N), n = (int)(idx % g.N);
+  const int64_t kb = g.K / 2, ks = g.K / 16;
+  float acc = 0.0f;
+  for (int b = 0; b < g.K / 16; ++b) {
+    const float sa = e4m3_decode(g.a_scales[m * ks + b]);
+    const float sw = e4m3_decode(g.w_scales[n * ks + b]);
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t ca = g.a_codes[m * kb + b * 8 + i], cw = g.w_codes[n * kb + b * 8 + i];
+      acc = __builtin_fmaf(e2m1_value(ca & 15u) * sa, e2m1_value(cw & 15u) * sw, acc);
+      acc = __builtin_fmaf(e2m1_value(ca >> 4) * sa, e2m1_value(cw >> 4) * sw, acc);
+    }
+  }
+  store_out(g, m, n, (acc * g.a_global[g.a_per_row ? m : 0]) * g.w_globals[segment_of(n, g.seg)]);
+}
+
+}  // namespace
+
+size_t gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+
+int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+                const float* a_global, int a_global_per_row, const uint8_t* w_codes, const uint8_t* w_scales,
+                const float* w_globals, const SegmentTable& seg, void* y, int y_dtype, int64_t ldy, void*,
+                hipStream_t stream) {
+  if (M == 0 || N == 0) return NVFP4_OK;
+  GemmArgs g;
+  g.M = (int32_t)M;
+  g.N = (int32_t)N;
+  g.K = (int32_t)K;
+  g.a_codes = a_codes;
+  g.a_scales = a_scales;
+  g.a_global = a_global;
+  g.a_per_row = a_global_per_row;
+  g.w_codes = w_codes;
+  g.w_scales = w_scales;
+  g.w_globals = w_globals;
+  g.y = y;
+  g.y_bf16 = y_dtype == NVFP4_BF16;
+  g.ldy = ldy;
+  g.seg = seg;
+  if (K % 128 != 0) {
+    const int64_t total = M * N;
+    gemm_plain_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(g);
+  } else if (M <= 16) {
+    gemm_decode_kernel<<<(unsigned)((N + 15) / 16), kDecodeThreads, 0, stream>>>(g);
+  } else {
+    // The 88 KB of dynamic LDS exceed the default limit; raise it once per device.
+    static bool attr_set[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return NVFP4_ERR_HIP;
+    if (!attr_set[dev]) {
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_prefill_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStageBytes) != hipSuccess)
+        return NVFP4_ERR_HIP;
+      attr_set[dev] = true;
+    }
+    const int tiles = (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
+    gemm_prefill_kernel<<<tiles, kPrefillThreads, 2 * kStageBytes, stream>>>(g);
+  }
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+}  // namespace nvfp4

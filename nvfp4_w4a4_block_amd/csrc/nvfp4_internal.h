@@ -1,0 +1,56 @@
+// Host-side internals shared by the C ABI and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/nvfp4.h"
+
+namespace nvfp4 {
+
+// Unsigned 32-bit division by a runtime constant with a multiply-high (round-up method of
+// Granlund and Montgomery, "Division by invariant integers using multiplication", 1994).
+struct FastDivU32 {
+  uint32_t d, m, s1, s2;
+};
+
+inline FastDivU32 make_fastdiv(uint32_t d) {
+  FastDivU32 f;
+  f.d = d;
+  uint32_t l = 0;
+  while (l < 32 && (1ull << l) < d) ++l;              // l = ceil(log2 d)
+  f.m = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+  f.s1 = l < 1 ? l : 1;
+  f.s2 = l > 1 ? l - 1 : 0;
+  return f;
+}
+
+__host__ __device__ inline uint32_t fastdiv(uint32_t n, const FastDivU32& f) {
+#ifdef __HIP_DEVICE_COMPILE__
+  uint32_t t1 = __umulhi(f.m, n);
+#else
+  uint32_t t1 = (uint32_t)(((uint64_t)f.m * n) >> 32);
+#endif
+  return (t1 + ((n - t1) >> f.s1)) >> f.s2;
+}
+
+// Quantize launchers (quantize.hip).  All validation is done by the caller.
+int launch_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                    uint8_t* codes, uint8_t* scales, float* global_scale, int mode,
+                    void* workspace, hipStream_t stream);
+size_t quantize_workspace_bytes(int64_t rows, int64_t cols, int mode);
+
+// GEMM launchers (gemm.hip).
+struct SegmentTable {
+  int32_t count;
+  int32_t bound[NVFP4_MAX_SEGMENTS + 1];   // column offsets; bound[0] = 0, bound[count] = N
+};
+
+int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+                const float* a_global, int a_global_per_row, const uint8_t* w_codes,
+                const uint8_t* w_scales, const float* w_globals, const SegmentTable& seg,
+                void* y, int y_dtype, int64_t ldy, void* workspace, hipStream_t stream);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+}  // namespace nvfp4

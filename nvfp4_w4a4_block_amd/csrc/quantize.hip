@@ -1,0 +1,214 @@
+// NVFP4 quantization kernels for gfx950.
+//
+// Steps, per "Why Gated DeltaNet Survives 4-Bit Quantization" ("The deep dive": four-bit
+// values, one shared scale per sixteen-element block) and "NVFP4 W4A4 Quantization
+// Compresses 27B Hybrid Models" (section "Challenging the Recurrence Fragility
+// Assumption": E2M1 values, E4M3 block scale):
+//   global scale  s_g = fl32(max|x| / 2688)  (per tensor or per row; or given)
+//   block scale   s_j = E4M3_RNE_SAT(fl32(a_j / fl32(6 s_g))),  a_j = max |x| of the block
+//   element       code = sign | E2M1_RNE_SAT(fl32(x / fl32(E4M3(s_j) s_g)))
+//
+// Memory-bound design: one lane encodes one 16-element block (32 B of bf16 in, 8 B of codes
+// and 1 B of scale out), so a wavefront streams 2 KB of contiguous input per block row.  The
+// per-tensor global scale needs a grid-wide max before the first block can be encoded:
+// pass 1 writes one NaN-propagating partial max per workgroup, and every workgroup of pass
+// 2 reduces those few partials itself, so no atomics, counters or zero-initialised
+// workspace are needed and the result is deterministic.
+#include "nvfp4_device.h"
+#include "nvfp4_internal.h"
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxPartials = 1024;        // pass-1 workgroups (4 partials per pass-2 thread)
+
+// 16 B of input as fp32 values.
+__device__ __forceinline__ void widen(const uint4& w, float* v, const uint16_t*) {
+  uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(a[i] << 16);
+    v[2 * i + 1] = __uint_as_float(a[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void widen(const uint4& w, float* v, const float*) {
+  v[0] = __uint_as_float(w.x);
+  v[1] = __uint_as_float(w.y);
+  v[2] = __uint_as_float(w.z);
+  v[3] = __uint_as_float(w.w);
+}
+
+// Largest |x| bit pattern of 16 B of input, as an fp32 bit pattern.  Integer max of the
+// magnitude bits orders NaN above +inf above every finite value, so NaN propagates.
+__device__ __forceinline__ uint32_t max_abs_bits(const uint4& w, const uint16_t*) {
+  uint32_t m = 0;
+  uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t lo = (a[i] & 0x7FFFu), hi = (a[i] >> 16) & 0x7FFFu;
+    m = max(m, max(lo, hi));
+  }
+  return m << 16;
+}
+__device__ __forceinline__ uint32_t max_abs_bits(const uint4& w, const float*) {
+  return max(max(w.x & 0x7FFFFFFFu, w.y & 0x7FFFFFFFu), max(w.z & 0x7FFFFFFFu, w.w & 0x7FFFFFFFu));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+
+// Workgroup max of one value per thread; the result is valid in every thread.
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
+  __shared__ uint32_t red[kThreads / 64];
+  v = wave_max_u32(v);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  uint32_t r = red[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) r = max(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
+template <typename T>
+constexpr int kElemsPer16B = 16 / sizeof(T);
+
+// Pass 1 of the per-tensor mode: one partial max (fp32 magnitude bits) per workgroup.
+// Workgroups stride over rows, threads over the 16 B chunks of a row.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void amax_partial_kernel(const T* __restrict__ x, int64_t rows,
+                                                                 int64_t cols, int64_t ldx,
+                                                                 uint32_t* __restrict__ partial) {
+  const int64_t chunks = cols / kElemsPer16B<T>;
+  uint32_t m = 0;
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const uint4* row = reinterpret_cast<const uint4*>(x + r * ldx);
+    for (int64_t c = threadIdx.x; c < chunks; c += kThreads) m = max(m, max_abs_bits(row[c], x));
+  }
+  m = block_max_u32(m);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+// Per-row global scales: one workgroup per row (strided), s_g[r] = fl32(amax_r / 2688).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void row_scale_kernel(const T* __restrict__ x, int64_t rows,
+                                                              int64_t cols, int64_t ldx,
+                                                              float* __restrict__ sg_out) {
+  const int64_t chunks = cols / kElemsPer16B<T>;
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const uint4* row = reinterpret_cast<const uint4*>(x + r * ldx);
+    uint32_t m = 0;
+    for (int64_t c = threadIdx.x; c < chunks; c += kThreads) m = max(m, max_abs_bits(row[c], x));
+    m = block_max_u32(m);
+    if (threadIdx.x == 0) sg_out[r] = __uint_as_float(m) / kGlobalDivisor;
+  }
+}
+
+enum Mode { kPerTensor = 0, kPerRow = 1, kGiven = 2 };
+
+// Pass 2 (or the only pass): one lane per 16-element block, flat block index over
+// rows x (cols / 16); grid-stride.
+template <typename T, int MODE>
+__global__ __launch_bounds__(kThreads) void encode_kernel(const T* __restrict__ x, uint32_t rows,
+                                                           uint32_t bpr, int64_t ldx, FastDivU32 div_bpr,
+                                                           uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ scales,
+                                                           float* __restrict__ global_scale,
+                                                           const uint32_t* __restrict__ partial,
+                                                           int npartial) {
+  float sg = 0.0f;
+  if (MODE == kPerTensor) {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < npartial; i += kThreads) m = max(m, partial[i]);
+    m = block_max_u32(m);
+    sg = __uint_as_float(m) / kGlobalDivisor;
+    if (blockIdx.x == 0 && threadIdx.x == 0) global_scale[0] = sg;
+  } else if (MODE == kGiven) {
+    sg = global_scale[0];
+  }
+  const uint32_t total = rows * bpr;
+  const bool dense = ldx == (int64_t)bpr * 16;
+  for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < total; i += gridDim.x * kThreads) {
+    uint32_t r = 0, b = i;
+    if (MODE == kPerRow || !dense) {
+      r = fastdiv(i, div_bpr);
+      b = i - r * bpr;
+    }
+    const T* src = dense ? x + (int64_t)i * 16 : x + (int64_t)r * ldx + (int64_t)b * 16;
+    const uint4* p = reinterpret_cast<const uint4*>(src);
+    float v[16];
+#pragma unroll
+    for (int c = 0; c < 16 / kElemsPer16B<T>; ++c) widen(p[c], v + c * kElemsPer16B<T>, x);
+    const float s = MODE == kPerRow ? global_scale[r] : sg;
+    uint32_t sb, lo, hi;
+    encode_block(v, s, sb, lo, hi);
+    reinterpret_cast<uint2*>(codes)[i] = make_uint2(lo, hi);
+    scales[i] = (uint8_t)sb;
+  }
+}
+
+template <typename T>
+int launch_typed(const T* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* codes,
+                 uint8_t* scales, float* global_scale, int mode, void* workspace,
+                 hipStream_t stream) {
+  const uint32_t bpr = (uint32_t)(cols / 16);
+  const uint64_t total = (uint64_t)rows * bpr;
+  if (mode == kPerTensor && rows == 0) {
+    // max over an empty tensor is 0, so s_g = 0; write it with a one-lane launch.
+    encode_kernel<T, kPerTensor><<<1, kThreads, 0, stream>>>(x, 0, bpr, ldx, make_fastdiv(bpr), codes,
+                                                            scales, global_scale,
+                                                            static_cast<const uint32_t*>(workspace), 0);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+  }
+  if (rows == 0) return NVFP4_OK;
+  const uint32_t want = (uint32_t)((total + kThreads - 1) / kThreads);
+  const uint32_t grid = want < 8192u ? want : 8192u;   // grid-stride beyond 2M blocks
+  const FastDivU32 fd = make_fastdiv(bpr);
+  switch (mode) {
+    case kPerTensor: {
+      uint32_t* partial = static_cast<uint32_t*>(workspace);
+      const int np = (int)(rows < kMaxPartials ? rows : kMaxPartials);
+      amax_partial_kernel<T><<<np, kThreads, 0, stream>>>(x, rows, cols, ldx, partial);
+      encode_kernel<T, kPerTensor><<<grid, kThreads, 0, stream>>>(x, (uint32_t)rows, bpr, ldx, fd, codes,
+                                                                  scales, global_scale, partial, np);
+      break;
+    }
+    case kPerRow: {
+      const int g = (int)(rows < 4096 ? rows : 4096);
+      row_scale_kernel<T><<<g, kThreads, 0, stream>>>(x, rows, cols, ldx, global_scale);
+      encode_kernel<T, kPerRow><<<grid, kThreads, 0, stream>>>(x, (uint32_t)rows, bpr, ldx, fd, codes,
+                                                               scales, global_scale, nullptr, 0);
+      break;
+    }
+    default:
+      encode_kernel<T, kGiven><<<grid, kThreads, 0, stream>>>(x, (uint32_t)rows, bpr, ldx, fd, codes,
+                                                              scales, global_scale, nullptr, 0);
+      break;
+  }
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+}  // namespace
+
+size_t quantize_workspace_bytes(int64_t rows, int64_t, int mode) {
+  if (mode != kPerTensor) return 0;
+  const int64_t np = rows < kMaxPartials ? rows : kMaxPartials;
+  return (size_t)(np > 0 ? np : 1) * sizeof(uint32_t);
+}
+
+int launch_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, uint8_t* codes,
+                    uint8_t* scales, float* global_scale, int mode, void* workspace, hipStream_t stream) {
+  if (x_dtype == NVFP4_BF16)
+    return launch_typed(static_cast<const uint16_t*>(x), rows, cols, ldx, codes, scales, global_scale, mode,
+                        workspace, stream);
+  return launch_typed(static_cast<const float*>(x), rows, cols, ldx, codes, scales, global_scale, mode,
+                      workspace, stream);
+}
+
+}  // namespace nvfp4

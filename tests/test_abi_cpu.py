@@ -1,0 +1,128 @@
+"""CPU checks of the C-ABI library: it loads, exports every function the header declares,
+and rejects bad arguments on the host before touching a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import nvfp4_w4a4_block_amd as m
+    return m
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    fns = _declared_functions()
+    for f in ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_fused_segments"):
+        assert f in fns
+
+
+def test_library_exports_every_declared_function(nv):
+    out = subprocess.run(["nm", "-D", "--defined-only", nv.library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (nvfp4_[a-z0-9_]+)", out))
+    missing = [f for f in _declared_functions() if f not in exported]
+    assert not missing, missing
+    assert set(nv.EXPORTED_SYMBOLS) == set(_declared_functions())
+    for f in _declared_functions():
+        assert hasattr(ctypes.CDLL(nv.library_path()), f)
+
+
+def test_status_strings(nv):
+    for s in range(5):
+        assert nv.lib.nvfp4_status_string(s)
+    assert nv.lib.nvfp4_status_string(99) == b"unknown status"
+    assert nv.lib.nvfp4_version() >= 100
+
+
+# Host-side validation: every call below must return before any HIP call.  Pointers are
+# fake addresses, never dereferenced.
+A16 = 0x10000
+MIS = 0x10001
+
+
+def q(nv, x=A16, dt=1, rows=4, cols=32, ldx=32, codes=A16, scales=A16, g=A16, mode=2, ws=None, wsb=0):
+    return nv.lib.nvfp4_quantize(x, dt, rows, cols, ldx, codes, scales, g, mode, ws, wsb, None)
+
+
+def test_quantize_argument_errors(nv):
+    assert q(nv, cols=24, ldx=24) == 1             # cols not a multiple of 16
+    assert q(nv, cols=0, ldx=0) == 1
+    assert q(nv, rows=-1) == 1
+    assert q(nv, ldx=16) == 1                      # ldx < cols
+    assert q(nv, x=None) == 1
+    assert q(nv, codes=None) == 1
+    assert q(nv, scales=None) == 1
+    assert q(nv, g=None) == 1
+    assert q(nv, x=MIS) == 1                       # misaligned input
+    assert q(nv, ldx=36) == 1                      # row pitch not a multiple of 16 B
+    assert q(nv, dt=7) == 1
+    assert q(nv, mode=5) == 1
+    assert q(nv, mode=0) == 3                      # per-tensor needs a workspace
+    assert q(nv, mode=0, ws=A16, wsb=1) == 3       # too small
+    assert q(nv, rows=1 << 27, cols=1 << 10, ldx=1 << 10) == 2   # too many blocks
+    assert nv.lib.nvfp4_quantize_workspace_size(4096, 5120, 0) >= 4
+    assert nv.lib.nvfp4_quantize_workspace_size(4096, 5120, 2) == 0
+
+
+def g(nv, M=32, N=32, K=128, a=A16, sa=A16, ga=A16, pr=0, w=A16, sw=A16, gw=A16, y=A16, dt=1, ldy=32):
+    return nv.lib.nvfp4_gemm(M, N, K, a, sa, ga, pr, w, sw, gw, y, dt, ldy, None, 0, None)
+
+
+def test_gemm_argument_errors(nv):
+    assert g(nv, K=24) == 1
+    assert g(nv, K=0) == 1
+    assert g(nv, M=-1) == 1
+    assert g(nv, ldy=16) == 1
+    assert g(nv, a=None) == 1
+    assert g(nv, w=MIS) == 1
+    assert g(nv, gw=None) == 1
+    assert g(nv, dt=3) == 1
+    assert g(nv, pr=2) == 1
+    assert g(nv, M=0) == 0 and g(nv, N=0, ldy=0) == 0     # empty products are no-ops
+
+
+def test_fused_argument_errors(nv):
+    widths = (ctypes.c_int64 * 3)(16, 0, 16)
+    f = nv.lib.nvfp4_gemm_fused_segments
+    assert f(32, 128, A16, A16, A16, 0, 3, ctypes.cast(widths, ctypes.c_void_p), A16, A16, A16, A16, 1, 48,
+             None, 0, None) == 1                   # zero-width segment
+    assert f(32, 128, A16, A16, A16, 0, 0, None, A16, A16, A16, A16, 1, 48, None, 0, None) == 1
+    many = (ctypes.c_int64 * 65)(*([16] * 65))
+    assert f(32, 128, A16, A16, A16, 0, 65, ctypes.cast(many, ctypes.c_void_p), A16, A16, A16, A16, 1,
+             1040, None, 0, None) == 2
+    ok = (ctypes.c_int64 * 2)(16, 16)
+    assert f(32, 128, A16, A16, A16, 0, 2, ctypes.cast(ok, ctypes.c_void_p), A16, A16, A16, A16, 1, 16,
+             None, 0, None) == 1                   # ldy < sum of widths
+
+
+def test_fastdiv_host_logic(tmp_path):
+    # The flat block index of the encoder is split into (row, block) with a multiply-high
+    # division; check it on the host against integer division.
+    src = tmp_path / "fd.cpp"
+    src.write_text(
+        '#include "nvfp4_internal.h"\n#include <cstdio>\nint main(){unsigned long long bad=0;\n'
+        'unsigned ds[]={1,2,3,5,7,16,20,64,320,1088,1089,4095,65537,1000003,2147483647u,4294967295u};\n'
+        'for(unsigned d: ds){auto f=nvfp4::make_fastdiv(d); unsigned long long x=88172645463325252ull;\n'
+        ' for(long i=0;i<2000000;i++){x^=x<<13;x^=x>>7;x^=x<<17; unsigned n=(unsigned)x; if(i<1000) n=i;\n'
+        '  if(i>=1000&&i<2000) n=0xFFFFFFFFu-(unsigned)(i-1000);\n'
+        '  if(nvfp4::fastdiv(n,f)!=n/d) bad++;}}\nprintf("%llu\\n",bad); return bad!=0;}\n')
+    exe = tmp_path / "fd"
+    inc = os.path.join(ROOT, "nvfp4_w4a4_block_amd", "csrc")
+    r = subprocess.run(["/opt/rocm/bin/hipcc", "-O1", "-x", "hip", "--cuda-host-only", "-I", inc, str(src), "-o",
+                        str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.strip() == "0", r.stdout

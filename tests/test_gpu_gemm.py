@@ -1,0 +1,169 @@
+"""GPU parity of nvfp4_gemm and nvfp4_gemm_fused_segments against the oracle:
+per-element |y - Y| <= 1e-4 * sum_k |a_k w_k| (plus half a bf16 ulp for bf16 output), an
+integer-exact special case compared bitwise, fused == separate, and the global-scale
+mismatch reproduced as a negative control."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import nvfp4_ref as ref
+from tests.gpu_helpers import DEV, assert_gemm_close, assert_quant_equal, nv, to_device, to_gpu, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _quant_pair(x, w, a_mode="per_tensor", bf16=True):
+    """Quantize on the GPU, check bit-exactness, return (gpu A, gpu W, oracle A, oracle W)."""
+    xg, wg = to_gpu(x, bf16), to_gpu(w, bf16)
+    a, q = nv().quantize(xg, a_mode), nv().quantize(wg)
+    oa = ref.quantize(xg.float().cpu().numpy(), ref.PER_ROW if a_mode == "per_row" else ref.PER_TENSOR)
+    ow = ref.quantize(wg.float().cpu().numpy())
+    assert_quant_equal(a, oa, what="A")
+    assert_quant_equal(q, ow, what="W")
+    return a, q, oa, ow
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_tiny(out_dtype):
+    t = workloads.TINY
+    a, w, oa, ow = _quant_pair(t.x(), t.w(), bf16=False)
+    y = nv().gemm(a, w, out_dtype)
+    Y, T = ref.gemm(oa, ow)
+    assert_gemm_close(y, Y, T, "tiny")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_prefill_sampled_rows(out_dtype):
+    p = workloads.PREFILL
+    a, w, oa, ow = _quant_pair(p.x(), p.w())
+    y = nv().gemm(a, w, out_dtype)
+    rows = np.sort(np.random.default_rng(1).choice(p.M, 48, replace=False))
+    rows = np.concatenate([[0, p.M - 1], rows])
+    Y, T = ref.gemm(oa, ow, rows)
+    worst = assert_gemm_close(y[torch.from_numpy(rows).to(DEV)], Y, T, "prefill")
+    print(f"prefill max err/T = {worst:.3g}")
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("a_mode", ["per_row", "per_tensor"])
+def test_decode(M, a_mode):
+    d = workloads.DECODE
+    a, w, oa, ow = _quant_pair(d.x(M), d.w(), a_mode)
+    y = nv().gemm(a, w, torch.bfloat16)
+    Y, T = ref.gemm(oa, ow)
+    assert_gemm_close(y, Y, T, f"decode M={M}")
+
+
+def _fused_weights(f, K=None, rows=None):
+    segs_gpu, segs_ora = [], []
+    for i in range(len(f.widths)):
+        wg = to_gpu(f.w(i))
+        q = nv().quantize(wg)
+        o = ref.quantize(wg.float().cpu().numpy())
+        assert_quant_equal(q, o, what=f"w{i}")
+        segs_gpu.append(q)
+        segs_ora.append(o)
+    codes = torch.cat([q.codes for q in segs_gpu])
+    scales = torch.cat([q.scales for q in segs_gpu])
+    globals_ = torch.cat([q.global_scale for q in segs_gpu])
+    return segs_gpu, segs_ora, codes, scales, globals_
+
+
+def test_fused_gdn_projections():
+    f = workloads.FUSED
+    xg = to_gpu(f.x())
+    a = nv().quantize(xg)
+    oa = ref.quantize(xg.float().cpu().numpy())
+    assert_quant_equal(a, oa, what="x")
+    segs_gpu, segs_ora, codes, scales, globals_ = _fused_weights(f)
+    y = nv().gemm_fused_segments(a, codes, scales, f.widths, globals_, torch.bfloat16)
+    rows = np.concatenate([[0, f.M - 1], np.random.default_rng(3).choice(f.M, 30, replace=False)])
+    Y, T = ref.fused_segments(oa, segs_ora, rows)
+    assert_gemm_close(y[torch.from_numpy(rows).to(DEV)], Y, T, "fused")
+    # fused == six separate launches, bitwise (same kernel, same K order per element)
+    off = 0
+    for q, n in zip(segs_gpu, f.widths):
+        ys = nv().gemm(a, q, torch.bfloat16)
+        assert torch.equal(ys, y[:, off:off + n]), f"segment at {off}"
+        off += n
+
+
+def test_shared_global_scale_reproduces_the_mismatch():
+    # A fused launch that applies the first module's global scale to every segment scales
+    # segment i by s_g0 / s_gi: the global-scale mismatch (repaired by per-segment scales).
+    f = workloads.FUSED
+    xg = to_gpu(f.x(256))
+    a = nv().quantize(xg)
+    segs_gpu, segs_ora, codes, scales, globals_ = _fused_weights(f)
+    good = nv().gemm_fused_segments(a, codes, scales, f.widths, globals_, torch.float32)
+    bad = nv().gemm_fused_segments(a, codes, scales, f.widths, globals_[:1].repeat(len(f.widths)),
+                                   torch.float32)
+    off = 0
+    g0 = globals_[0].item()
+    for i, n in enumerate(f.widths):
+        ratio = g0 / globals_[i].item()
+        gs, bs = good[:, off:off + n].double(), bad[:, off:off + n].double()
+        assert torch.allclose(bs, gs * ratio, rtol=1e-6, atol=1e-30 + 1e-6 * gs.abs().max().item() * ratio)
+        off += n
+    # the gate segments (sigma 0.05) come out at less than half their true size
+    assert g0 / globals_[4].item() < 0.5
+
+
+def _unit_scale(codes_np):
+    R, C = codes_np.shape
+    return ref.NVFP4(ref.pack_codes(codes_np), np.full((R, C // 16), 0x38, np.uint8), np.ones(1, np.float32), R, C)
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 17408, 5120), (16, 5120, 17408), (1, 5120, 17408), (8192, 12384, 5120),
+                                   (300, 200, 384)])
+def test_integer_exact_special_case(M, N, K):
+    # Scale bytes 0x38 (1.0) and global scales 1.0: Y = integer matmul / 4, exact in fp32 in
+    # any summation order, so the GPU must match int64 arithmetic bit for bit.
+    g = np.random.default_rng(M + N + K)
+    ca = g.integers(0, 16, (M, K), dtype=np.uint8)
+    cw = g.integers(0, 16, (N, K), dtype=np.uint8)
+    y = nv().gemm(to_device(_unit_scale(ca)), to_device(_unit_scale(cw)), torch.float32)
+    twice = np.array([0, 1, 2, 3, 4, 6, 8, 12], np.int64)
+    rows = np.arange(M) if M <= 64 else np.sort(g.choice(M, 64, replace=False))
+    ia = (np.where(ca[rows] & 8, -1, 1) * twice[ca[rows] & 7]).astype(np.float64)
+    iw = (np.where(cw & 8, -1, 1) * twice[cw & 7]).astype(np.float64)
+    want = (ia @ iw.T) / 4.0          # integers below 2^53: exact in float64 BLAS
+    got = y[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 50, 128), (37, 300, 384), (300, 1, 256), (257, 257, 128),
+                                   (5, 33, 272), (40, 24, 16), (2, 7, 4112)])
+@pytest.mark.parametrize("a_mode", ["per_tensor", "per_row"])
+def test_ragged_shapes(M, N, K, a_mode):
+    x = workloads.activation(31, M, M, K, outlier_frac=0.02)
+    w = workloads.weight(31, 1000 + N, N, K)
+    a, q, oa, ow = _quant_pair(x, w, a_mode)
+    for dt in (torch.float32, torch.bfloat16):
+        y = nv().gemm(a, q, dt)
+        Y, T = ref.gemm(oa, ow)
+        assert_gemm_close(y, Y, T, f"{M}x{N}x{K} {a_mode} {dt}")
+
+
+def test_output_row_pitch():
+    x = workloads.activation(32, 0, 40, 256)
+    w = workloads.weight(32, 1, 96, 256)
+    a, q, oa, ow = _quant_pair(x, w)
+    big = torch.full((40, 128), 7.0, dtype=torch.float32, device=DEV)
+    nv().gemm(a, q, torch.float32, out=big[:, :96])
+    Y, T = ref.gemm(oa, ow)
+    assert_gemm_close(big[:, :96], Y, T, "pitched")
+    assert (big[:, 96:] == 7.0).all()
+
+
+def test_empty_products():
+    a = nv().quantize(torch.zeros((0, 128), dtype=torch.bfloat16, device=DEV), "per_row")
+    w = nv().quantize(torch.ones((8, 128), dtype=torch.bfloat16, device=DEV))
+    assert nv().gemm(a, w).shape == (0, 8)
+
+
+def test_deterministic():
+    p = workloads.PREFILL
+    a, w, _, _ = _quant_pair(p.x(512), p.w()[:1024])
+    assert torch.equal(nv().gemm(a, w), nv().gemm(a, w))
