@@ -1,0 +1,252 @@
+"""Throughput of the NVFP4 W4A4 hot path on one MI355X.
+
+One step = one pass of the hot path over one batch: dynamic per-tensor NVFP4 quantization of
+the activations X (global scale, block scales, E2M1 codes) followed by the block-scaled
+NVFP4 GEMM Y = X^ . W^T with fp32 accumulation and bf16 output.  W is quantized offline
+(untimed), as a served checkpoint would be.  Inputs are resident in HBM before timing;
+several X copies are rotated so that no step reads its X from the 256 MB last-level cache.
+
+Workloads (--workload):
+  prefill  X[4096x5120] bf16 (0.1% channels x50), W[17408x5120]        (default)
+  decode   X[M x 17408], W[5120x17408], M in {1,4,16}, per-token scales
+  fused    X[8192x5120], six GDN input projections with their own global scales
+
+Prints one JSON line.  `value` is GEMM flops of the whole step divided by the step time.
+`roofline` describes the dominant kernel (the GEMM) from HIP events on the launch stream;
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
+
+
+def _events(n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def _bytes_quantize(rows: int, cols: int, in_bytes: int = 2) -> float:
+    # algorithmic bytes: X read once, codes (0.5 B/elem) and scales (1/16 B/elem) written
+    return rows * cols * (in_bytes + 0.5 + 1.0 / 16)
+
+
+def bench_prefill(nv, steps: int, warmup: int, rotate: int = 4):
+    p = workloads.PREFILL
+    dev = torch.device("cuda:0")
+    x0 = torch.from_numpy(p.x()).to(dev).to(torch.bfloat16)
+    xs = [x0] + [x0.roll(i + 1, dims=0).contiguous() for i in range(rotate - 1)]
+    w = nv.quantize(torch.from_numpy(p.w()).to(dev).to(torch.bfloat16))
+    a_bufs = [nv.quantize(x) for x in xs]          # preallocated outputs
+    y = torch.empty((p.M, p.N), dtype=torch.bfloat16, device=dev)
+
+    def step(i, ev=None):
+        a = a_bufs[i % rotate]
+        if ev is not None:
+            ev[0].record()
+        nv.quantize(xs[i % rotate], out=a)
+        if ev is not None:
+            ev[1].record()
+        nv.gemm(a, w, torch.bfloat16, out=y)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [_events(3) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    g_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    flops = p.flops
+    qbytes = _bytes_quantize(p.M, p.K)
+    res = {
+        "wall_s": wall,
+        "ms_per_step": wall * 1e3 / steps,
+        "gemm_ms": g_ms,
+        "quant_ms": q_ms,
+        "gemm_tflops": flops / (g_ms * 1e-3) / 1e12,
+        "quant_gbs": qbytes / (q_ms * 1e-3) / 1e9,
+        "flops": flops,
+        "qbytes": qbytes,
+    }
+    return res, (p, w)
+
+
+def cpu_baseline_prefill(p, sample_rows: int = 128):
+    """The oracle as it stands, on a bounded sample: quantize `sample_rows` rows of X under
+    the tensor's global scale and compute those rows of Y against the oracle-quantized W."""
+    import threadpoolctl
+    from oracle import nvfp4_ref as ref
+
+    x = p.x()
+    wq = ref.quantize(p.w())                                      # offline, untimed
+    sg = ref.global_scale(x, ref.PER_TENSOR)
+    rows = np.arange(sample_rows)
+    t0 = time.perf_counter()
+    aq = ref.quantize(x[rows], ref.GIVEN, float(sg[0]))
+    ref.gemm(aq, wq)
+    dt = time.perf_counter() - t0
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    flops = 2.0 * sample_rows * p.N * p.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{sample_rows} of {p.M} rows of X: quantize (numpy, 1 thread) + fp64 GEMM against "
+                      f"all {p.N} W rows (dequantize W + BLAS matmul, {cores} threads); {dt:.1f} s"}
+
+
+def bench_decode(nv, steps: int, warmup: int, rotate: int = 8):
+    d = workloads.DECODE
+    dev = torch.device("cuda:0")
+    w0 = torch.from_numpy(d.w()).to(dev).to(torch.bfloat16)
+    ws = [nv.quantize(w0)]
+    for _ in range(rotate - 1):        # distinct copies: 8 x 56 MB defeats the 256 MB cache
+        q = ws[0]
+        ws.append(nv.NVFP4Tensor(q.codes.clone(), q.scales.clone(), q.global_scale.clone()))
+    out = {}
+    for M in d.Ms:
+        x = torch.from_numpy(d.x(M)).to(dev).to(torch.bfloat16)
+        a = nv.quantize(x, "per_row")
+        y = torch.empty((M, d.N), dtype=torch.bfloat16, device=dev)
+        for i in range(warmup):
+            nv.quantize(x, "per_row", out=a)
+            nv.gemm(a, ws[i % rotate], torch.bfloat16, out=y)
+        torch.cuda.synchronize()
+        evs = [_events(3) for _ in range(steps)]
+        for i in range(steps):
+            evs[i][0].record()
+            nv.quantize(x, "per_row", out=a)
+            evs[i][1].record()
+            nv.gemm(a, ws[i % rotate], torch.bfloat16, out=y)
+            evs[i][2].record()
+        torch.cuda.synchronize()
+        q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        g_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        wbytes = d.N * d.K * (0.5 + 1 / 16) + 4
+        abytes = M * d.K * (0.5 + 1 / 16) + 4 * M
+        ybytes = M * d.N * 2
+        gb = (wbytes + abytes + ybytes)
+        out[f"M={M}"] = {"gemm_us": g_ms * 1e3, "quant_us": q_ms * 1e3,
+                         "gemm_gbs": gb / (g_ms * 1e-3) / 1e9,
+                         "gemm_frac_hbm": gb / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "quant_gbs": _bytes_quantize(M, d.K) / (q_ms * 1e-3) / 1e9}
+    return out
+
+
+def bench_fused(nv, steps: int, warmup: int):
+    f = workloads.FUSED
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(f.x()).to(dev).to(torch.bfloat16)
+    qs = [nv.quantize(torch.from_numpy(f.w(i)).to(dev).to(torch.bfloat16)) for i in range(len(f.widths))]
+    codes = torch.cat([q.codes for q in qs])
+    scales = torch.cat([q.scales for q in qs])
+    gl = torch.cat([q.global_scale for q in qs])
+    a = nv.quantize(x)
+    y = torch.empty((f.M, f.N), dtype=torch.bfloat16, device=dev)
+    for _ in range(warmup):
+        nv.gemm_fused_segments(a, codes, scales, f.widths, gl, torch.bfloat16, out=y)
+    torch.cuda.synchronize()
+    evs = [_events(2) for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        nv.gemm_fused_segments(a, codes, scales, f.widths, gl, torch.bfloat16, out=y)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    flops = 2.0 * f.M * f.N * f.K
+    return {"gemm_ms": ms, "gemm_tflops": flops / (ms * 1e-3) / 1e12,
+            "frac_mfma_f16": flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=["prefill", "decode", "fused"], default="prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM bytes per GEMM launch measured with rocprofv3 counters")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this library's hot path is single-GPU data parallel "
+              f"(every GPU runs the same kernels on its own tokens); --gpus {args.gpus} is not "
+              f"supported.", file=sys.stderr)
+        return 2
+    import nvfp4_w4a4_block_amd as nv
+
+    if args.workload == "decode":
+        print(json.dumps({"workload": "decode", "results": bench_decode(nv, args.steps, args.warmup)}))
+        return 0
+    if args.workload == "fused":
+        print(json.dumps({"workload": "fused", "results": bench_fused(nv, args.steps, args.warmup)}))
+        return 0
+
+    res, (p, w) = bench_prefill(nv, args.steps, args.warmup)
+    print(f"[bench] prefill: step {res['ms_per_step']:.3f} ms, gemm {res['gemm_ms']:.3f} ms "
+          f"({res['gemm_tflops']:.1f} TFLOP/s), quantize {res['quant_ms'] * 1e3:.1f} us "
+          f"({res['quant_gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            t = json.load(open(args.traffic_json))
+            traffic = t.get("prefill_gemm_bytes_per_launch")
+        except (ValueError, OSError):
+            traffic = None
+    value = res["flops"] / (res["ms_per_step"] * 1e-3) / 1e12
+    line = {
+        "metric": "NVFP4 W4A4 GEMM TFLOP/s @M=4096 + quantize GB/s, as % of roofline",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "prefill up-projection: per-tensor NVFP4 quantize of X[4096x5120] bf16 + "
+                               "NVFP4 GEMM Y[4096x17408]=X.W^T (K=5120), W pre-quantized, bf16 output",
+                   "M": p.M, "N": p.N, "K": p.K,
+                   "compute": "exact E2M1xE4M3 dequant to fp16, fp16 MFMA, fp32 accumulation"},
+        "roofline": {"bound": "mfma", "achieved": round(res["gemm_tflops"], 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(res["gemm_tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": traffic},
+        "components": {
+            "gemm": {"ms": round(res["gemm_ms"], 4), "tflops": round(res["gemm_tflops"], 2),
+                     "frac_mfma_f16": round(res["gemm_tflops"] / MFMA_F16_PEAK_TFLOPS, 4)},
+            "quantize": {"us": round(res["quant_ms"] * 1e3, 2), "gbs": round(res["quant_gbs"], 1),
+                         "frac_hbm": round(res["quant_gbs"] / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes": res["qbytes"]},
+        },
+        "context": {"pages": "17.5 GiB NVFP4 checkpoint and +14-19% prefill vs the other recipes compared; "
+                             "hardware not stated"},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_prefill(p)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

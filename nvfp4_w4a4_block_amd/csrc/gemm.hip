@@ -67,54 +67,47 @@ __device__ __forceinline__ half2_t pair_of_byte(uint32_t dw, int k) {
 
 constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int kRowBytes = BK / 2;           // 64 B of codes per row per K step
-constexpr int kRowStride = kRowBytes + 16;  // padded LDS row: conflict-free 16 B reads
-constexpr int kCodeTile = BM * kRowStride;  // bytes per operand per stage
+constexpr int kCodeTile = BM * kRowBytes;   // bytes of codes per operand per stage
 constexpr int kScaleTile = BM * 8;          // 8 scale bytes per row per K step
 constexpr int kStageBytes = 2 * kCodeTile + 2 * kScaleTile;
+constexpr int kStages = 2;
 constexpr int kPrefillThreads = 256;
 
-struct StageRegs {
-  uint4 a[4], b[4];
-  uint2 sa, sb;
-};
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Scale bytes of one row for one K step [b0..b7] reordered to [b0 b1 b4 b5 | b2 b3 b6 b7]
-// so that lane half h reads its four bytes (blocks 2h, 2h+1 of both 64-wide chunks) as one
-// dword.
-__device__ __forceinline__ uint2 permute_scales(uint2 s) {
-  return make_uint2(__builtin_amdgcn_perm(s.y, s.x, 0x05040100u), __builtin_amdgcn_perm(s.y, s.x, 0x07060302u));
-}
+// LDS layout of a stage: codes of A (256 rows x 64 B), codes of W, scale bytes of A
+// (256 rows x 8 B), scale bytes of W.  Rows of codes are unpadded; the four 16 B slots of a
+// row are XOR-swizzled with slot_swizzle(row) so that the fragment reads (32 rows, one slot
+// each) hit distinct LDS banks for both 128 B and 256 B per cycle bank layouts.
+__device__ __forceinline__ int slot_swizzle(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
-__device__ __forceinline__ void load_stage(const GemmArgs& g, int m0, int n0, int kt, StageRegs& r) {
-  const int t = threadIdx.x;
+// Enqueue the copy of K step kt of both operands straight into LDS (no registers): each
+// wavefront-wide load writes 1 KB (codes) or 256 B (scales) of consecutive LDS.
+__device__ __forceinline__ void load_stage_lds(const GemmArgs& g, int m0, int n0, int kt, uint8_t* stage) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t kb = (int64_t)g.K / 2, ks = (int64_t)g.K / 16;
-  const int seg16 = t & 3;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int row = (t >> 2) + 64 * j;
+    const int chunk = j * 4 + wave;                  // 1 KB chunk = 16 rows
+    const int row = chunk * 16 + (lane >> 2);
+    const int seg = (lane & 3) ^ slot_swizzle(row);  // logical 16 B segment stored in slot lane&3
     const int am = min(m0 + row, g.M - 1), wn = min(n0 + row, g.N - 1);
-    r.a[j] = *reinterpret_cast<const uint4*>(g.a_codes + am * kb + kt * kRowBytes + seg16 * 16);
-    r.b[j] = *reinterpret_cast<const uint4*>(g.w_codes + wn * kb + kt * kRowBytes + seg16 * 16);
+    __builtin_amdgcn_global_load_lds(g.a_codes + am * kb + kt * kRowBytes + seg * 16,
+                                     (lds_void_t*)(stage + chunk * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(g.w_codes + wn * kb + kt * kRowBytes + seg * 16,
+                                     (lds_void_t*)(stage + kCodeTile + chunk * 1024), 16, 0, 0);
   }
-  const int am = min(m0 + t, g.M - 1), wn = min(n0 + t, g.N - 1);
-  r.sa = *reinterpret_cast<const uint2*>(g.a_scales + am * ks + kt * 8);
-  r.sb = *reinterpret_cast<const uint2*>(g.w_scales + wn * ks + kt * 8);
-}
-
-__device__ __forceinline__ void store_stage(uint8_t* lds, const StageRegs& r) {
-  const int t = threadIdx.x;
-  uint8_t* ca = lds;
-  uint8_t* cb = lds + kCodeTile;
-  uint8_t* sa = lds + 2 * kCodeTile;
-  uint8_t* sb = sa + kScaleTile;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = (t >> 2) + 64 * j;
-    *reinterpret_cast<uint4*>(ca + row * kRowStride + (t & 3) * 16) = r.a[j];
-    *reinterpret_cast<uint4*>(cb + row * kRowStride + (t & 3) * 16) = r.b[j];
+  for (int j = 0; j < 2; ++j) {
+    const int chunk = j * 4 + wave;                  // 256 B chunk = 32 rows x 8 B
+    const int dw = chunk * 64 + lane;
+    const int row = dw >> 1, half = dw & 1;
+    const int am = min(m0 + row, g.M - 1), wn = min(n0 + row, g.N - 1);
+    __builtin_amdgcn_global_load_lds(g.a_scales + am * ks + kt * 8 + half * 4,
+                                     (lds_void_t*)(stage + 2 * kCodeTile + chunk * 256), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(g.w_scales + wn * ks + kt * 8 + half * 4,
+                                     (lds_void_t*)(stage + 2 * kCodeTile + kScaleTile + chunk * 256), 4, 0, 0);
   }
-  *reinterpret_cast<uint2*>(sa + t * 8) = permute_scales(r.sa);
-  *reinterpret_cast<uint2*>(sb + t * 8) = permute_scales(r.sb);
 }
 
 // Tile index -> (tile_m, tile_n).  Workgroups are dispatched round-robin over the 8 XCDs;
@@ -135,6 +128,21 @@ __device__ __forceinline__ void tile_coords(int i, int tiles_m, int tiles_n, int
   tn = in / gsize;
 }
 
+// Dequantize the fragments of one 16-deep K step (step s of chunk c) for the 4 A and 4 W
+// row groups of this wavefront: dword s of each lane's 16 B of codes, scaled by the pair
+// for block (2h + s/2) of the chunk.
+__device__ __forceinline__ void dequant_step(const uint4 (&qa)[4], const uint4 (&qb)[4], const half2_t (&pa)[4][2],
+                                             const half2_t (&pb)[4][2], int s, half8_t (&fa)[4],
+                                             half8_t (&fb)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t wa = s == 0 ? qa[i].x : s == 1 ? qa[i].y : s == 2 ? qa[i].z : qa[i].w;
+    const uint32_t wb = s == 0 ? qb[i].x : s == 1 ? qb[i].y : s == 2 ? qb[i].z : qb[i].w;
+    fa[i] = dequant8_f16(wa, pa[i][s >> 1]);
+    fb[i] = dequant8_f16(wb, pb[i][s >> 1]);
+  }
+}
+
 __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(GemmArgs g) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
@@ -145,6 +153,8 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(GemmAr
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
   const int r = lane & 31, h = lane >> 5;
+  const int swz = slot_swizzle(r);                 // rows wm + 32 i + r share r's swizzle
+  const int slot0 = (h ^ swz) * 16, slot1 = ((2 + h) ^ swz) * 16;
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -153,51 +163,76 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(GemmAr
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
   const int nk = g.K / BK;
-  StageRegs regs;
-  load_stage(g, m0, n0, 0, regs);
-  store_stage(lds, regs);
-  __syncthreads();
+  load_stage_lds(g, m0, n0, 0, lds);
 
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load_stage(g, m0, n0, kt + 1, regs);
-    const uint8_t* buf = lds + (kt & 1) * kStageBytes;
-    const uint8_t* ca = buf;
-    const uint8_t* cb = buf + kCodeTile;
-    const uint8_t* sa_t = buf + 2 * kCodeTile;
-    const uint8_t* sb_t = sa_t + kScaleTile;
-    uint32_t sa[4], sb[4];
+    // Stage kt has landed once this wave's copies are done and every wave has passed the
+    // barrier; the barrier also retires all reads of the buffer refilled below.
+    __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
+    __syncthreads();
+    if (kt + 1 < nk) load_stage_lds(g, m0, n0, kt + 1, lds + ((kt + 1) % kStages) * kStageBytes);
+    const uint8_t* buf = lds + (kt % kStages) * kStageBytes;
+    const uint8_t* ca = buf + (wm + r) * kRowBytes;
+    const uint8_t* cb = buf + kCodeTile + (wn + r) * kRowBytes;
+    const uint8_t* sa_t = buf + 2 * kCodeTile + (wm + r) * 8;
+    const uint8_t* sb_t = buf + 2 * kCodeTile + kScaleTile + (wn + r) * 8;
+    uint2 sa[4], sb[4];
+    uint4 qa[4], qb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sa[i] = *reinterpret_cast<const uint32_t*>(sa_t + (wm + 32 * i + r) * 8 + 4 * h);
-      sb[i] = *reinterpret_cast<const uint32_t*>(sb_t + (wn + 32 * i + r) * 8 + 4 * h);
+      sa[i] = *reinterpret_cast<const uint2*>(sa_t + 32 * i * 8);
+      sb[i] = *reinterpret_cast<const uint2*>(sb_t + 32 * i * 8);
+      qa[i] = *reinterpret_cast<const uint4*>(ca + 32 * i * kRowBytes + slot0);
+      qb[i] = *reinterpret_cast<const uint4*>(cb + 32 * i * kRowBytes + slot0);
     }
+    // Lane half h covers blocks 2h and 2h+1 of each 64-wide chunk: bytes 2h and 2h+1 of the
+    // chunk's scale dword (.x for the first chunk, .y for the second).
+    half2_t pa[4][2], pb[4][2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      uint4 qa[4], qb[4];
+    for (int i = 0; i < 4; ++i) {
+      pa[i][0] = pair_of_byte(sa[i].x, 2 * h);
+      pa[i][1] = pair_of_byte(sa[i].x, 2 * h + 1);
+      pb[i][0] = pair_of_byte(sb[i].x, 2 * h);
+      pb[i][1] = pair_of_byte(sb[i].x, 2 * h + 1);
+    }
+    half8_t fa[4], fb[4];
+    dequant_step(qa, qb, pa, pb, 0, fa, fb);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        qa[i] = *reinterpret_cast<const uint4*>(ca + (wm + 32 * i + r) * kRowStride + c * 32 + h * 16);
-        qb[i] = *reinterpret_cast<const uint4*>(cb + (wn + 32 * i + r) * kRowStride + c * 32 + h * 16);
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        half8_t fa[4], fb[4];
+    for (int step = 0; step < 8; ++step) {
+      __builtin_amdgcn_sched_barrier(0);
+      half8_t na[4], nb[4];
+      if (step == 3) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t wa = s == 0 ? qa[i].x : s == 1 ? qa[i].y : s == 2 ? qa[i].z : qa[i].w;
-          const uint32_t wb = s == 0 ? qb[i].x : s == 1 ? qb[i].y : s == 2 ? qb[i].z : qb[i].w;
-          fa[i] = dequant8_f16(wa, pair_of_byte(sa[i], 2 * c + (s >> 1)));
-          fb[i] = dequant8_f16(wb, pair_of_byte(sb[i], 2 * c + (s >> 1)));
+          qa[i] = *reinterpret_cast<const uint4*>(ca + 32 * i * kRowBytes + slot1);
+          qb[i] = *reinterpret_cast<const uint4*>(cb + 32 * i * kRowBytes + slot1);
+          pa[i][0] = pair_of_byte(sa[i].y, 2 * h);
+          pa[i][1] = pair_of_byte(sa[i].y, 2 * h + 1);
+          pb[i][0] = pair_of_byte(sb[i].y, 2 * h);
+          pb[i][1] = pair_of_byte(sb[i].y, 2 * h + 1);
         }
+      }
+      if (step < 7) dequant_step(qa, qb, pa, pb, (step + 1) & 3, na, nb);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      // Interleave: one MFMA, then four VALU ops of the next step's dequantization.
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      if (step < 7) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          fa[i] = na[i];
+          fb[i] = nb[i];
+        }
       }
     }
-    if (kt + 1 < nk) store_stage(lds + ((kt + 1) & 1) * kStageBytes, regs);
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Epilogue: y = (acc * s_gA[m]) * s_gW[seg(n)].
@@ -338,18 +373,18 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
   } else if (M <= 16) {
     gemm_decode_kernel<<<(unsigned)((N + 15) / 16), kDecodeThreads, 0, stream>>>(g);
   } else {
-    // The 88 KB of dynamic LDS exceed the default limit; raise it once per device.
+    // The 72 KB of dynamic LDS exceed the default limit; raise it once per device.
     static bool attr_set[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return NVFP4_ERR_HIP;
     if (!attr_set[dev]) {
       if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_prefill_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStageBytes) != hipSuccess)
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kStages * kStageBytes) != hipSuccess)
         return NVFP4_ERR_HIP;
       attr_set[dev] = true;
     }
     const int tiles = (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-    gemm_prefill_kernel<<<tiles, kPrefillThreads, 2 * kStageBytes, stream>>>(g);
+    gemm_prefill_kernel<<<tiles, kPrefillThreads, kStages * kStageBytes, stream>>>(g);
   }
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
