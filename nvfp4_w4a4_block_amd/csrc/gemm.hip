@@ -65,29 +65,37 @@ __device__ __forceinline__ half2_t pair_of_byte(uint32_t dw, int k) {
 
 // ------------------------------------------------------------------ prefill kernel
 
-constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int BK = 128;
 constexpr int kRowBytes = BK / 2;           // 64 B of codes per row per K step
-constexpr int kCodeTile = BM * kRowBytes;   // bytes of codes per operand per stage
-constexpr int kScaleTile = BM * 8;          // 8 scale bytes per row per K step
-constexpr int kStageBytes = 2 * kCodeTile + 2 * kScaleTile;
 constexpr int kStages = 2;
 constexpr int kPrefillThreads = 256;
 
+// Stage layout for a T x T output tile: codes of A (T rows x 64 B), codes of W, scale bytes
+// of A (T rows x 8 B), scale bytes of W.
+template <int T> struct TileCfg {
+  static constexpr int kCodeTile = T * kRowBytes;
+  static constexpr int kScaleTile = T * 8;
+  static constexpr int kStageBytes = 2 * kCodeTile + 2 * kScaleTile;
+  static constexpr int F = T / 64;           // MFMA 32x32 tiles per wavefront per dimension
+};
+constexpr int kPrefillLds = kStages * TileCfg<256>::kStageBytes;
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// LDS layout of a stage: codes of A (256 rows x 64 B), codes of W, scale bytes of A
-// (256 rows x 8 B), scale bytes of W.  Rows of codes are unpadded; the four 16 B slots of a
-// row are XOR-swizzled with slot_swizzle(row) so that the fragment reads (32 rows, one slot
-// each) hit distinct LDS banks for both 128 B and 256 B per cycle bank layouts.
+// Rows of codes are unpadded; the four 16 B slots of a row are XOR-swizzled with
+// slot_swizzle(row) so that the fragment reads (32 rows, one slot each) hit distinct LDS
+// banks for both 128 B and 256 B per cycle bank layouts.
 __device__ __forceinline__ int slot_swizzle(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
 // Enqueue the copy of K step kt of both operands straight into LDS (no registers): each
 // wavefront-wide load writes 1 KB (codes) or 256 B (scales) of consecutive LDS.
+template <int T>
 __device__ __forceinline__ void load_stage_lds(const GemmArgs& g, int m0, int n0, int kt, uint8_t* stage) {
+  using C = TileCfg<T>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t kb = (int64_t)g.K / 2, ks = (int64_t)g.K / 16;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < T / 64; ++j) {
     const int chunk = j * 4 + wave;                  // 1 KB chunk = 16 rows
     const int row = chunk * 16 + (lane >> 2);
     const int seg = (lane & 3) ^ slot_swizzle(row);  // logical 16 B segment stored in slot lane&3
@@ -95,18 +103,18 @@ __device__ __forceinline__ void load_stage_lds(const GemmArgs& g, int m0, int n0
     __builtin_amdgcn_global_load_lds(g.a_codes + am * kb + kt * kRowBytes + seg * 16,
                                      (lds_void_t*)(stage + chunk * 1024), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(g.w_codes + wn * kb + kt * kRowBytes + seg * 16,
-                                     (lds_void_t*)(stage + kCodeTile + chunk * 1024), 16, 0, 0);
+                                     (lds_void_t*)(stage + C::kCodeTile + chunk * 1024), 16, 0, 0);
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < T / 128; ++j) {
     const int chunk = j * 4 + wave;                  // 256 B chunk = 32 rows x 8 B
     const int dw = chunk * 64 + lane;
     const int row = dw >> 1, half = dw & 1;
     const int am = min(m0 + row, g.M - 1), wn = min(n0 + row, g.N - 1);
     __builtin_amdgcn_global_load_lds(g.a_scales + am * ks + kt * 8 + half * 4,
-                                     (lds_void_t*)(stage + 2 * kCodeTile + chunk * 256), 4, 0, 0);
+                                     (lds_void_t*)(stage + 2 * C::kCodeTile + chunk * 256), 4, 0, 0);
     __builtin_amdgcn_global_load_lds(g.w_scales + wn * ks + kt * 8 + half * 4,
-                                     (lds_void_t*)(stage + 2 * kCodeTile + kScaleTile + chunk * 256), 4, 0, 0);
+                                     (lds_void_t*)(stage + 2 * C::kCodeTile + C::kScaleTile + chunk * 256), 4, 0, 0);
   }
 }
 
@@ -128,14 +136,15 @@ __device__ __forceinline__ void tile_coords(int i, int tiles_m, int tiles_n, int
   tn = in / gsize;
 }
 
-// Dequantize the fragments of one 16-deep K step (step s of chunk c) for the 4 A and 4 W
-// row groups of this wavefront: dword s of each lane's 16 B of codes, scaled by the pair
-// for block (2h + s/2) of the chunk.
-__device__ __forceinline__ void dequant_step(const uint4 (&qa)[4], const uint4 (&qb)[4], const half2_t (&pa)[4][2],
-                                             const half2_t (&pb)[4][2], int s, half8_t (&fa)[4],
-                                             half8_t (&fb)[4]) {
+// Dequantize the fragments of one 16-deep K step (step s of a 64-wide chunk) for the F A
+// and F W row groups of this wavefront: dword s of each lane's 16 B of codes, scaled by
+// the pair for block (2h + s/2) of the chunk.
+template <int F>
+__device__ __forceinline__ void dequant_step(const uint4 (&qa)[F], const uint4 (&qb)[F], const half2_t (&pa)[F][2],
+                                             const half2_t (&pb)[F][2], int s, half8_t (&fa)[F],
+                                             half8_t (&fb)[F]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < F; ++i) {
     const uint32_t wa = s == 0 ? qa[i].x : s == 1 ? qa[i].y : s == 2 ? qa[i].z : qa[i].w;
     const uint32_t wb = s == 0 ? qb[i].x : s == 1 ? qb[i].y : s == 2 ? qb[i].z : qb[i].w;
     fa[i] = dequant8_f16(wa, pa[i][s >> 1]);
@@ -143,43 +152,41 @@ __device__ __forceinline__ void dequant_step(const uint4 (&qa)[4], const uint4 (
   }
 }
 
-__global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(GemmArgs g) {
-  extern __shared__ __align__(16) uint8_t lds[];
-  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
-  int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-
+// One T x T output tile at (m0, n0): 4 wavefronts as 2 x 2, each (T/2) x (T/2) outputs.
+template <int T>
+__device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, int m0, int n0) {
+  using C = TileCfg<T>;
+  constexpr int F = C::F;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const int wm = (wave >> 1) * (T / 2), wn = (wave & 1) * (T / 2);
   const int r = lane & 31, h = lane >> 5;
   const int swz = slot_swizzle(r);                 // rows wm + 32 i + r share r's swizzle
   const int slot0 = (h ^ swz) * 16, slot1 = ((2 + h) ^ swz) * 16;
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[F][F];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < F; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+    for (int j = 0; j < F; ++j) acc[i][j] = f32x16_t{};
 
   const int nk = g.K / BK;
-  load_stage_lds(g, m0, n0, 0, lds);
+  load_stage_lds<T>(g, m0, n0, 0, lds);
 
   for (int kt = 0; kt < nk; ++kt) {
     // Stage kt has landed once this wave's copies are done and every wave has passed the
     // barrier; the barrier also retires all reads of the buffer refilled below.
     __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
     __syncthreads();
-    if (kt + 1 < nk) load_stage_lds(g, m0, n0, kt + 1, lds + ((kt + 1) % kStages) * kStageBytes);
-    const uint8_t* buf = lds + (kt % kStages) * kStageBytes;
+    if (kt + 1 < nk) load_stage_lds<T>(g, m0, n0, kt + 1, lds + ((kt + 1) % kStages) * C::kStageBytes);
+    const uint8_t* buf = lds + (kt % kStages) * C::kStageBytes;
     const uint8_t* ca = buf + (wm + r) * kRowBytes;
-    const uint8_t* cb = buf + kCodeTile + (wn + r) * kRowBytes;
-    const uint8_t* sa_t = buf + 2 * kCodeTile + (wm + r) * 8;
-    const uint8_t* sb_t = buf + 2 * kCodeTile + kScaleTile + (wn + r) * 8;
-    uint2 sa[4], sb[4];
-    uint4 qa[4], qb[4];
+    const uint8_t* cb = buf + C::kCodeTile + (wn + r) * kRowBytes;
+    const uint8_t* sa_t = buf + 2 * C::kCodeTile + (wm + r) * 8;
+    const uint8_t* sb_t = buf + 2 * C::kCodeTile + C::kScaleTile + (wn + r) * 8;
+    uint2 sa[F], sb[F];
+    uint4 qa[F], qb[F];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < F; ++i) {
       sa[i] = *reinterpret_cast<const uint2*>(sa_t + 32 * i * 8);
       sb[i] = *reinterpret_cast<const uint2*>(sb_t + 32 * i * 8);
       qa[i] = *reinterpret_cast<const uint4*>(ca + 32 * i * kRowBytes + slot0);
@@ -187,23 +194,23 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(GemmAr
     }
     // Lane half h covers blocks 2h and 2h+1 of each 64-wide chunk: bytes 2h and 2h+1 of the
     // chunk's scale dword (.x for the first chunk, .y for the second).
-    half2_t pa[4][2], pb[4][2];
+    half2_t pa[F][2], pb[F][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < F; ++i) {
       pa[i][0] = pair_of_byte(sa[i].x, 2 * h);
       pa[i][1] = pair_of_byte(sa[i].x, 2 * h + 1);
       pb[i][0] = pair_of_byte(sb[i].x, 2 * h);
       pb[i][1] = pair_of_byte(sb[i].x, 2 * h + 1);
     }
-    half8_t fa[4], fb[4];
-    dequant_step(qa, qb, pa, pb, 0, fa, fb);
+    half8_t fa[F], fb[F];
+    dequant_step<F>(qa, qb, pa, pb, 0, fa, fb);
 #pragma unroll
     for (int step = 0; step < 8; ++step) {
       __builtin_amdgcn_sched_barrier(0);
-      half8_t na[4], nb[4];
+      half8_t na[F], nb[F];
       if (step == 3) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < F; ++i) {
           qa[i] = *reinterpret_cast<const uint4*>(ca + 32 * i * kRowBytes + slot1);
           qb[i] = *reinterpret_cast<const uint4*>(cb + 32 * i * kRowBytes + slot1);
           pa[i][0] = pair_of_byte(sa[i].y, 2 * h);
@@ -212,21 +219,21 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(GemmAr
           pb[i][1] = pair_of_byte(sb[i].y, 2 * h + 1);
         }
       }
-      if (step < 7) dequant_step(qa, qb, pa, pb, (step + 1) & 3, na, nb);
+      if (step < 7) dequant_step<F>(qa, qb, pa, pb, (step + 1) & 3, na, nb);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < F; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < F; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-      // Interleave: one MFMA, then four VALU ops of the next step's dequantization.
+      // Interleave: one MFMA, then the next step's dequantization spread between them.
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
+      for (int k = 0; k < F * F; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 16 / F, 0);
       }
       if (step < 7) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < F; ++i) {
           fa[i] = na[i];
           fb[i] = nb[i];
         }
@@ -236,25 +243,42 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(GemmAr
   }
 
   // Epilogue: y = (acc * s_gA[m]) * s_gW[seg(n)].
-  float sw[4];
-  int ncol[4];
+  float sw[F];
+  int ncol[F];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < F; ++j) {
     ncol[j] = n0 + wn + 32 * j + r;
     sw[j] = g.w_globals[segment_of(min(ncol[j], g.N - 1), g.seg)];
   }
   const float sa0 = g.a_global[0];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < F; ++i) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int m = m0 + wm + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
       if (m >= g.M) continue;
       const float sam = g.a_per_row ? g.a_global[m] : sa0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < F; ++j)
         if (ncol[j] < g.N) store_out(g, m, ncol[j], (acc[i][j][q] * sam) * sw[j]);
     }
+  }
+}
+
+// Workgroups [0, tiles_big) compute 256 x 256 tiles over columns [0, n_split); the rest
+// compute 128 x 128 tiles over columns [n_split, N).  Peeling the last tile columns into
+// small tiles keeps the final dispatch round from running a few large tiles on a mostly
+// idle GPU.
+__global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(GemmArgs g, int n_split, int tiles_big) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  if ((int)blockIdx.x < tiles_big) {
+    int tm, tn;
+    tile_coords(blockIdx.x, (g.M + 255) / 256, (n_split + 255) / 256, tm, tn);
+    prefill_tile<256>(g, lds, tm * 256, tn * 256);
+  } else {
+    int tm, tn;
+    tile_coords(blockIdx.x - tiles_big, (g.M + 127) / 128, (g.N - n_split + 127) / 128, tm, tn);
+    prefill_tile<128>(g, lds, tm * 128, n_split + tn * 128);
   }
 }
 
@@ -375,16 +399,31 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
   } else {
     // The 72 KB of dynamic LDS exceed the default limit; raise it once per device.
     static bool attr_set[64] = {};
+    static int cus[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return NVFP4_ERR_HIP;
     if (!attr_set[dev]) {
       if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_prefill_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kStages * kStageBytes) != hipSuccess)
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kPrefillLds) != hipSuccess)
+        return NVFP4_ERR_HIP;
+      if (hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return NVFP4_ERR_HIP;
       attr_set[dev] = true;
     }
-    const int tiles = (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-    gemm_prefill_kernel<<<tiles, kPrefillThreads, kStages * kStageBytes, stream>>>(g);
+    // One 256 x 256 tile per CU at a time.  If the last round of tiles would fill at most
+    // half of the CUs, move enough whole tile columns to 128 x 128 tiles to absorb it.
+    const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256;
+    const int64_t rem = (tm * tn) % cus[dev];
+    int64_t n_split = N, peel = 0;
+    if (rem > 0 && rem <= cus[dev] / 2) {
+      peel = (rem + tm - 1) / tm;
+      if (peel >= tn) peel = 0;
+      n_split = (tn - peel) * 256;
+    }
+    const int64_t big = tm * ((n_split + 255) / 256);
+    const int64_t small = peel ? ((M + 127) / 128) * ((N - n_split + 127) / 128) : 0;
+    gemm_prefill_kernel<<<(unsigned)(big + small), kPrefillThreads, kPrefillLds, stream>>>(g, (int)n_split,
+                                                                                          (int)big);
   }
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
