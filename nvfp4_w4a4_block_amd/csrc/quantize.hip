@@ -80,16 +80,29 @@ template <typename T>
 constexpr int kElemsPer16B = 16 / sizeof(T);
 
 // Pass 1 of the per-tensor mode: one partial max (fp32 magnitude bits) per workgroup.
-// Workgroups stride over rows, threads over the 16 B chunks of a row.
+// Contiguous input is read as a flat array of 16 B chunks, four independent loads per
+// thread per iteration; otherwise workgroups stride over rows and threads over a row.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void amax_partial_kernel(const T* __restrict__ x, int64_t rows,
                                                                  int64_t cols, int64_t ldx,
                                                                  uint32_t* __restrict__ partial) {
   const int64_t chunks = cols / kElemsPer16B<T>;
   uint32_t m = 0;
-  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-    const uint4* row = reinterpret_cast<const uint4*>(x + r * ldx);
-    for (int64_t c = threadIdx.x; c < chunks; c += kThreads) m = max(m, max_abs_bits(row[c], x));
+  if (ldx == cols) {
+    const uint4* p = reinterpret_cast<const uint4*>(x);
+    const int64_t total = rows * chunks;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    for (; i + 3 * stride < total; i += 4 * stride) {
+      const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+      m = max(m, max(max(max_abs_bits(a, x), max_abs_bits(b, x)), max(max_abs_bits(c, x), max_abs_bits(d, x))));
+    }
+    for (; i < total; i += stride) m = max(m, max_abs_bits(p[i], x));
+  } else {
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+      const uint4* row = reinterpret_cast<const uint4*>(x + r * ldx);
+      for (int64_t c = threadIdx.x; c < chunks; c += kThreads) m = max(m, max_abs_bits(row[c], x));
+    }
   }
   m = block_max_u32(m);
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
@@ -113,7 +126,33 @@ __global__ __launch_bounds__(kThreads) void row_scale_kernel(const T* __restrict
 enum Mode { kPerTensor = 0, kPerRow = 1, kGiven = 2 };
 
 // Pass 2 (or the only pass): one lane per 16-element block, flat block index over
-// rows x (cols / 16); grid-stride.
+// rows x (cols / 16).  The grid is sized to the machine (persistent workgroups), so the
+// per-tensor prologue that reduces the pass-1 partials runs once per workgroup; each
+// iteration encodes two blocks whose loads are issued together.
+template <typename T, int MODE>
+__device__ __forceinline__ void encode_one(const T* __restrict__ x, uint32_t i, uint32_t bpr, int64_t ldx,
+                                           bool dense, const FastDivU32& div_bpr, uint8_t* __restrict__ codes,
+                                           uint8_t* __restrict__ scales, const float* __restrict__ row_sg,
+                                           float sg, const uint4 (&w)[16 / kElemsPer16B<T>]) {
+  float v[16];
+#pragma unroll
+  for (int c = 0; c < 16 / kElemsPer16B<T>; ++c) widen(w[c], v + c * kElemsPer16B<T>, x);
+  float s = sg;
+  if (MODE == kPerRow) s = row_sg[fastdiv(i, div_bpr)];
+  uint32_t sb, lo, hi;
+  encode_block(v, s, sb, lo, hi);
+  reinterpret_cast<uint2*>(codes)[i] = make_uint2(lo, hi);
+  scales[i] = (uint8_t)sb;
+}
+
+template <typename T, int MODE>
+__device__ __forceinline__ const uint4* block_src(const T* __restrict__ x, uint32_t i, uint32_t bpr, int64_t ldx,
+                                                  bool dense, const FastDivU32& div_bpr) {
+  if (dense) return reinterpret_cast<const uint4*>(x + (int64_t)i * 16);
+  const uint32_t r = fastdiv(i, div_bpr), b = i - r * bpr;
+  return reinterpret_cast<const uint4*>(x + (int64_t)r * ldx + (int64_t)b * 16);
+}
+
 template <typename T, int MODE>
 __global__ __launch_bounds__(kThreads) void encode_kernel(const T* __restrict__ x, uint32_t rows,
                                                            uint32_t bpr, int64_t ldx, FastDivU32 div_bpr,
@@ -122,6 +161,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const T* __restrict__ 
                                                            float* __restrict__ global_scale,
                                                            const uint32_t* __restrict__ partial,
                                                            int npartial) {
+  constexpr int NC = 16 / kElemsPer16B<T>;        // 16 B loads per block
   float sg = 0.0f;
   if (MODE == kPerTensor) {
     uint32_t m = 0;
@@ -134,23 +174,36 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const T* __restrict__ 
   }
   const uint32_t total = rows * bpr;
   const bool dense = ldx == (int64_t)bpr * 16;
-  for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < total; i += gridDim.x * kThreads) {
-    uint32_t r = 0, b = i;
-    if (MODE == kPerRow || !dense) {
-      r = fastdiv(i, div_bpr);
-      b = i - r * bpr;
-    }
-    const T* src = dense ? x + (int64_t)i * 16 : x + (int64_t)r * ldx + (int64_t)b * 16;
-    const uint4* p = reinterpret_cast<const uint4*>(src);
-    float v[16];
+  const uint32_t stride = gridDim.x * kThreads;
+  uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+  for (; i + stride < total; i += 2 * stride) {
+    const uint4* p0 = block_src<T, MODE>(x, i, bpr, ldx, dense, div_bpr);
+    const uint4* p1 = block_src<T, MODE>(x, i + stride, bpr, ldx, dense, div_bpr);
+    uint4 w0[NC], w1[NC];
 #pragma unroll
-    for (int c = 0; c < 16 / kElemsPer16B<T>; ++c) widen(p[c], v + c * kElemsPer16B<T>, x);
-    const float s = MODE == kPerRow ? global_scale[r] : sg;
-    uint32_t sb, lo, hi;
-    encode_block(v, s, sb, lo, hi);
-    reinterpret_cast<uint2*>(codes)[i] = make_uint2(lo, hi);
-    scales[i] = (uint8_t)sb;
+    for (int c = 0; c < NC; ++c) {
+      w0[c] = p0[c];
+      w1[c] = p1[c];
+    }
+    encode_one<T, MODE>(x, i, bpr, ldx, dense, div_bpr, codes, scales, global_scale, sg, w0);
+    encode_one<T, MODE>(x, i + stride, bpr, ldx, dense, div_bpr, codes, scales, global_scale, sg, w1);
   }
+  if (i < total) {
+    const uint4* p0 = block_src<T, MODE>(x, i, bpr, ldx, dense, div_bpr);
+    uint4 w0[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) w0[c] = p0[c];
+    encode_one<T, MODE>(x, i, bpr, ldx, dense, div_bpr, codes, scales, global_scale, sg, w0);
+  }
+}
+
+int num_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev] && hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 256;
+  return cus[dev];
 }
 
 template <typename T>
@@ -167,13 +220,19 @@ int launch_typed(const T* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* c
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
   }
   if (rows == 0) return NVFP4_OK;
+  const int cus = num_cus();
   const uint32_t want = (uint32_t)((total + kThreads - 1) / kThreads);
-  const uint32_t grid = want < 8192u ? want : 8192u;   // grid-stride beyond 2M blocks
+  const uint32_t grid = want < (uint32_t)(8 * cus) ? want : (uint32_t)(8 * cus);
   const FastDivU32 fd = make_fastdiv(bpr);
   switch (mode) {
     case kPerTensor: {
       uint32_t* partial = static_cast<uint32_t*>(workspace);
-      const int np = (int)(rows < kMaxPartials ? rows : kMaxPartials);
+      const int64_t chunks16 = rows * (cols / kElemsPer16B<T>);
+      int64_t np64 = (chunks16 + 4 * kThreads - 1) / (4 * kThreads);
+      if (ldx != cols) np64 = rows;
+      int64_t cap = 4 * (int64_t)cus;
+      if (cap > kMaxPartials) cap = kMaxPartials;
+      const int np = (int)(np64 < cap ? np64 : cap);     // <= kMaxPartials: fits the workspace
       amax_partial_kernel<T><<<np, kThreads, 0, stream>>>(x, rows, cols, ldx, partial);
       encode_kernel<T, kPerTensor><<<grid, kThreads, 0, stream>>>(x, (uint32_t)rows, bpr, ldx, fd, codes,
                                                                   scales, global_scale, partial, np);
@@ -196,10 +255,9 @@ int launch_typed(const T* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* c
 
 }  // namespace
 
-size_t quantize_workspace_bytes(int64_t rows, int64_t, int mode) {
-  if (mode != kPerTensor) return 0;
-  const int64_t np = rows < kMaxPartials ? rows : kMaxPartials;
-  return (size_t)(np > 0 ? np : 1) * sizeof(uint32_t);
+size_t quantize_workspace_bytes(int64_t, int64_t, int mode) {
+  // one partial max per pass-1 workgroup, at most kMaxPartials of them
+  return mode == kPerTensor ? (size_t)kMaxPartials * sizeof(uint32_t) : 0;
 }
 
 int launch_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, uint8_t* codes,
