@@ -284,61 +284,130 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(GemmAr
 
 // ------------------------------------------------------------------ decode kernel
 
-constexpr int kDecodeWaves = 8;
-constexpr int kDecodeThreads = 64 * kDecodeWaves;
+// Packed operands of one 128-wide K chunk for one lane: 16 B of codes and the 2 scale bytes
+// of the lane's two 16-element blocks, for A (token row rr) and both W row groups.
+struct DecodeChunk {
+  uint4 a, w0, w1;
+  uint32_t as, ws0, ws1;
+};
 
-__global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(GemmArgs g) {
-  __shared__ float red[kDecodeWaves][64][4];
+__device__ __forceinline__ void decode_load(const uint8_t* ac, const uint8_t* asc, bool arow, const uint8_t* wc0,
+                                            const uint8_t* wsc0, const uint8_t* wc1, const uint8_t* wsc1, int c,
+                                            DecodeChunk& d) {
+  d.w0 = *reinterpret_cast<const uint4*>(wc0 + c * 64);
+  d.w1 = *reinterpret_cast<const uint4*>(wc1 + c * 64);
+  d.ws0 = *reinterpret_cast<const uint16_t*>(wsc0 + c * 8);
+  d.ws1 = *reinterpret_cast<const uint16_t*>(wsc1 + c * 8);
+  if (arow) {
+    d.a = *reinterpret_cast<const uint4*>(ac + c * 64);
+    d.as = *reinterpret_cast<const uint16_t*>(asc + c * 8);
+  } else {
+    d.a = make_uint4(0, 0, 0, 0);
+    d.as = 0;
+  }
+}
+
+// 4 MFMA 16x16x32 steps per W row group; one dequantized A fragment serves both groups.
+__device__ __forceinline__ void decode_mma(const DecodeChunk& d, f32x4_t& acc0, f32x4_t& acc1) {
+  const half2_t pa0 = pair_of_byte(d.as, 0), pa1 = pair_of_byte(d.as, 1);
+  const half2_t p00 = pair_of_byte(d.ws0, 0), p01 = pair_of_byte(d.ws0, 1);
+  const half2_t p10 = pair_of_byte(d.ws1, 0), p11 = pair_of_byte(d.ws1, 1);
+  const uint32_t aw[4] = {d.a.x, d.a.y, d.a.z, d.a.w};
+  const uint32_t w0[4] = {d.w0.x, d.w0.y, d.w0.z, d.w0.w};
+  const uint32_t w1[4] = {d.w1.x, d.w1.y, d.w1.z, d.w1.w};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const half8_t fa = dequant8_f16(aw[s], s < 2 ? pa0 : pa1);
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, dequant8_f16(w0[s], s < 2 ? p00 : p01), acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, dequant8_f16(w1[s], s < 2 ? p10 : p11), acc1, 0, 0, 0);
+  }
+}
+
+// M <= 16 tokens: memory-bound streaming of W, split along K over the whole machine.
+// Workgroup (x, y) owns W rows [32x, 32x + 32) and K chunks [y nc / S, (y+1) nc / S); its 4
+// wavefronts split that range further, keep four chunks of loads in flight each, and reduce
+// their 16x16 tiles (token x W row) through LDS in a fixed order.  The workgroup's fp32
+// partial is written to the workspace; gemm_decode_reduce sums the S partials in order.
+constexpr int kDecodeThreads = 256;
+constexpr int kDecodeWaves = kDecodeThreads / 64;
+constexpr int kDecodeRows = 32;             // W rows per workgroup: two 16-row MFMA groups
+constexpr int kDecodeMaxSplit = 32;
+
+__global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(GemmArgs g, float* __restrict__ partial) {
+  __shared__ f32x4_t red[kDecodeWaves][2][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rr = lane & 15, grp = lane >> 4;
-  const int n0 = blockIdx.x * 16;
+  const int n0 = blockIdx.x * kDecodeRows;
+  const int split = blockIdx.y, nsplit = gridDim.y;
   const int64_t kb = (int64_t)g.K / 2, ks = (int64_t)g.K / 16;
   const int nchunks = g.K / 128;
-  const int c0 = wave * nchunks / kDecodeWaves, c1 = (wave + 1) * nchunks / kDecodeWaves;
+  const int s0 = split * nchunks / nsplit, s1 = (split + 1) * nchunks / nsplit;
+  const int c0 = s0 + wave * (s1 - s0) / kDecodeWaves, c1 = s0 + (wave + 1) * (s1 - s0) / kDecodeWaves;
 
-  const int wrow = min(n0 + rr, g.N - 1);
-  const bool arow_ok = rr < g.M;
-  const uint8_t* wc = g.w_codes + wrow * kb + grp * 16;
-  const uint8_t* wsc = g.w_scales + wrow * ks + grp * 2;
-  const uint8_t* ac = g.a_codes + (arow_ok ? rr : 0) * kb + grp * 16;
-  const uint8_t* asc = g.a_scales + (arow_ok ? rr : 0) * ks + grp * 2;
+  const int wr0 = min(n0 + rr, g.N - 1), wr1 = min(n0 + 16 + rr, g.N - 1);
+  const bool arow = rr < g.M;
+  const uint8_t* ac = g.a_codes + (arow ? rr : 0) * kb + grp * 16;
+  const uint8_t* asc = g.a_scales + (arow ? rr : 0) * ks + grp * 2;
+  const uint8_t* wc0 = g.w_codes + wr0 * kb + grp * 16;
+  const uint8_t* wsc0 = g.w_scales + wr0 * ks + grp * 2;
+  const uint8_t* wc1 = g.w_codes + wr1 * kb + grp * 16;
+  const uint8_t* wsc1 = g.w_scales + wr1 * ks + grp * 2;
 
-  f32x4_t acc = f32x4_t{};
-#pragma unroll 4
-  for (int c = c0; c < c1; ++c) {
-    const uint4 w = *reinterpret_cast<const uint4*>(wc + c * 64);
-    const uint32_t ws = *reinterpret_cast<const uint16_t*>(wsc + c * 8);
-    uint4 a = make_uint4(0, 0, 0, 0);
-    uint32_t as = 0;
-    if (arow_ok) {
-      a = *reinterpret_cast<const uint4*>(ac + c * 64);
-      as = *reinterpret_cast<const uint16_t*>(asc + c * 8);
-    }
-    const half2_t pw0 = pair_of_byte(ws, 0), pw1 = pair_of_byte(ws, 1);
-    const half2_t pa0 = pair_of_byte(as, 0), pa1 = pair_of_byte(as, 1);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(a.x, pa0), dequant8_f16(w.x, pw0), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(a.y, pa0), dequant8_f16(w.y, pw0), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(a.z, pa1), dequant8_f16(w.z, pw1), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16(a.w, pa1), dequant8_f16(w.w, pw1), acc, 0, 0, 0);
+  // Four chunks in flight per lane: chunk c is multiplied while c+1..c+3 are loading.
+  f32x4_t acc0 = f32x4_t{}, acc1 = f32x4_t{};
+  DecodeChunk q0, q1, q2, q3;
+  if (c0 + 0 < c1) decode_load(ac, asc, arow, wc0, wsc0, wc1, wsc1, c0 + 0, q0);
+  if (c0 + 1 < c1) decode_load(ac, asc, arow, wc0, wsc0, wc1, wsc1, c0 + 1, q1);
+  if (c0 + 2 < c1) decode_load(ac, asc, arow, wc0, wsc0, wc1, wsc1, c0 + 2, q2);
+  if (c0 + 3 < c1) decode_load(ac, asc, arow, wc0, wsc0, wc1, wsc1, c0 + 3, q3);
+  for (int c = c0; c < c1; c += 4) {
+    decode_mma(q0, acc0, acc1);
+    if (c + 4 < c1) decode_load(ac, asc, arow, wc0, wsc0, wc1, wsc1, c + 4, q0);
+    if (c + 1 >= c1) break;
+    decode_mma(q1, acc0, acc1);
+    if (c + 5 < c1) decode_load(ac, asc, arow, wc0, wsc0, wc1, wsc1, c + 5, q1);
+    if (c + 2 >= c1) break;
+    decode_mma(q2, acc0, acc1);
+    if (c + 6 < c1) decode_load(ac, asc, arow, wc0, wsc0, wc1, wsc1, c + 6, q2);
+    if (c + 3 >= c1) break;
+    decode_mma(q3, acc0, acc1);
+    if (c + 7 < c1) decode_load(ac, asc, arow, wc0, wsc0, wc1, wsc1, c + 7, q3);
   }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) red[wave][lane][q] = acc[q];
+  red[wave][0][lane] = acc0;
+  red[wave][1][lane] = acc1;
   __syncthreads();
-  if (wave == 0) {
-    f32x4_t s = f32x4_t{};
-    for (int w = 0; w < kDecodeWaves; ++w)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) s[q] += red[w][lane][q];
-    const int n = n0 + rr;
+  if (wave < 2) {
+    f32x4_t sum = f32x4_t{};
+    for (int w = 0; w < kDecodeWaves; ++w) sum += red[w][wave][lane];
+    const int n = n0 + 16 * wave + rr;
     if (n < g.N) {
-      const float swn = g.w_globals[segment_of(n, g.seg)];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int m = 4 * grp + q;
-        if (m < g.M) store_out(g, m, n, (s[q] * g.a_global[g.a_per_row ? m : 0]) * swn);
+        if (m < g.M) partial[((int64_t)split * g.M + m) * g.N + n] = sum[q];
       }
     }
   }
+}
+
+// Y[m, n] = ((sum over splits, in order, of the partials) * s_gA[m]) * s_gW[seg(n)].
+__global__ __launch_bounds__(256) void gemm_decode_reduce(GemmArgs g, const float* __restrict__ partial, int nsplit) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)g.M * g.N) return;
+  const int m = (int)(idx / g.N), n = (int)(idx - (int64_t)m * g.N);
+  float acc = 0.0f;
+  for (int s = 0; s < nsplit; ++s) acc += partial[(int64_t)s * g.M * g.N + idx];
+  store_out(g, m, n, (acc * g.a_global[g.a_per_row ? m : 0]) * g.w_globals[segment_of(n, g.seg)]);
+}
+
+// Number of K splits for the decode path: about 8 workgroups per CU, at most one split per
+// 128-wide K chunk.
+int decode_splits(int64_t N, int64_t K, int cus) {
+  const int64_t groups = (N + kDecodeRows - 1) / kDecodeRows;
+  int64_t s = (8 * (int64_t)cus + groups - 1) / groups;
+  if (s > K / 128) s = K / 128;
+  if (s > kDecodeMaxSplit) s = kDecodeMaxSplit;
+  return (int)(s < 1 ? 1 : s);
 }
 
 // ------------------------------------------------------------------ plain kernel
@@ -369,11 +438,24 @@ __global__ __launch_bounds__(256) void gemm_plain_kernel(GemmArgs g) {
 
 }  // namespace
 
-size_t gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  // the decode path keeps one fp32 partial of Y per K split
+  if (M < 1 || M > 16 || K % 128 != 0) return 0;
+  return (size_t)kDecodeMaxSplit * M * N * sizeof(float);
+}
+
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev] && hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 256;
+  return cus[dev];
+}
 
 int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
                 const float* a_global, int a_global_per_row, const uint8_t* w_codes, const uint8_t* w_scales,
-                const float* w_globals, const SegmentTable& seg, void* y, int y_dtype, int64_t ldy, void*,
+                const float* w_globals, const SegmentTable& seg, void* y, int y_dtype, int64_t ldy, void* workspace,
                 hipStream_t stream) {
   if (M == 0 || N == 0) return NVFP4_OK;
   GemmArgs g;
@@ -395,7 +477,11 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
     const int64_t total = M * N;
     gemm_plain_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(g);
   } else if (M <= 16) {
-    gemm_decode_kernel<<<(unsigned)((N + 15) / 16), kDecodeThreads, 0, stream>>>(g);
+    const int nsplit = decode_splits(N, K, device_cus());
+    float* partial = static_cast<float*>(workspace);
+    const dim3 grid((unsigned)((N + kDecodeRows - 1) / kDecodeRows), (unsigned)nsplit);
+    gemm_decode_kernel<<<grid, kDecodeThreads, 0, stream>>>(g, partial);
+    gemm_decode_reduce<<<(unsigned)((M * N + 255) / 256), 256, 0, stream>>>(g, partial, nsplit);
   } else {
     // The 72 KB of dynamic LDS exceed the default limit; raise it once per device.
     static bool attr_set[64] = {};

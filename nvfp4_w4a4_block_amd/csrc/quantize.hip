@@ -123,6 +123,50 @@ __global__ __launch_bounds__(kThreads) void row_scale_kernel(const T* __restrict
   }
 }
 
+// Per-row mode in one pass: one workgroup per row (strided over rows) keeps the row's blocks
+// in registers (up to MAXB per thread), reduces the row max, writes s_g[r] and encodes.
+template <typename T, int MAXB>
+__global__ __launch_bounds__(kThreads) void row_quant_kernel(const T* __restrict__ x, int64_t rows, uint32_t bpr,
+                                                              int64_t ldx, uint8_t* __restrict__ codes,
+                                                              uint8_t* __restrict__ scales,
+                                                              float* __restrict__ sg_out) {
+  constexpr int NC = 16 / kElemsPer16B<T>;
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const T* row = x + r * ldx;
+    uint4 w[MAXB][NC];
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < MAXB; ++j) {
+      const uint32_t b = threadIdx.x + j * kThreads;
+      if (b < bpr) {
+        const uint4* p = reinterpret_cast<const uint4*>(row + (int64_t)b * 16);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          w[j][c] = p[c];
+          m = max(m, max_abs_bits(w[j][c], x));
+        }
+      }
+    }
+    m = block_max_u32(m);
+    const float sg = __uint_as_float(m) / kGlobalDivisor;
+    if (threadIdx.x == 0) sg_out[r] = sg;
+#pragma unroll
+    for (int j = 0; j < MAXB; ++j) {
+      const uint32_t b = threadIdx.x + j * kThreads;
+      if (b < bpr) {
+        float v[16];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) widen(w[j][c], v + c * kElemsPer16B<T>, x);
+        uint32_t sb, lo, hi;
+        encode_block(v, sg, sb, lo, hi);
+        const int64_t i = r * (int64_t)bpr + b;
+        reinterpret_cast<uint2*>(codes)[i] = make_uint2(lo, hi);
+        scales[i] = (uint8_t)sb;
+      }
+    }
+  }
+}
+
 enum Mode { kPerTensor = 0, kPerRow = 1, kGiven = 2 };
 
 // Pass 2 (or the only pass): one lane per 16-element block, flat block index over
@@ -239,7 +283,15 @@ int launch_typed(const T* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* c
       break;
     }
     case kPerRow: {
-      const int g = (int)(rows < 4096 ? rows : 4096);
+      const int g = (int)(rows < 8 * cus ? rows : 8 * cus);
+      constexpr int kMaxB = sizeof(T) == 2 ? 8 : 4;     // blocks per thread held in registers
+      if (bpr <= (uint32_t)(kMaxB * kThreads)) {
+        if (bpr <= (uint32_t)(2 * kThreads))
+          row_quant_kernel<T, 2><<<g, kThreads, 0, stream>>>(x, rows, bpr, ldx, codes, scales, global_scale);
+        else
+          row_quant_kernel<T, kMaxB><<<g, kThreads, 0, stream>>>(x, rows, bpr, ldx, codes, scales, global_scale);
+        break;
+      }
       row_scale_kernel<T><<<g, kThreads, 0, stream>>>(x, rows, cols, ldx, global_scale);
       encode_kernel<T, kPerRow><<<grid, kThreads, 0, stream>>>(x, (uint32_t)rows, bpr, ldx, fd, codes,
                                                                scales, global_scale, nullptr, 0);
