@@ -33,6 +33,86 @@ import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
+GEMM_SOURCE = os.path.join(ROOT, "nvfp4_w4a4_block_amd", "csrc", "gemm.hip")
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_digest(path: str = GEMM_SOURCE) -> str:
+    import hashlib
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def copy_calibration(mb: int) -> None:
+    """One device-to-device copy of `mb` MiB: the reference kernel of known size that scales
+    the FETCH_SIZE / WRITE_SIZE counters of a profiling run."""
+    if mb <= 0:
+        return
+    n = mb << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.bitwise_not(src, out=dst)      # reads n bytes, writes n bytes; a unique kernel name
+    torch.cuda.synchronize()
+
+
+def summarize(prof_dir: str, out: str | None, command: str, copy_mb: int) -> int:
+    """Per-kernel statistics (and counters, if collected) from rocprofv3 result databases
+    under `prof_dir`, as a markdown table; with a copy calibration, also HBM bytes per
+    dispatch scaled by the copy kernel's reading."""
+    import glob
+    import sqlite3
+    dbs = sorted(glob.glob(os.path.join(prof_dir, "**", "*_results.db"), recursive=True))
+    if not dbs:
+        print(f"no rocprofv3 results under {prof_dir}", file=sys.stderr)
+        return 1
+    lines = [f"command: `{command}`", ""]
+    kstats, counters = {}, {}
+
+    def short(name: str) -> str:
+        name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+        return name.split("(")[0][:90]
+
+    for db in dbs:
+        c = sqlite3.connect(db)
+        for name, n, avg, mn, mx in c.execute(
+                "select name, count(*), avg(duration), min(duration), max(duration) from kernels group by name"):
+            kstats.setdefault(name, []).append((n, avg, mn, mx))
+        try:
+            for name, cn, v, n in c.execute("select kernel_name, counter_name, avg(value), count(*) "
+                                            "from counters_collection group by kernel_name, counter_name"):
+                counters.setdefault(name, {})[cn] = v
+        except sqlite3.OperationalError:
+            pass
+    if kstats:
+        lines += ["| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+        for name, rows in sorted(kstats.items(), key=lambda kv: -sum(r[0] * r[1] for r in kv[1])):
+            n = sum(r[0] for r in rows)
+            avg = sum(r[0] * r[1] for r in rows) / n
+            lines.append(f"| `{short(name)}` | {n} | {avg / 1e3:.2f} | {min(r[2] for r in rows) / 1e3:.2f} "
+                         f"| {max(r[3] for r in rows) / 1e3:.2f} |")
+    if counters:
+        names = sorted({cn for v in counters.values() for cn in v})
+        lines += ["", "| kernel | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
+        for k, v in counters.items():
+            lines.append(f"| `{short(k)}` | " + " | ".join(f"{v.get(cn, float('nan')):.4g}" for cn in names) + " |")
+        copy = [v for k, v in counters.items() if "bitwise_not" in k]
+        if copy_mb and copy:
+            true = float(copy_mb << 20)
+            lines += ["", f"Calibration: plain copy of {copy_mb} MiB (read {true:.0f} B, write {true:.0f} B)."]
+            cal = copy[0]
+            f_scale = true / (cal["FETCH_SIZE"] * 1024) if cal.get("FETCH_SIZE") else None
+            w_scale = true / (cal["WRITE_SIZE"] * 1024) if cal.get("WRITE_SIZE") else None
+            lines.append(f"Scale factors: FETCH_SIZE {f_scale}, WRITE_SIZE {w_scale} (bytes per KiB-reading / 1024).")
+            for k, v in counters.items():
+                if "FETCH_SIZE" in v or "WRITE_SIZE" in v:
+                    fb = v.get("FETCH_SIZE", 0) * 1024 * (f_scale or 0)
+                    wb = v.get("WRITE_SIZE", 0) * 1024 * (w_scale or 0)
+                    lines.append(f"- `{short(k)}`: HBM fetch {fb:.4g} B, write {wb:.4g} B per dispatch (scaled)")
+    text = "\n".join(lines) + "\n"
+    print(text)
+    if out:
+        open(out, "w").write(text)
+    return 0
 
 
 def _events(n):
@@ -91,7 +171,7 @@ def bench_prefill(nv, steps: int, warmup: int, rotate: int = 4):
     return res, (p, w)
 
 
-def cpu_baseline_prefill(p, sample_rows: int = 128):
+def cpu_baseline_prefill(p, sample_rows: int = 4096):
     """The oracle as it stands, on a bounded sample: quantize `sample_rows` rows of X under
     the tensor's global scale and compute those rows of Y against the oracle-quantized W."""
     import threadpoolctl
@@ -183,9 +263,16 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=["prefill", "decode", "fused"], default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+    ap.add_argument("--traffic-json", default=TRAFFIC_JSON,
                     help="HBM bytes per GEMM launch measured with rocprofv3 counters")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="run one device copy of this many MiB first (counter calibration)")
+    ap.add_argument("--summarize", metavar="DIR", help="summarize rocprofv3 results under DIR and exit")
+    ap.add_argument("--summary-out", help="write the --summarize markdown here")
+    ap.add_argument("--summary-command", default="", help="profiling command recorded in the summary")
     args = ap.parse_args()
+    if args.summarize:
+        return summarize(args.summarize, args.summary_out, args.summary_command, args.copy_calibration_mb)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this library's hot path is single-GPU data parallel "
               f"(every GPU runs the same kernels on its own tokens); --gpus {args.gpus} is not "
@@ -193,6 +280,7 @@ def main() -> int:
         return 2
     import nvfp4_w4a4_block_amd as nv
 
+    copy_calibration(args.copy_calibration_mb)
     if args.workload == "decode":
         print(json.dumps({"workload": "decode", "results": bench_decode(nv, args.steps, args.warmup)}))
         return 0
@@ -208,7 +296,8 @@ def main() -> int:
     if os.path.exists(args.traffic_json):
         try:
             t = json.load(open(args.traffic_json))
-            traffic = t.get("prefill_gemm_bytes_per_launch")
+            if t.get("gemm_source_sha256_16") == source_digest():
+                traffic = t.get("prefill_gemm_bytes_per_launch")
         except (ValueError, OSError):
             traffic = None
     value = res["flops"] / (res["ms_per_step"] * 1e-3) / 1e12
