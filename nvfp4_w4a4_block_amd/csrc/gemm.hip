@@ -65,16 +65,18 @@ __device__ __forceinline__ half2_t pair_of_byte(uint32_t dw, int k) {
 
 // ------------------------------------------------------------------ prefill kernel
 
-constexpr int BK = 128;
-constexpr int kRowBytes = BK / 2;           // 64 B of codes per row per K step
+constexpr int BK = 256;
+constexpr int kRowBytes = BK / 2;           // 128 B of codes per row per K step
+constexpr int kScaleRow = BK / 16;          // 16 scale bytes per row per K step
+constexpr int kChunks = BK / 64;            // 64-wide chunks per K step
 constexpr int kStages = 2;
 constexpr int kPrefillThreads = 256;
 
-// Stage layout for a T x T output tile: codes of A (T rows x 64 B), codes of W, scale bytes
-// of A (T rows x 8 B), scale bytes of W.
+// Stage layout for a T x T output tile: codes of A (T rows x 128 B), codes of W, scale bytes
+// of A (T rows x 16 B), scale bytes of W.
 template <int T> struct TileCfg {
   static constexpr int kCodeTile = T * kRowBytes;
-  static constexpr int kScaleTile = T * 8;
+  static constexpr int kScaleTile = T * kScaleRow;
   static constexpr int kStageBytes = 2 * kCodeTile + 2 * kScaleTile;
   static constexpr int F = T / 64;           // MFMA 32x32 tiles per wavefront per dimension
 };
@@ -82,23 +84,23 @@ constexpr int kPrefillLds = kStages * TileCfg<256>::kStageBytes;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Rows of codes are unpadded; the four 16 B slots of a row are XOR-swizzled with
-// slot_swizzle(row) so that the fragment reads (32 rows, one slot each) hit distinct LDS
-// banks for both 128 B and 256 B per cycle bank layouts.
-__device__ __forceinline__ int slot_swizzle(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// Rows of codes are unpadded; the eight 16 B slots of a row are XOR-swizzled with
+// slot_swizzle(row) so that fragment reads (16 consecutive rows, one slot each) hit distinct
+// LDS bank groups whether the LDS serves 128 B or 256 B per cycle.
+__device__ __forceinline__ int slot_swizzle(int row) { return (row ^ (row >> 3)) & 7; }
 
 // Enqueue the copy of K step kt of both operands straight into LDS (no registers): each
-// wavefront-wide load writes 1 KB (codes) or 256 B (scales) of consecutive LDS.
+// wavefront-wide load writes 1 KB of consecutive LDS (8 rows of codes, or 64 rows of scales).
 template <int T>
 __device__ __forceinline__ void load_stage_lds(const GemmArgs& g, int m0, int n0, int kt, uint8_t* stage) {
   using C = TileCfg<T>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t kb = (int64_t)g.K / 2, ks = (int64_t)g.K / 16;
 #pragma unroll
-  for (int j = 0; j < T / 64; ++j) {
-    const int chunk = j * 4 + wave;                  // 1 KB chunk = 16 rows
-    const int row = chunk * 16 + (lane >> 2);
-    const int seg = (lane & 3) ^ slot_swizzle(row);  // logical 16 B segment stored in slot lane&3
+  for (int j = 0; j < T / 32; ++j) {
+    const int chunk = j * 4 + wave;                  // 1 KB chunk = 8 rows
+    const int row = chunk * 8 + (lane >> 3);
+    const int seg = (lane & 7) ^ slot_swizzle(row);  // logical 16 B segment stored in slot lane&7
     const int am = min(m0 + row, g.M - 1), wn = min(n0 + row, g.N - 1);
     __builtin_amdgcn_global_load_lds(g.a_codes + am * kb + kt * kRowBytes + seg * 16,
                                      (lds_void_t*)(stage + chunk * 1024), 16, 0, 0);
@@ -106,15 +108,24 @@ __device__ __forceinline__ void load_stage_lds(const GemmArgs& g, int m0, int n0
                                      (lds_void_t*)(stage + C::kCodeTile + chunk * 1024), 16, 0, 0);
   }
 #pragma unroll
-  for (int j = 0; j < T / 128; ++j) {
-    const int chunk = j * 4 + wave;                  // 256 B chunk = 32 rows x 8 B
-    const int dw = chunk * 64 + lane;
-    const int row = dw >> 1, half = dw & 1;
+  for (int j = 0; j < T / 256; ++j) {
+    const int chunk = j * 4 + wave;                  // 1 KB chunk = 64 rows x 16 B
+    const int row = chunk * 64 + lane;
     const int am = min(m0 + row, g.M - 1), wn = min(n0 + row, g.N - 1);
-    __builtin_amdgcn_global_load_lds(g.a_scales + am * ks + kt * 8 + half * 4,
-                                     (lds_void_t*)(stage + 2 * C::kCodeTile + chunk * 256), 4, 0, 0);
-    __builtin_amdgcn_global_load_lds(g.w_scales + wn * ks + kt * 8 + half * 4,
-                                     (lds_void_t*)(stage + 2 * C::kCodeTile + C::kScaleTile + chunk * 256), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(g.a_scales + am * ks + kt * kScaleRow,
+                                     (lds_void_t*)(stage + 2 * C::kCodeTile + chunk * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(g.w_scales + wn * ks + kt * kScaleRow,
+                                     (lds_void_t*)(stage + 2 * C::kCodeTile + C::kScaleTile + chunk * 1024), 16, 0, 0);
+  }
+  if (T / 256 == 0) {   // 128-row tiles: 128 rows x 16 B = 2 KB per operand, half the waves each
+    const int row = (wave & 1) * 64 + lane;
+    const int am = min(m0 + row, g.M - 1), wn = min(n0 + row, g.N - 1);
+    if (wave < 2)
+      __builtin_amdgcn_global_load_lds(g.a_scales + am * ks + kt * kScaleRow,
+                                       (lds_void_t*)(stage + 2 * C::kCodeTile + (wave & 1) * 1024), 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(g.w_scales + wn * ks + kt * kScaleRow,
+                                       (lds_void_t*)(stage + 2 * C::kCodeTile + C::kScaleTile + (wave & 1) * 1024), 16, 0, 0);
   }
 }
 
@@ -153,6 +164,8 @@ __device__ __forceinline__ void dequant_step(const uint4 (&qa)[F], const uint4 (
 }
 
 // One T x T output tile at (m0, n0): 4 wavefronts as 2 x 2, each (T/2) x (T/2) outputs.
+// Per K step (4 chunks of 64): 16 steps of 16 deep; step s's fragments are dequantized during
+// step s-1's MFMAs, and chunk c+1's codes are read from LDS one step before first use.
 template <int T>
 __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, int m0, int n0) {
   using C = TileCfg<T>;
@@ -160,8 +173,12 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = (wave >> 1) * (T / 2), wn = (wave & 1) * (T / 2);
   const int r = lane & 31, h = lane >> 5;
-  const int swz = slot_swizzle(r);                 // rows wm + 32 i + r share r's swizzle
-  const int slot0 = (h ^ swz) * 16, slot1 = ((2 + h) ^ swz) * 16;
+  int swa[F], swb[F];
+#pragma unroll
+  for (int i = 0; i < F; ++i) {
+    swa[i] = slot_swizzle(wm + 32 * i + r);
+    swb[i] = slot_swizzle(wn + 32 * i + r);
+  }
 
   f32x16_t acc[F][F];
 #pragma unroll
@@ -181,19 +198,19 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
     const uint8_t* buf = lds + (kt % kStages) * C::kStageBytes;
     const uint8_t* ca = buf + (wm + r) * kRowBytes;
     const uint8_t* cb = buf + C::kCodeTile + (wn + r) * kRowBytes;
-    const uint8_t* sa_t = buf + 2 * C::kCodeTile + (wm + r) * 8;
-    const uint8_t* sb_t = buf + 2 * C::kCodeTile + C::kScaleTile + (wn + r) * 8;
-    uint2 sa[F], sb[F];
+    const uint8_t* sa_t = buf + 2 * C::kCodeTile + (wm + r) * kScaleRow;
+    const uint8_t* sb_t = buf + 2 * C::kCodeTile + C::kScaleTile + (wn + r) * kScaleRow;
+    // Lane half h covers blocks 2h and 2h+1 of each 64-wide chunk c: bytes 2h and 2h+1 of
+    // scale dword c.
+    uint4 sa[F], sb[F];
     uint4 qa[F], qb[F];
 #pragma unroll
     for (int i = 0; i < F; ++i) {
-      sa[i] = *reinterpret_cast<const uint2*>(sa_t + 32 * i * 8);
-      sb[i] = *reinterpret_cast<const uint2*>(sb_t + 32 * i * 8);
-      qa[i] = *reinterpret_cast<const uint4*>(ca + 32 * i * kRowBytes + slot0);
-      qb[i] = *reinterpret_cast<const uint4*>(cb + 32 * i * kRowBytes + slot0);
+      sa[i] = *reinterpret_cast<const uint4*>(sa_t + 32 * i * kScaleRow);
+      sb[i] = *reinterpret_cast<const uint4*>(sb_t + 32 * i * kScaleRow);
+      qa[i] = *reinterpret_cast<const uint4*>(ca + 32 * i * kRowBytes + ((h ^ swa[i]) << 4));
+      qb[i] = *reinterpret_cast<const uint4*>(cb + 32 * i * kRowBytes + ((h ^ swb[i]) << 4));
     }
-    // Lane half h covers blocks 2h and 2h+1 of each 64-wide chunk: bytes 2h and 2h+1 of the
-    // chunk's scale dword (.x for the first chunk, .y for the second).
     half2_t pa[F][2], pb[F][2];
 #pragma unroll
     for (int i = 0; i < F; ++i) {
@@ -205,21 +222,32 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
     half8_t fa[F], fb[F];
     dequant_step<F>(qa, qb, pa, pb, 0, fa, fb);
 #pragma unroll
-    for (int step = 0; step < 8; ++step) {
+    for (int step = 0; step < 4 * kChunks; ++step) {
       __builtin_amdgcn_sched_barrier(0);
+      const int c = step >> 2;
       half8_t na[F], nb[F];
-      if (step == 3) {
+      if ((step & 3) == 3 && c + 1 < kChunks) {
+        // scale pairs of chunk c+1 (its codes were read during the previous step)
 #pragma unroll
         for (int i = 0; i < F; ++i) {
-          qa[i] = *reinterpret_cast<const uint4*>(ca + 32 * i * kRowBytes + slot1);
-          qb[i] = *reinterpret_cast<const uint4*>(cb + 32 * i * kRowBytes + slot1);
-          pa[i][0] = pair_of_byte(sa[i].y, 2 * h);
-          pa[i][1] = pair_of_byte(sa[i].y, 2 * h + 1);
-          pb[i][0] = pair_of_byte(sb[i].y, 2 * h);
-          pb[i][1] = pair_of_byte(sb[i].y, 2 * h + 1);
+          const uint32_t da = c == 0 ? sa[i].y : c == 1 ? sa[i].z : sa[i].w;
+          const uint32_t db = c == 0 ? sb[i].y : c == 1 ? sb[i].z : sb[i].w;
+          pa[i][0] = pair_of_byte(da, 2 * h);
+          pa[i][1] = pair_of_byte(da, 2 * h + 1);
+          pb[i][0] = pair_of_byte(db, 2 * h);
+          pb[i][1] = pair_of_byte(db, 2 * h + 1);
         }
       }
-      if (step < 7) dequant_step<F>(qa, qb, pa, pb, (step + 1) & 3, na, nb);
+      if (step + 1 < 4 * kChunks) dequant_step<F>(qa, qb, pa, pb, (step + 1) & 3, na, nb);
+      if ((step & 3) == 2 && c + 1 < kChunks) {
+        // chunk c's codes are dequantized to the end now: read chunk c+1's for the next step
+        const int slot = 2 * (c + 1) + h;
+#pragma unroll
+        for (int i = 0; i < F; ++i) {
+          qa[i] = *reinterpret_cast<const uint4*>(ca + 32 * i * kRowBytes + ((slot ^ swa[i]) << 4));
+          qb[i] = *reinterpret_cast<const uint4*>(cb + 32 * i * kRowBytes + ((slot ^ swb[i]) << 4));
+        }
+      }
 #pragma unroll
       for (int i = 0; i < F; ++i)
 #pragma unroll
@@ -231,7 +259,7 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 16 / F, 0);
       }
-      if (step < 7) {
+      if (step + 1 < 4 * kChunks) {
 #pragma unroll
         for (int i = 0; i < F; ++i) {
           fa[i] = na[i];
@@ -473,7 +501,7 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
   g.y_bf16 = y_dtype == NVFP4_BF16;
   g.ldy = ldy;
   g.seg = seg;
-  if (K % 128 != 0) {
+  if (K % 128 != 0 || (M > 16 && K % BK != 0)) {
     const int64_t total = M * N;
     gemm_plain_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(g);
   } else if (M <= 16) {
@@ -483,7 +511,7 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
     gemm_decode_kernel<<<grid, kDecodeThreads, 0, stream>>>(g, partial);
     gemm_decode_reduce<<<(unsigned)((M * N + 255) / 256), 256, 0, stream>>>(g, partial, nsplit);
   } else {
-    // The 72 KB of dynamic LDS exceed the default limit; raise it once per device.
+    // The 144 KB of dynamic LDS exceed the default limit; raise it once per device.
     static bool attr_set[64] = {};
     static int cus[64] = {};
     int dev = 0;

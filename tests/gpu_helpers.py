@@ -2,7 +2,7 @@
 compare the library's outputs with the oracle.
 
 The HIP binding is imported lazily (``nv()``) so that CPU-only test collection does not
-need it; on a GPU machine a missing library makes every GPU test fail loudly."""
+need it; on a machine with a GPU a missing library makes every GPU test fail loudly."""
 from __future__ import annotations
 
 import numpy as np
