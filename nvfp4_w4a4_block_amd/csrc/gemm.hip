@@ -163,9 +163,101 @@ __device__ __forceinline__ void dequant_step(const uint4 (&qa)[F], const uint4 (
   }
 }
 
-// One T x T output tile at (m0, n0): 4 wavefronts as 2 x 2, each (T/2) x (T/2) outputs.
-// Per K step (4 chunks of 64): 16 steps of 16 deep; step s's fragments are dequantized during
-// step s-1's MFMAs, and chunk c+1's codes are read from LDS one step before first use.
+// Registers one wave carries through the K loop of a T x T tile.
+template <int T>
+struct PrefillRegs {
+  static constexpr int F = T / 64;
+  f32x16_t acc[F][F];
+  uint4 sa[F], sb[F], qa[F], qb[F];   // scale bytes of the stage, codes of the current chunk
+  half2_t pa[F][2], pb[F][2];         // scale pairs of the current chunk
+  half8_t fa[F], fb[F];               // fragments of the current step
+  int swa[F], swb[F];                 // slot swizzles of the lane's rows
+};
+
+// One 256-deep stage kt of a tile, as 16 steps of 16-deep MFMAs.  Step 12 waits for stage
+// kt+1's copies and publishes them with the stage's only barrier; right after it the copies
+// of stage kt+2 are issued into stage kt's buffer when LOAD (no wave reads that buffer after
+// step 10).  Stage kt+1's scales and first codes are read at steps 13 and 14 and its first
+// fragments dequantized during step 15, so every stage starts straight with MFMAs.  In the
+// last stage that look-ahead reads a stale buffer and its results are never used; keeping
+// it unconditional keeps the loop free of branches.
+template <int T, bool LOAD>
+__device__ __forceinline__ void prefill_stage(const GemmArgs& g, uint8_t* lds, int m0, int n0, int kt,
+                                              PrefillRegs<T>& R) {
+  using C = TileCfg<T>;
+  constexpr int F = C::F;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = (wave >> 1) * (T / 2), wn = (wave & 1) * (T / 2);
+  const int r = lane & 31, h = lane >> 5;
+  uint8_t* buf = lds + (kt & 1) * C::kStageBytes;
+  const uint8_t* nbuf = lds + ((kt + 1) & 1) * C::kStageBytes;
+#pragma unroll
+  for (int step = 0; step < 4 * kChunks; ++step) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int c = step >> 2;
+    if (step == 12) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0): stage kt+1 copied by this wave
+      __syncthreads();                           // ... and by every wave
+      if (LOAD) load_stage_lds<T>(g, m0, n0, kt + 2, buf);
+    }
+    if (step == 13) {
+      const uint8_t* sa_t = nbuf + 2 * C::kCodeTile + (wm + r) * kScaleRow;
+      const uint8_t* sb_t = nbuf + 2 * C::kCodeTile + C::kScaleTile + (wn + r) * kScaleRow;
+#pragma unroll
+      for (int i = 0; i < F; ++i) {
+        R.sa[i] = *reinterpret_cast<const uint4*>(sa_t + 32 * i * kScaleRow);
+        R.sb[i] = *reinterpret_cast<const uint4*>(sb_t + 32 * i * kScaleRow);
+      }
+    }
+    if ((step & 3) == 3) {
+      // scale pairs of the next chunk (this stage's chunk c+1, or the next stage's chunk 0)
+#pragma unroll
+      for (int i = 0; i < F; ++i) {
+        const uint32_t da = c == 0 ? R.sa[i].y : c == 1 ? R.sa[i].z : c == 2 ? R.sa[i].w : R.sa[i].x;
+        const uint32_t db = c == 0 ? R.sb[i].y : c == 1 ? R.sb[i].z : c == 2 ? R.sb[i].w : R.sb[i].x;
+        R.pa[i][0] = pair_of_byte(da, 2 * h);
+        R.pa[i][1] = pair_of_byte(da, 2 * h + 1);
+        R.pb[i][0] = pair_of_byte(db, 2 * h);
+        R.pb[i][1] = pair_of_byte(db, 2 * h + 1);
+      }
+    }
+    half8_t na[F], nb[F];
+    dequant_step<F>(R.qa, R.qb, R.pa, R.pb, (step + 1) & 3, na, nb);
+    if ((step & 3) == 2) {
+      // chunk c's codes are dequantized to the end now: read the next chunk's codes
+      const uint8_t* src = c + 1 < kChunks ? buf : nbuf;
+      const int slot = c + 1 < kChunks ? 2 * (c + 1) + h : h;
+      const uint8_t* ca = src + (wm + r) * kRowBytes;
+      const uint8_t* cb = src + C::kCodeTile + (wn + r) * kRowBytes;
+#pragma unroll
+      for (int i = 0; i < F; ++i) {
+        R.qa[i] = *reinterpret_cast<const uint4*>(ca + 32 * i * kRowBytes + ((slot ^ R.swa[i]) << 4));
+        R.qb[i] = *reinterpret_cast<const uint4*>(cb + 32 * i * kRowBytes + ((slot ^ R.swb[i]) << 4));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < F; ++i)
+#pragma unroll
+      for (int j = 0; j < F; ++j)
+        R.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(R.fa[i], R.fb[j], R.acc[i][j], 0, 0, 0);
+    // Interleave: one MFMA, then the next step's dequantization spread between them.
+#pragma unroll
+    for (int k = 0; k < F * F; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 16 / F, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < F; ++i) {
+      R.fa[i] = na[i];
+      R.fb[i] = nb[i];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One T x T output tile (T = 256 or 128) on 4 waves in a 2 x 2 grid, each wave T/2 x T/2 as
+// (T/64) x (T/64) MFMA 32x32x16 f16 tiles, over the whole K range in 256-deep stages
+// double-buffered in LDS.
 template <int T>
 __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, int m0, int n0) {
   using C = TileCfg<T>;
@@ -173,102 +265,48 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = (wave >> 1) * (T / 2), wn = (wave & 1) * (T / 2);
   const int r = lane & 31, h = lane >> 5;
-  int swa[F], swb[F];
+  PrefillRegs<T> R;
 #pragma unroll
   for (int i = 0; i < F; ++i) {
-    swa[i] = slot_swizzle(wm + 32 * i + r);
-    swb[i] = slot_swizzle(wn + 32 * i + r);
+    R.swa[i] = slot_swizzle(wm + 32 * i + r);
+    R.swb[i] = slot_swizzle(wn + 32 * i + r);
   }
-
-  f32x16_t acc[F][F];
 #pragma unroll
   for (int i = 0; i < F; ++i)
 #pragma unroll
-    for (int j = 0; j < F; ++j) acc[i][j] = f32x16_t{};
+    for (int j = 0; j < F; ++j) R.acc[i][j] = f32x16_t{};
 
+  // Prologue: stages 0 and 1 in flight, stage 0 published, its first step's fragments made.
   const int nk = g.K / BK;
   load_stage_lds<T>(g, m0, n0, 0, lds);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    // Stage kt has landed once this wave's copies are done and every wave has passed the
-    // barrier; the barrier also retires all reads of the buffer refilled below.
-    __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
-    __syncthreads();
-    if (kt + 1 < nk) load_stage_lds<T>(g, m0, n0, kt + 1, lds + ((kt + 1) % kStages) * C::kStageBytes);
-    const uint8_t* buf = lds + (kt % kStages) * C::kStageBytes;
-    const uint8_t* ca = buf + (wm + r) * kRowBytes;
-    const uint8_t* cb = buf + C::kCodeTile + (wn + r) * kRowBytes;
-    const uint8_t* sa_t = buf + 2 * C::kCodeTile + (wm + r) * kScaleRow;
-    const uint8_t* sb_t = buf + 2 * C::kCodeTile + C::kScaleTile + (wn + r) * kScaleRow;
-    // Lane half h covers blocks 2h and 2h+1 of each 64-wide chunk c: bytes 2h and 2h+1 of
-    // scale dword c.
-    uint4 sa[F], sb[F];
-    uint4 qa[F], qb[F];
+  if (nk > 1) load_stage_lds<T>(g, m0, n0, 1, lds + C::kStageBytes);
+  __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
+  __syncthreads();
+  {
+    const uint8_t* ca = lds + (wm + r) * kRowBytes;
+    const uint8_t* cb = lds + C::kCodeTile + (wn + r) * kRowBytes;
+    const uint8_t* sa_t = lds + 2 * C::kCodeTile + (wm + r) * kScaleRow;
+    const uint8_t* sb_t = lds + 2 * C::kCodeTile + C::kScaleTile + (wn + r) * kScaleRow;
 #pragma unroll
     for (int i = 0; i < F; ++i) {
-      sa[i] = *reinterpret_cast<const uint4*>(sa_t + 32 * i * kScaleRow);
-      sb[i] = *reinterpret_cast<const uint4*>(sb_t + 32 * i * kScaleRow);
-      qa[i] = *reinterpret_cast<const uint4*>(ca + 32 * i * kRowBytes + ((h ^ swa[i]) << 4));
-      qb[i] = *reinterpret_cast<const uint4*>(cb + 32 * i * kRowBytes + ((h ^ swb[i]) << 4));
+      R.sa[i] = *reinterpret_cast<const uint4*>(sa_t + 32 * i * kScaleRow);
+      R.sb[i] = *reinterpret_cast<const uint4*>(sb_t + 32 * i * kScaleRow);
+      R.qa[i] = *reinterpret_cast<const uint4*>(ca + 32 * i * kRowBytes + ((h ^ R.swa[i]) << 4));
+      R.qb[i] = *reinterpret_cast<const uint4*>(cb + 32 * i * kRowBytes + ((h ^ R.swb[i]) << 4));
     }
-    half2_t pa[F][2], pb[F][2];
 #pragma unroll
     for (int i = 0; i < F; ++i) {
-      pa[i][0] = pair_of_byte(sa[i].x, 2 * h);
-      pa[i][1] = pair_of_byte(sa[i].x, 2 * h + 1);
-      pb[i][0] = pair_of_byte(sb[i].x, 2 * h);
-      pb[i][1] = pair_of_byte(sb[i].x, 2 * h + 1);
+      R.pa[i][0] = pair_of_byte(R.sa[i].x, 2 * h);
+      R.pa[i][1] = pair_of_byte(R.sa[i].x, 2 * h + 1);
+      R.pb[i][0] = pair_of_byte(R.sb[i].x, 2 * h);
+      R.pb[i][1] = pair_of_byte(R.sb[i].x, 2 * h + 1);
     }
-    half8_t fa[F], fb[F];
-    dequant_step<F>(qa, qb, pa, pb, 0, fa, fb);
-#pragma unroll
-    for (int step = 0; step < 4 * kChunks; ++step) {
-      __builtin_amdgcn_sched_barrier(0);
-      const int c = step >> 2;
-      half8_t na[F], nb[F];
-      if ((step & 3) == 3 && c + 1 < kChunks) {
-        // scale pairs of chunk c+1 (its codes were read during the previous step)
-#pragma unroll
-        for (int i = 0; i < F; ++i) {
-          const uint32_t da = c == 0 ? sa[i].y : c == 1 ? sa[i].z : sa[i].w;
-          const uint32_t db = c == 0 ? sb[i].y : c == 1 ? sb[i].z : sb[i].w;
-          pa[i][0] = pair_of_byte(da, 2 * h);
-          pa[i][1] = pair_of_byte(da, 2 * h + 1);
-          pb[i][0] = pair_of_byte(db, 2 * h);
-          pb[i][1] = pair_of_byte(db, 2 * h + 1);
-        }
-      }
-      if (step + 1 < 4 * kChunks) dequant_step<F>(qa, qb, pa, pb, (step + 1) & 3, na, nb);
-      if ((step & 3) == 2 && c + 1 < kChunks) {
-        // chunk c's codes are dequantized to the end now: read chunk c+1's for the next step
-        const int slot = 2 * (c + 1) + h;
-#pragma unroll
-        for (int i = 0; i < F; ++i) {
-          qa[i] = *reinterpret_cast<const uint4*>(ca + 32 * i * kRowBytes + ((slot ^ swa[i]) << 4));
-          qb[i] = *reinterpret_cast<const uint4*>(cb + 32 * i * kRowBytes + ((slot ^ swb[i]) << 4));
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < F; ++i)
-#pragma unroll
-        for (int j = 0; j < F; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-      // Interleave: one MFMA, then the next step's dequantization spread between them.
-#pragma unroll
-      for (int k = 0; k < F * F; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 16 / F, 0);
-      }
-      if (step + 1 < 4 * kChunks) {
-#pragma unroll
-        for (int i = 0; i < F; ++i) {
-          fa[i] = na[i];
-          fb[i] = nb[i];
-        }
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    dequant_step<F>(R.qa, R.qb, R.pa, R.pb, 0, R.fa, R.fb);
   }
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) prefill_stage<T, true>(g, lds, m0, n0, kt, R);
+  for (; kt < nk; ++kt) prefill_stage<T, false>(g, lds, m0, n0, kt, R);
+  auto& acc = R.acc;
 
   // Epilogue: y = (acc * s_gA[m]) * s_gW[seg(n)].
   float sw[F];
