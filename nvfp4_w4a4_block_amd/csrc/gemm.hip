@@ -41,6 +41,7 @@ struct GemmArgs {
   const float* w_globals;
   void* y;
   int32_t y_bf16;
+  int32_t y_vec;      // y and its row pitch allow 16-byte stores
   int64_t ldy;
   SegmentTable seg;
 };
@@ -308,26 +309,65 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
   for (; kt < nk; ++kt) prefill_stage<T, false>(g, lds, m0, n0, kt, R);
   auto& acc = R.acc;
 
-  // Epilogue: y = (acc * s_gA[m]) * s_gW[seg(n)].
+  // Epilogue: y = (acc * s_gA[m]) * s_gW[seg(n)].  The scaled fp32 results go through LDS
+  // (free once every wave has left the K loop) in passes of 128 tile rows, so that each row
+  // of the tile leaves as whole 16-byte stores instead of one 2- or 4-byte store per lane.
+  // Row pitch T + 8 floats: the two row groups a store instruction touches (4 rows apart)
+  // fall in disjoint LDS banks.
+  constexpr int kPitch = T + 8;
+  constexpr int kPasses = T / 128;
+  constexpr int kVecPerRow = T / 8;
+  constexpr int kRowsPerIter = kPrefillThreads / kVecPerRow;
+  float* out = reinterpret_cast<float*>(lds);
   float sw[F];
-  int ncol[F];
 #pragma unroll
-  for (int j = 0; j < F; ++j) {
-    ncol[j] = n0 + wn + 32 * j + r;
-    sw[j] = g.w_globals[segment_of(min(ncol[j], g.N - 1), g.seg)];
-  }
+  for (int j = 0; j < F; ++j) sw[j] = g.w_globals[segment_of(min(n0 + wn + 32 * j + r, g.N - 1), g.seg)];
   const float sa0 = g.a_global[0];
+  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < F; ++i) {
+  for (int p = 0; p < kPasses; ++p) {
+    if (wm == 128 * p || kPasses == 1) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int m = m0 + wm + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
-      if (m >= g.M) continue;
-      const float sam = g.a_per_row ? g.a_global[m] : sa0;
+      for (int i = 0; i < F; ++i) {
 #pragma unroll
-      for (int j = 0; j < F; ++j)
-        if (ncol[j] < g.N) store_out(g, m, ncol[j], (acc[i][j][q] * sam) * sw[j]);
+        for (int q = 0; q < 16; ++q) {
+          const int lr = wm - 128 * p + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+          const float sam = g.a_per_row ? g.a_global[min(m0 + 128 * p + lr, g.M - 1)] : sa0;
+#pragma unroll
+          for (int j = 0; j < F; ++j) out[lr * kPitch + wn + 32 * j + r] = (acc[i][j][q] * sam) * sw[j];
+        }
+      }
     }
+    __syncthreads();
+#pragma unroll 4
+    for (int it = 0; it < 128 / kRowsPerIter; ++it) {
+      const int v = it * kPrefillThreads + (int)threadIdx.x;
+      const int lr = v / kVecPerRow, c8 = (v % kVecPerRow) * 8;
+      const int m = m0 + 128 * p + lr, n = n0 + c8;
+      if (m >= g.M) continue;
+      const float4 lo = *reinterpret_cast<const float4*>(out + lr * kPitch + c8);
+      const float4 hi = *reinterpret_cast<const float4*>(out + lr * kPitch + c8 + 4);
+      if (g.y_vec && n + 8 <= g.N) {
+        if (g.y_bf16) {
+          uint4 o;
+          o.x = f32_to_bf16_rne(lo.x) | ((uint32_t)f32_to_bf16_rne(lo.y) << 16);
+          o.y = f32_to_bf16_rne(lo.z) | ((uint32_t)f32_to_bf16_rne(lo.w) << 16);
+          o.z = f32_to_bf16_rne(hi.x) | ((uint32_t)f32_to_bf16_rne(hi.y) << 16);
+          o.w = f32_to_bf16_rne(hi.z) | ((uint32_t)f32_to_bf16_rne(hi.w) << 16);
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.y) + (int64_t)m * g.ldy + n) = o;
+        } else {
+          float* dst = static_cast<float*>(g.y) + (int64_t)m * g.ldy + n;
+          *reinterpret_cast<float4*>(dst) = lo;
+          *reinterpret_cast<float4*>(dst + 4) = hi;
+        }
+      } else {
+        const float e[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (n + k < g.N) store_out(g, m, n + k, e[k]);
+      }
+    }
+    if (p + 1 < kPasses) __syncthreads();
   }
 }
 
@@ -538,6 +578,7 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
   g.y = y;
   g.y_bf16 = y_dtype == NVFP4_BF16;
   g.ldy = ldy;
+  g.y_vec = reinterpret_cast<uintptr_t>(y) % 16 == 0 && (ldy * (g.y_bf16 ? 2 : 4)) % 16 == 0;
   g.seg = seg;
   if (K % 128 != 0 || (M > 16 && K % BK != 0)) {
     const int64_t total = M * N;
