@@ -81,7 +81,9 @@ template <int T> struct TileCfg {
   static constexpr int kStageBytes = 2 * kCodeTile + 2 * kScaleTile;
   static constexpr int F = T / 64;           // MFMA 32x32 tiles per wavefront per dimension
 };
-constexpr int kPrefillLds = kStages * TileCfg<256>::kStageBytes;
+// Behind the stage buffers: the tile's row and column global scales (256 floats each).
+constexpr int kScaleTableOffset = kStages * TileCfg<256>::kStageBytes;
+constexpr int kPrefillLds = kScaleTableOffset + 2 * 256 * 4;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -277,10 +279,17 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
 #pragma unroll
     for (int j = 0; j < F; ++j) R.acc[i][j] = f32x16_t{};
 
-  // Prologue: stages 0 and 1 in flight, stage 0 published, its first step's fragments made.
+  // Prologue: stages 0 and 1 in flight, the scale tables filled, stage 0 published, its
+  // first step's fragments made.
   const int nk = g.K / BK;
   load_stage_lds<T>(g, m0, n0, 0, lds);
   if (nk > 1) load_stage_lds<T>(g, m0, n0, 1, lds + C::kStageBytes);
+  {
+    float* row_scale = reinterpret_cast<float*>(lds + kScaleTableOffset);
+    for (int t = threadIdx.x; t < 2 * T; t += kPrefillThreads)
+      row_scale[t] = t < T ? g.a_global[g.a_per_row ? min(m0 + t, g.M - 1) : 0]
+                           : g.w_globals[segment_of(min(n0 + t - T, g.N - 1), g.seg)];
+  }
   __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
   __syncthreads();
   {
@@ -309,65 +318,90 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
   for (; kt < nk; ++kt) prefill_stage<T, false>(g, lds, m0, n0, kt, R);
   auto& acc = R.acc;
 
-  // Epilogue: y = (acc * s_gA[m]) * s_gW[seg(n)].  The scaled fp32 results go through LDS
-  // (free once every wave has left the K loop) in passes of 128 tile rows, so that each row
-  // of the tile leaves as whole 16-byte stores instead of one 2- or 4-byte store per lane.
-  // Row pitch T + 8 floats: the two row groups a store instruction touches (4 rows apart)
-  // fall in disjoint LDS banks.
-  constexpr int kPitch = T + 8;
-  constexpr int kPasses = T / 128;
-  constexpr int kVecPerRow = T / 8;
-  constexpr int kRowsPerIter = kPrefillThreads / kVecPerRow;
-  float* out = reinterpret_cast<float*>(lds);
+  // Epilogue: y = (acc * s_gA[m]) * s_gW[seg(n)], with the scales from the tables.
+  const float* row_scale = reinterpret_cast<const float*>(lds + kScaleTableOffset);
+  const float* col_scale = row_scale + T;
   float sw[F];
 #pragma unroll
-  for (int j = 0; j < F; ++j) sw[j] = g.w_globals[segment_of(min(n0 + wn + 32 * j + r, g.N - 1), g.seg)];
-  const float sa0 = g.a_global[0];
+  for (int j = 0; j < F; ++j) sw[j] = col_scale[wn + 32 * j + r];
+  if (!g.y_bf16) {
+    // fp32: each store instruction covers 128 contiguous bytes of two rows; store directly.
+#pragma unroll
+    for (int i = 0; i < F; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int lr = wm + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+        if (m0 + lr >= g.M) continue;
+        const float sam = row_scale[lr];
+#pragma unroll
+        for (int j = 0; j < F; ++j) {
+          const int n = n0 + wn + 32 * j + r;
+          if (n < g.N) store_out(g, m0 + lr, n, (acc[i][j][q] * sam) * sw[j]);
+        }
+      }
+    return;
+  }
+  // bf16: the rounded results go through LDS (free once every wave has left the K loop) so
+  // that rows leave as whole 16-byte segments.  A lane holds rows 2u and 2u+1 of a column in
+  // consecutive accumulator registers; they are packed into one dword of row pair u, column
+  // n.  Pitch T + 16 dwords per row pair: the two row pairs one write touches fall in
+  // disjoint LDS banks.
+  constexpr int kPitch = T + 16;
+  constexpr int kVecPerPair = T / 8;
+  constexpr int kPairsPerIter = kPrefillThreads / kVecPerPair;
+  uint32_t* out = reinterpret_cast<uint32_t*>(lds);
   __syncthreads();
 #pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    if (wm == 128 * p || kPasses == 1) {
+  for (int i = 0; i < F; ++i)
 #pragma unroll
-      for (int i = 0; i < F; ++i) {
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int lr = wm + 32 * i + 8 * g4 + 4 * h;          // rows lr .. lr+3 of this lane
+      const float4 sam = *reinterpret_cast<const float4*>(row_scale + lr);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int lr = wm - 128 * p + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
-          const float sam = g.a_per_row ? g.a_global[min(m0 + 128 * p + lr, g.M - 1)] : sa0;
-#pragma unroll
-          for (int j = 0; j < F; ++j) out[lr * kPitch + wn + 32 * j + r] = (acc[i][j][q] * sam) * sw[j];
-        }
+      for (int j = 0; j < F; ++j) {
+        const int col = wn + 32 * j + r;
+        const f32x16_t& c = acc[i][j];
+        out[(lr >> 1) * kPitch + col] =
+            bf16_pair((c[4 * g4] * sam.x) * sw[j], (c[4 * g4 + 1] * sam.y) * sw[j]);
+        out[((lr >> 1) + 1) * kPitch + col] =
+            bf16_pair((c[4 * g4 + 2] * sam.z) * sw[j], (c[4 * g4 + 3] * sam.w) * sw[j]);
       }
     }
-    __syncthreads();
+  __syncthreads();
+  const int c8 = ((int)threadIdx.x % kVecPerPair) * 8;
+  const int n = n0 + c8;
+  const bool vec = g.y_vec && n + 8 <= g.N;
+  uint16_t* y = static_cast<uint16_t*>(g.y);
 #pragma unroll 4
-    for (int it = 0; it < 128 / kRowsPerIter; ++it) {
-      const int v = it * kPrefillThreads + (int)threadIdx.x;
-      const int lr = v / kVecPerRow, c8 = (v % kVecPerRow) * 8;
-      const int m = m0 + 128 * p + lr, n = n0 + c8;
-      if (m >= g.M) continue;
-      const float4 lo = *reinterpret_cast<const float4*>(out + lr * kPitch + c8);
-      const float4 hi = *reinterpret_cast<const float4*>(out + lr * kPitch + c8 + 4);
-      if (g.y_vec && n + 8 <= g.N) {
-        if (g.y_bf16) {
-          uint4 o;
-          o.x = f32_to_bf16_rne(lo.x) | ((uint32_t)f32_to_bf16_rne(lo.y) << 16);
-          o.y = f32_to_bf16_rne(lo.z) | ((uint32_t)f32_to_bf16_rne(lo.w) << 16);
-          o.z = f32_to_bf16_rne(hi.x) | ((uint32_t)f32_to_bf16_rne(hi.y) << 16);
-          o.w = f32_to_bf16_rne(hi.z) | ((uint32_t)f32_to_bf16_rne(hi.w) << 16);
-          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.y) + (int64_t)m * g.ldy + n) = o;
-        } else {
-          float* dst = static_cast<float*>(g.y) + (int64_t)m * g.ldy + n;
-          *reinterpret_cast<float4*>(dst) = lo;
-          *reinterpret_cast<float4*>(dst + 4) = hi;
-        }
-      } else {
-        const float e[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  for (int it = 0; it < T / 2 / kPairsPerIter; ++it) {
+    const int u = it * kPairsPerIter + (int)threadIdx.x / kVecPerPair;
+    const int m = m0 + 2 * u;
+    if (m >= g.M) continue;
+    const uint4 p0 = *reinterpret_cast<const uint4*>(out + u * kPitch + c8);
+    const uint4 p1 = *reinterpret_cast<const uint4*>(out + u * kPitch + c8 + 4);
+    // low halves -> row 2u, high halves -> row 2u+1
+    uint4 r0, r1;
+    r0.x = __builtin_amdgcn_perm(p0.y, p0.x, 0x05040100u);
+    r0.y = __builtin_amdgcn_perm(p0.w, p0.z, 0x05040100u);
+    r0.z = __builtin_amdgcn_perm(p1.y, p1.x, 0x05040100u);
+    r0.w = __builtin_amdgcn_perm(p1.w, p1.z, 0x05040100u);
+    r1.x = __builtin_amdgcn_perm(p0.y, p0.x, 0x07060302u);
+    r1.y = __builtin_amdgcn_perm(p0.w, p0.z, 0x07060302u);
+    r1.z = __builtin_amdgcn_perm(p1.y, p1.x, 0x07060302u);
+    r1.w = __builtin_amdgcn_perm(p1.w, p1.z, 0x07060302u);
+    const bool second = m + 1 < g.M;
+    if (vec) {
+      *reinterpret_cast<uint4*>(y + (int64_t)m * g.ldy + n) = r0;
+      if (second) *reinterpret_cast<uint4*>(y + (int64_t)(m + 1) * g.ldy + n) = r1;
+    } else {
+      const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w}, w1[4] = {r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (n + k < g.N) store_out(g, m, n + k, e[k]);
+      for (int k = 0; k < 8; ++k) {
+        if (n + k >= g.N) break;
+        y[(int64_t)m * g.ldy + n + k] = (uint16_t)(w0[k >> 1] >> (16 * (k & 1)));
+        if (second) y[(int64_t)(m + 1) * g.ldy + n + k] = (uint16_t)(w1[k >> 1] >> (16 * (k & 1)));
       }
     }
-    if (p + 1 < kPasses) __syncthreads();
   }
 }
 
@@ -590,7 +624,7 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
     gemm_decode_kernel<<<grid, kDecodeThreads, 0, stream>>>(g, partial);
     gemm_decode_reduce<<<(unsigned)((M * N + 255) / 256), 256, 0, stream>>>(g, partial, nsplit);
   } else {
-    // The 144 KB of dynamic LDS exceed the default limit; raise it once per device.
+    // The 146 KB of dynamic LDS exceed the default limit; raise it once per device.
     static bool attr_set[64] = {};
     static int cus[64] = {};
     int dev = 0;

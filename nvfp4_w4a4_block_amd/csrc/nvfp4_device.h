@@ -128,4 +128,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two fp32 values -> packed bf16 (lo in the low half) by the hardware conversion: round to
+// nearest even, NaN kept NaN with the quiet bit set.  Gives the same bits as f32_to_bf16_rne
+// for every fp32 input.
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
 }  // namespace nvfp4
