@@ -92,6 +92,21 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // LDS bank groups whether the LDS serves 128 B or 256 B per cycle.
 __device__ __forceinline__ int slot_swizzle(int row) { return (row ^ (row >> 3)) & 7; }
 
+// Copy 16 B per lane from global memory straight into LDS: lane l's bytes land at
+// lds_base + 16 l (1 KB of consecutive LDS per wavefront).  Issued from inline assembly on
+// purpose: the compiler then does not treat the copy as an LDS store that every later LDS
+// read must wait for (it cannot tell the two stage buffers apart).  The copy writes no
+// registers; the K loop orders it explicitly: a stage's copies are waited for (vmcnt(0)) and
+// published with a barrier before any wavefront reads that stage, and they are issued only
+// after a barrier that follows every read of the buffer they overwrite.
+// lds_dst must be the same for every lane of the wavefront.  M0 cannot be named as clobbered
+// (the compiler reserves it); nothing else in this file's kernels uses M0, which a CPU test
+// checks on the generated assembly.
+__device__ __forceinline__ void copy16_to_lds(const uint8_t* src, const uint8_t* lds_dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds_dst);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(base) : "memory");
+}
+
 // Enqueue the copy of K step kt of both operands straight into LDS (no registers): each
 // wavefront-wide load writes 1 KB of consecutive LDS (8 rows of codes, or 64 rows of scales).
 template <int T>
@@ -105,30 +120,24 @@ __device__ __forceinline__ void load_stage_lds(const GemmArgs& g, int m0, int n0
     const int row = chunk * 8 + (lane >> 3);
     const int seg = (lane & 7) ^ slot_swizzle(row);  // logical 16 B segment stored in slot lane&7
     const int am = min(m0 + row, g.M - 1), wn = min(n0 + row, g.N - 1);
-    __builtin_amdgcn_global_load_lds(g.a_codes + am * kb + kt * kRowBytes + seg * 16,
-                                     (lds_void_t*)(stage + chunk * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(g.w_codes + wn * kb + kt * kRowBytes + seg * 16,
-                                     (lds_void_t*)(stage + C::kCodeTile + chunk * 1024), 16, 0, 0);
+    copy16_to_lds(g.a_codes + am * kb + kt * kRowBytes + seg * 16, stage + chunk * 1024);
+    copy16_to_lds(g.w_codes + wn * kb + kt * kRowBytes + seg * 16, stage + C::kCodeTile + chunk * 1024);
   }
 #pragma unroll
   for (int j = 0; j < T / 256; ++j) {
     const int chunk = j * 4 + wave;                  // 1 KB chunk = 64 rows x 16 B
     const int row = chunk * 64 + lane;
     const int am = min(m0 + row, g.M - 1), wn = min(n0 + row, g.N - 1);
-    __builtin_amdgcn_global_load_lds(g.a_scales + am * ks + kt * kScaleRow,
-                                     (lds_void_t*)(stage + 2 * C::kCodeTile + chunk * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(g.w_scales + wn * ks + kt * kScaleRow,
-                                     (lds_void_t*)(stage + 2 * C::kCodeTile + C::kScaleTile + chunk * 1024), 16, 0, 0);
+    copy16_to_lds(g.a_scales + am * ks + kt * kScaleRow, stage + 2 * C::kCodeTile + chunk * 1024);
+    copy16_to_lds(g.w_scales + wn * ks + kt * kScaleRow, stage + 2 * C::kCodeTile + C::kScaleTile + chunk * 1024);
   }
   if (T / 256 == 0) {   // 128-row tiles: 128 rows x 16 B = 2 KB per operand, half the waves each
     const int row = (wave & 1) * 64 + lane;
     const int am = min(m0 + row, g.M - 1), wn = min(n0 + row, g.N - 1);
     if (wave < 2)
-      __builtin_amdgcn_global_load_lds(g.a_scales + am * ks + kt * kScaleRow,
-                                       (lds_void_t*)(stage + 2 * C::kCodeTile + (wave & 1) * 1024), 16, 0, 0);
+      copy16_to_lds(g.a_scales + am * ks + kt * kScaleRow, stage + 2 * C::kCodeTile + (wave & 1) * 1024);
     else
-      __builtin_amdgcn_global_load_lds(g.w_scales + wn * ks + kt * kScaleRow,
-                                       (lds_void_t*)(stage + 2 * C::kCodeTile + C::kScaleTile + (wave & 1) * 1024), 16, 0, 0);
+      copy16_to_lds(g.w_scales + wn * ks + kt * kScaleRow, stage + 2 * C::kCodeTile + C::kScaleTile + (wave & 1) * 1024);
   }
 }
 

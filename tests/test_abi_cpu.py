@@ -126,3 +126,28 @@ def test_fastdiv_host_logic(tmp_path):
     assert r.returncode == 0, r.stderr[-2000:]
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0 and r.stdout.strip() == "0", r.stdout
+
+
+def test_m0_is_only_set_for_lds_copies(tmp_path):
+    """The GEMM's direct-to-LDS copies set M0 in inline assembly, which the compiler cannot be
+    told about.  Check on the generated gfx950 assembly that every M0 write is one of those
+    copies (immediately followed by its global_load_lds) and that nothing else reads M0."""
+    from nvfp4_w4a4_block_amd import build as b
+    flags = [f for f in b.HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
+    out = tmp_path / "gemm.s"
+    r = subprocess.run([b.hipcc(), *flags, "--cuda-device-only", "-S", "-I", os.path.join(ROOT, "include"),
+                        os.path.join(b.CSRC, "gemm.hip"), "-o", str(out)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l.strip() for l in out.read_text().splitlines()]
+    code = [l for l in lines if l and not l.startswith((";", "."))]
+    writes = 0
+    for i, l in enumerate(code):
+        if not re.search(r"\bm0\b", l):
+            continue
+        assert re.fullmatch(r"s_mov_b32 m0, s\d+", l), l
+        assert code[i + 1].startswith("global_load_lds_dwordx4"), (l, code[i + 1])
+        writes += 1
+    assert writes > 0
+    # global_load_lds reads M0 implicitly: each one must follow its own M0 write.
+    loads = [i for i, l in enumerate(code) if l.startswith("global_load_lds")]
+    assert all(code[i - 1].startswith("s_mov_b32 m0,") for i in loads)
