@@ -92,52 +92,58 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // LDS bank groups whether the LDS serves 128 B or 256 B per cycle.
 __device__ __forceinline__ int slot_swizzle(int row) { return (row ^ (row >> 3)) & 7; }
 
-// Copy 16 B per lane from global memory straight into LDS: lane l's bytes land at
-// lds_base + 16 l (1 KB of consecutive LDS per wavefront).  Issued from inline assembly on
+// Copy 16 B per lane from global memory straight into LDS: lane l reads base + off (off a
+// per-lane byte offset, base the same for the whole wavefront) and its bytes land at
+// lds_dst + 16 l (1 KB of consecutive LDS per wavefront).  Issued from inline assembly on
 // purpose: the compiler then does not treat the copy as an LDS store that every later LDS
 // read must wait for (it cannot tell the two stage buffers apart).  The copy writes no
 // registers; the K loop orders it explicitly: a stage's copies are waited for (vmcnt(0)) and
 // published with a barrier before any wavefront reads that stage, and they are issued only
-// after a barrier that follows every read of the buffer they overwrite.
-// lds_dst must be the same for every lane of the wavefront.  M0 cannot be named as clobbered
-// (the compiler reserves it); nothing else in this file's kernels uses M0, which a CPU test
-// checks on the generated assembly.
-__device__ __forceinline__ void copy16_to_lds(const uint8_t* src, const uint8_t* lds_dst) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds_dst);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(base) : "memory");
+// after a barrier that follows every read of the buffer they overwrite.  lds_dst must be the
+// same for every lane.  M0 cannot be named as clobbered (the compiler reserves it); nothing
+// else in this file's kernels uses M0, which a CPU test checks on the generated assembly.
+__device__ __forceinline__ void copy16_to_lds(const uint8_t* base, uint32_t off, const uint8_t* lds_dst) {
+  const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds_dst);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "s"(dst) : "memory");
 }
 
 // Enqueue the copy of K step kt of both operands straight into LDS (no registers): each
 // wavefront-wide load writes 1 KB of consecutive LDS (8 rows of codes, or 64 rows of scales).
+// Rows past the end of A or W are clamped to the last row.  Addresses are a per-tile base in
+// scalar registers plus a 32-bit per-lane offset, row * row pitch + segment, with row < 256 and
+// the pitch < 2^23 (K < 2^24), so 24-bit multiplies serve.
 template <int T>
 __device__ __forceinline__ void load_stage_lds(const GemmArgs& g, int m0, int n0, int kt, uint8_t* stage) {
   using C = TileCfg<T>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t kb = (int64_t)g.K / 2, ks = (int64_t)g.K / 16;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const uint32_t kb = (uint32_t)g.K / 2, ks = (uint32_t)g.K / 16;
+  const int ra = g.M - 1 - m0, rw = g.N - 1 - n0;          // last valid tile row of A, W
+  const uint8_t* ac = g.a_codes + (size_t)m0 * kb + (size_t)kt * kRowBytes;
+  const uint8_t* wc = g.w_codes + (size_t)n0 * kb + (size_t)kt * kRowBytes;
+  const uint8_t* as = g.a_scales + (size_t)m0 * ks + (size_t)kt * kScaleRow;
+  const uint8_t* ws = g.w_scales + (size_t)n0 * ks + (size_t)kt * kScaleRow;
 #pragma unroll
   for (int j = 0; j < T / 32; ++j) {
     const int chunk = j * 4 + wave;                  // 1 KB chunk = 8 rows
     const int row = chunk * 8 + (lane >> 3);
-    const int seg = (lane & 7) ^ slot_swizzle(row);  // logical 16 B segment stored in slot lane&7
-    const int am = min(m0 + row, g.M - 1), wn = min(n0 + row, g.N - 1);
-    copy16_to_lds(g.a_codes + am * kb + kt * kRowBytes + seg * 16, stage + chunk * 1024);
-    copy16_to_lds(g.w_codes + wn * kb + kt * kRowBytes + seg * 16, stage + C::kCodeTile + chunk * 1024);
+    const uint32_t seg = (uint32_t)(((lane & 7) ^ slot_swizzle(row)) * 16);  // logical 16 B segment in slot lane&7
+    copy16_to_lds(ac, __umul24(min(row, ra), kb) + seg, stage + chunk * 1024);
+    copy16_to_lds(wc, __umul24(min(row, rw), kb) + seg, stage + C::kCodeTile + chunk * 1024);
   }
 #pragma unroll
   for (int j = 0; j < T / 256; ++j) {
     const int chunk = j * 4 + wave;                  // 1 KB chunk = 64 rows x 16 B
     const int row = chunk * 64 + lane;
-    const int am = min(m0 + row, g.M - 1), wn = min(n0 + row, g.N - 1);
-    copy16_to_lds(g.a_scales + am * ks + kt * kScaleRow, stage + 2 * C::kCodeTile + chunk * 1024);
-    copy16_to_lds(g.w_scales + wn * ks + kt * kScaleRow, stage + 2 * C::kCodeTile + C::kScaleTile + chunk * 1024);
+    copy16_to_lds(as, __umul24(min(row, ra), ks), stage + 2 * C::kCodeTile + chunk * 1024);
+    copy16_to_lds(ws, __umul24(min(row, rw), ks), stage + 2 * C::kCodeTile + C::kScaleTile + chunk * 1024);
   }
   if (T / 256 == 0) {   // 128-row tiles: 128 rows x 16 B = 2 KB per operand, half the waves each
     const int row = (wave & 1) * 64 + lane;
-    const int am = min(m0 + row, g.M - 1), wn = min(n0 + row, g.N - 1);
     if (wave < 2)
-      copy16_to_lds(g.a_scales + am * ks + kt * kScaleRow, stage + 2 * C::kCodeTile + (wave & 1) * 1024);
+      copy16_to_lds(as, __umul24(min(row, ra), ks), stage + 2 * C::kCodeTile + (wave & 1) * 1024);
     else
-      copy16_to_lds(g.w_scales + wn * ks + kt * kScaleRow, stage + 2 * C::kCodeTile + C::kScaleTile + (wave & 1) * 1024);
+      copy16_to_lds(ws, __umul24(min(row, rw), ks), stage + 2 * C::kCodeTile + C::kScaleTile + (wave & 1) * 1024);
   }
 }
 
@@ -159,19 +165,30 @@ __device__ __forceinline__ void tile_coords(int i, int tiles_m, int tiles_n, int
   tn = in / gsize;
 }
 
+// The two scale bytes of a lane's 32 elements of a 64-wide chunk (bytes 2h and 2h+1 of the
+// chunk's scale dword, picked by sel) as fp16 E4M3 * 2^-8 in the low and high half of one
+// register: the same bits scale_pair_f16 gives each byte.
+__device__ __forceinline__ uint32_t scale_halves(uint32_t dw, uint32_t sel) {
+  return __builtin_amdgcn_perm(0u, dw, sel) << 7;
+}
+
+// Selector for scale_halves: bytes 2h and 2h+1 to bytes 0 and 2, zeros elsewhere.
+__device__ __forceinline__ uint32_t scale_halves_sel(int h) { return h ? 0x0c030c02u : 0x0c010c00u; }
+
 // Dequantize the fragments of one 16-deep K step (step s of a 64-wide chunk) for the F A
 // and F W row groups of this wavefront: dword s of each lane's 16 B of codes, scaled by
-// the pair for block (2h + s/2) of the chunk.
+// the scale of block (2h + s/2) of the chunk (low half of pa/pb for s < 2, else high half).
 template <int F>
-__device__ __forceinline__ void dequant_step(const uint4 (&qa)[F], const uint4 (&qb)[F], const half2_t (&pa)[F][2],
-                                             const half2_t (&pb)[F][2], int s, half8_t (&fa)[F],
+__device__ __forceinline__ void dequant_step(const uint4 (&qa)[F], const uint4 (&qb)[F], const uint32_t (&pa)[F],
+                                             const uint32_t (&pb)[F], int s, half8_t (&fa)[F],
                                              half8_t (&fb)[F]) {
 #pragma unroll
   for (int i = 0; i < F; ++i) {
     const uint32_t wa = s == 0 ? qa[i].x : s == 1 ? qa[i].y : s == 2 ? qa[i].z : qa[i].w;
     const uint32_t wb = s == 0 ? qb[i].x : s == 1 ? qb[i].y : s == 2 ? qb[i].z : qb[i].w;
-    fa[i] = dequant8_f16(wa, pa[i][s >> 1]);
-    fb[i] = dequant8_f16(wb, pb[i][s >> 1]);
+    const half2_t ha = __builtin_bit_cast(half2_t, pa[i]), hb = __builtin_bit_cast(half2_t, pb[i]);
+    fa[i] = dequant8_f16(wa, s < 2 ? half2_t{ha[0], ha[0]} : half2_t{ha[1], ha[1]});
+    fb[i] = dequant8_f16(wb, s < 2 ? half2_t{hb[0], hb[0]} : half2_t{hb[1], hb[1]});
   }
 }
 
@@ -181,7 +198,8 @@ struct PrefillRegs {
   static constexpr int F = T / 64;
   f32x16_t acc[F][F];
   uint4 sa[F], sb[F], qa[F], qb[F];   // scale bytes of the stage, codes of the current chunk
-  half2_t pa[F][2], pb[F][2];         // scale pairs of the current chunk
+  uint32_t pa[F], pb[F];              // scales of the current chunk (scale_halves)
+  uint32_t sel;                       // scale_halves selector of this lane
   half8_t fa[F], fb[F];               // fragments of the current step
   int swa[F], swb[F];                 // slot swizzles of the lane's rows
 };
@@ -227,10 +245,8 @@ __device__ __forceinline__ void prefill_stage(const GemmArgs& g, uint8_t* lds, i
       for (int i = 0; i < F; ++i) {
         const uint32_t da = c == 0 ? R.sa[i].y : c == 1 ? R.sa[i].z : c == 2 ? R.sa[i].w : R.sa[i].x;
         const uint32_t db = c == 0 ? R.sb[i].y : c == 1 ? R.sb[i].z : c == 2 ? R.sb[i].w : R.sb[i].x;
-        R.pa[i][0] = pair_of_byte(da, 2 * h);
-        R.pa[i][1] = pair_of_byte(da, 2 * h + 1);
-        R.pb[i][0] = pair_of_byte(db, 2 * h);
-        R.pb[i][1] = pair_of_byte(db, 2 * h + 1);
+        R.pa[i] = scale_halves(da, R.sel);
+        R.pb[i] = scale_halves(db, R.sel);
       }
     }
     half8_t na[F], nb[F];
@@ -278,6 +294,7 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
   const int wm = (wave >> 1) * (T / 2), wn = (wave & 1) * (T / 2);
   const int r = lane & 31, h = lane >> 5;
   PrefillRegs<T> R;
+  R.sel = scale_halves_sel(h);
 #pragma unroll
   for (int i = 0; i < F; ++i) {
     R.swa[i] = slot_swizzle(wm + 32 * i + r);
@@ -315,10 +332,8 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
     }
 #pragma unroll
     for (int i = 0; i < F; ++i) {
-      R.pa[i][0] = pair_of_byte(R.sa[i].x, 2 * h);
-      R.pa[i][1] = pair_of_byte(R.sa[i].x, 2 * h + 1);
-      R.pb[i][0] = pair_of_byte(R.sb[i].x, 2 * h);
-      R.pb[i][1] = pair_of_byte(R.sb[i].x, 2 * h + 1);
+      R.pa[i] = scale_halves(R.sa[i].x, R.sel);
+      R.pb[i] = scale_halves(R.sb[i].x, R.sel);
     }
     dequant_step<F>(R.qa, R.qb, R.pa, R.pb, 0, R.fa, R.fb);
   }
@@ -623,7 +638,7 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
   g.ldy = ldy;
   g.y_vec = reinterpret_cast<uintptr_t>(y) % 16 == 0 && (ldy * (g.y_bf16 ? 2 : 4)) % 16 == 0;
   g.seg = seg;
-  if (K % 128 != 0 || (M > 16 && K % BK != 0)) {
+  if (K % 128 != 0 || (M > 16 && (K % BK != 0 || K >= (1 << 24)))) {
     const int64_t total = M * N;
     gemm_plain_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(g);
   } else if (M <= 16) {
