@@ -33,13 +33,18 @@ import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
-GEMM_SOURCE = os.path.join(ROOT, "nvfp4_w4a4_block_amd", "csrc", "gemm.hip")
+GEMM_SOURCES = [os.path.join(ROOT, "nvfp4_w4a4_block_amd", "csrc", f)
+                for f in ("gemm.hip", "nvfp4_device.h", "nvfp4_internal.h")]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def source_digest(path: str = GEMM_SOURCE) -> str:
+def source_digest(paths=GEMM_SOURCES) -> str:
+    """Digest of the GEMM kernel's sources: stored HBM byte counts apply only to this code."""
     import hashlib
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def copy_calibration(mb: int) -> None:
@@ -119,12 +124,24 @@ def _events(n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
+def _settle(step, seconds: float) -> None:
+    """Run untimed steps for about `seconds` of wall time before the counted warmup, so that
+    the GPU's clocks have reached their steady state under this load when timing starts."""
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
+
+
 def _bytes_quantize(rows: int, cols: int, in_bytes: int = 2) -> float:
     # algorithmic bytes: X read once, codes (0.5 B/elem) and scales (1/16 B/elem) written
     return rows * cols * (in_bytes + 0.5 + 1.0 / 16)
 
 
-def bench_prefill(nv, steps: int, warmup: int, rotate: int = 4):
+def bench_prefill(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: int = 4):
     p = workloads.PREFILL
     dev = torch.device("cuda:0")
     x0 = torch.from_numpy(p.x()).to(dev).to(torch.bfloat16)
@@ -144,6 +161,7 @@ def bench_prefill(nv, steps: int, warmup: int, rotate: int = 4):
         if ev is not None:
             ev[2].record()
 
+    _settle(step, settle_s)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -193,7 +211,7 @@ def cpu_baseline_prefill(p, sample_rows: int = 4096):
                       f"all {p.N} W rows (dequantize W + BLAS matmul, {cores} threads); {dt:.1f} s"}
 
 
-def bench_decode(nv, steps: int, warmup: int, rotate: int = 8):
+def bench_decode(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: int = 8):
     d = workloads.DECODE
     dev = torch.device("cuda:0")
     w0 = torch.from_numpy(d.w()).to(dev).to(torch.bfloat16)
@@ -206,6 +224,8 @@ def bench_decode(nv, steps: int, warmup: int, rotate: int = 8):
         x = torch.from_numpy(d.x(M)).to(dev).to(torch.bfloat16)
         a = nv.quantize(x, "per_row")
         y = torch.empty((M, d.N), dtype=torch.bfloat16, device=dev)
+        _settle(lambda i: (nv.quantize(x, "per_row", out=a), nv.gemm(a, ws[i % rotate], torch.bfloat16, out=y)),
+                settle_s)
         for i in range(warmup):
             nv.quantize(x, "per_row", out=a)
             nv.gemm(a, ws[i % rotate], torch.bfloat16, out=y)
@@ -231,7 +251,7 @@ def bench_decode(nv, steps: int, warmup: int, rotate: int = 8):
     return out
 
 
-def bench_fused(nv, steps: int, warmup: int):
+def bench_fused(nv, steps: int, warmup: int, settle_s: float = 0.0):
     f = workloads.FUSED
     dev = torch.device("cuda:0")
     x = torch.from_numpy(f.x()).to(dev).to(torch.bfloat16)
@@ -241,6 +261,7 @@ def bench_fused(nv, steps: int, warmup: int):
     gl = torch.cat([q.global_scale for q in qs])
     a = nv.quantize(x)
     y = torch.empty((f.M, f.N), dtype=torch.bfloat16, device=dev)
+    _settle(lambda i: nv.gemm_fused_segments(a, codes, scales, f.widths, gl, torch.bfloat16, out=y), settle_s)
     for _ in range(warmup):
         nv.gemm_fused_segments(a, codes, scales, f.widths, gl, torch.bfloat16, out=y)
     torch.cuda.synchronize()
@@ -261,6 +282,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="seconds of untimed steps before the warmup steps, for steady clocks")
     ap.add_argument("--workload", choices=["prefill", "decode", "fused"], default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=TRAFFIC_JSON,
@@ -282,13 +305,13 @@ def main() -> int:
 
     copy_calibration(args.copy_calibration_mb)
     if args.workload == "decode":
-        print(json.dumps({"workload": "decode", "results": bench_decode(nv, args.steps, args.warmup)}))
+        print(json.dumps({"workload": "decode", "results": bench_decode(nv, args.steps, args.warmup, args.settle_s)}))
         return 0
     if args.workload == "fused":
-        print(json.dumps({"workload": "fused", "results": bench_fused(nv, args.steps, args.warmup)}))
+        print(json.dumps({"workload": "fused", "results": bench_fused(nv, args.steps, args.warmup, args.settle_s)}))
         return 0
 
-    res, (p, w) = bench_prefill(nv, args.steps, args.warmup)
+    res, (p, w) = bench_prefill(nv, args.steps, args.warmup, args.settle_s)
     print(f"[bench] prefill: step {res['ms_per_step']:.3f} ms, gemm {res['gemm_ms']:.3f} ms "
           f"({res['gemm_tflops']:.1f} TFLOP/s), quantize {res['quant_ms'] * 1e3:.1f} us "
           f"({res['quant_gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
@@ -308,6 +331,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": args.settle_s,
         "ms_per_step": round(res["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
