@@ -39,11 +39,16 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def source_digest(paths=GEMM_SOURCES) -> str:
-    """Digest of the GEMM kernel's sources: stored HBM byte counts apply only to this code."""
+    """Digest of the GEMM kernel's code (comments and whitespace dropped): stored HBM byte
+    counts apply only to this code."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for p in paths:
-        h.update(open(p, "rb").read())
+        text = open(p).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -11,18 +11,20 @@
 //    MFMA, whose products are exact in fp32.  Only the fp32 accumulation rounds.  The
 //    global scales stay out of the operands and are applied in the epilogue, per row of A
 //    and per column segment of W.
-//  * Prefill kernel: 256 x 256 output tile per 256-thread workgroup (4 wavefronts, each a
-//    128 x 128 sub-tile of 4 x 4 MFMA 32x32x16 tiles), K step 128.  Packed codes (64 B per
-//    row per step) and scale bytes are staged in LDS, double-buffered; each lane reads 16 B
-//    of codes (32 elements of one row) per 64-wide K chunk and uses one dword per MFMA.  The
-//    K order inside a chunk is permuted identically for A and W, which leaves every dot
-//    product unchanged.  Tiles are mapped to XCDs so that each XCD's L2 serves a compact
-//    block of output tiles.
-//  * Decode kernel (M <= 16): memory-bound streaming of W.  A 512-thread workgroup owns 16
-//    rows of W; its 8 wavefronts split K, accumulate 16x16 MFMA tiles and reduce them in
-//    LDS in a fixed order (deterministic).
+//  * Prefill kernel (M > 16): 256 x 256 output tile per 256-thread workgroup (4 wavefronts,
+//    each a 128 x 128 sub-tile of 4 x 4 MFMA 32x32x16 tiles), K stages of 256.  Packed codes
+//    (128 B per row per stage) and scale bytes are copied straight into LDS, double-buffered;
+//    each lane reads 16 B of codes (32 elements of one row) per 64-wide K chunk and uses one
+//    dword per MFMA.  The K order inside a chunk is permuted identically for A and W, which
+//    leaves every dot product unchanged.  Tiles are mapped to XCDs so that each XCD's L2
+//    serves a compact block of output tiles; when the last round of tiles would leave most
+//    CUs idle, whole tile columns are done as 128 x 128 tiles in the same launch.
+//  * Decode kernel (M <= 16): memory-bound streaming of W.  Workgroups own 32 rows of W and a
+//    K range (split K), accumulate 16x16 MFMA tiles, reduce their 4 wavefronts in LDS and
+//    write fp32 partials; a second kernel sums the partials in a fixed order
+//    (deterministic) and applies the scales.
 //  * A plain kernel (one thread per output, fp32 FMA) serves shapes the fast kernels do not
-//    take (K not a multiple of 128).
+//    take (K not a multiple of 128; for M > 16, K not a multiple of 256 or K >= 2^24).
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
 
