@@ -96,11 +96,12 @@ size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols, int mode);
  * y = (acc * a_global[m or 0]) * w_global[0], stored as y_dtype (bf16: round to nearest
  * even).
  *   M >= 0, N >= 0 (zero is a no-op), K > 0 and a multiple of 16.
- *   a_codes/w_codes 16-byte aligned.
+ *   a_codes, a_scales, w_codes, w_scales 16-byte aligned.
  *   a_global      device [1] (a_global_per_row == 0) or [M] (== 1).
  *   w_global      device [1].
  *   y             [M, ldy] of y_dtype, ldy >= N.
- *   workspace     nvfp4_gemm_workspace_size(M, N, K) bytes (may be NULL if 0).
+ *   workspace     nvfp4_gemm_workspace_size(M, N, K) bytes (may be NULL if 0; every
+ *                 shape needs 0 bytes at present, the argument keeps the ABI stable).
  */
 int nvfp4_gemm(int64_t M, int64_t N, int64_t K,
                const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,

@@ -20,7 +20,9 @@ int check_gemm_common(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, c
   if (ldy < N) return NVFP4_ERR_INVALID_ARG;
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!a_codes || !a_scales || !a_global || !w_codes || !w_scales || !y) return NVFP4_ERR_INVALID_ARG;
-  if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_global, 4)) return NVFP4_ERR_INVALID_ARG;
+  if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_scales, 16) || !aligned(w_scales, 16) ||
+      !aligned(a_global, 4))
+    return NVFP4_ERR_INVALID_ARG;
   if (!aligned(y, y_dtype == NVFP4_F32 ? 4 : 2)) return NVFP4_ERR_INVALID_ARG;
   return NVFP4_OK;
 }

@@ -19,10 +19,9 @@
 //    leaves every dot product unchanged.  Tiles are mapped to XCDs so that each XCD's L2
 //    serves a compact block of output tiles; when the last round of tiles would leave most
 //    CUs idle, whole tile columns are done as 128 x 128 tiles in the same launch.
-//  * Decode kernel (M <= 16): memory-bound streaming of W.  Workgroups own 32 rows of W and a
-//    K range (split K), accumulate 16x16 MFMA tiles, reduce their 4 wavefronts in LDS and
-//    write fp32 partials; a second kernel sums the partials in a fixed order
-//    (deterministic) and applies the scales.
+//  * Decode kernel (M <= 16): memory-bound streaming of W in one launch.  Workgroups own 32
+//    rows of W and all of K, their 4 wavefronts split K, accumulate 16x16 MFMA tiles and
+//    reduce them in LDS in a fixed order (deterministic) before the scales are applied.
 //  * A plain kernel (one thread per output, fp32 FMA) serves shapes the fast kernels do not
 //    take (K not a multiple of 128; for M > 16, K not a multiple of 256 or K >= 2^24).
 #include "nvfp4_device.h"
@@ -450,31 +449,75 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(GemmAr
 
 // ------------------------------------------------------------------ decode kernel
 
-// Packed operands of one 128-wide K chunk for one lane: 16 B of codes and the 2 scale bytes
-// of the lane's two 16-element blocks, for A (token row rr) and both W row groups.
+// Operands of one 256-wide K stage for one lane of lane group g = lane / 16: the 32 B of codes
+// of K elements [64g, 64g + 64) of the stage and their 4 scale bytes, for A (token row) and
+// both W row groups.  The same permutation of K (lane group g takes a contiguous quarter of
+// the stage) applies to both operands, so every dot product is unchanged.
+struct DecodeStage {
+  uint4 a0, a1, w00, w01, w10, w11;
+  uint32_t as, ws0, ws1;
+};
+
+// Unconditional loads (no branch around any of them), so that the compiler's wait counts
+// stay exact and the stages in flight are waited for one at a time.
+__device__ __forceinline__ void decode_stage_load(const uint8_t* ac, const uint8_t* asc, const uint8_t* wc0,
+                                                  const uint8_t* wsc0, const uint8_t* wc1, const uint8_t* wsc1,
+                                                  int st, DecodeStage& d) {
+  d.w00 = *reinterpret_cast<const uint4*>(wc0 + st * 128);
+  d.w01 = *reinterpret_cast<const uint4*>(wc0 + st * 128 + 16);
+  d.w10 = *reinterpret_cast<const uint4*>(wc1 + st * 128);
+  d.w11 = *reinterpret_cast<const uint4*>(wc1 + st * 128 + 16);
+  d.ws0 = *reinterpret_cast<const uint32_t*>(wsc0 + st * 16);
+  d.ws1 = *reinterpret_cast<const uint32_t*>(wsc1 + st * 16);
+  d.a0 = *reinterpret_cast<const uint4*>(ac + st * 128);
+  d.a1 = *reinterpret_cast<const uint4*>(ac + st * 128 + 16);
+  d.as = *reinterpret_cast<const uint32_t*>(asc + st * 16);
+}
+
+// 8 MFMA 16x16x32 steps per W row group; one dequantized A fragment serves both groups.
+// Dword s of the lane's 32 B of codes belongs to block s/2 of its quarter: scale byte s/2.
+__device__ __forceinline__ void decode_stage_mma(const DecodeStage& d, f32x4_t& acc0, f32x4_t& acc1) {
+  const uint32_t sel_lo = 0x0c010c00u, sel_hi = 0x0c030c02u;
+  const half2_t pa[2] = {__builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, d.as, sel_lo) << 7),
+                         __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, d.as, sel_hi) << 7)};
+  const half2_t p0[2] = {__builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, d.ws0, sel_lo) << 7),
+                         __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, d.ws0, sel_hi) << 7)};
+  const half2_t p1[2] = {__builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, d.ws1, sel_lo) << 7),
+                         __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, d.ws1, sel_hi) << 7)};
+  const uint32_t aw[8] = {d.a0.x, d.a0.y, d.a0.z, d.a0.w, d.a1.x, d.a1.y, d.a1.z, d.a1.w};
+  const uint32_t w0[8] = {d.w00.x, d.w00.y, d.w00.z, d.w00.w, d.w01.x, d.w01.y, d.w01.z, d.w01.w};
+  const uint32_t w1[8] = {d.w10.x, d.w10.y, d.w10.z, d.w10.w, d.w11.x, d.w11.y, d.w11.z, d.w11.w};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int b = s >> 1;
+    const half2_t sa = (b & 1) ? half2_t{pa[b >> 1][1], pa[b >> 1][1]} : half2_t{pa[b >> 1][0], pa[b >> 1][0]};
+    const half2_t s0 = (b & 1) ? half2_t{p0[b >> 1][1], p0[b >> 1][1]} : half2_t{p0[b >> 1][0], p0[b >> 1][0]};
+    const half2_t s1 = (b & 1) ? half2_t{p1[b >> 1][1], p1[b >> 1][1]} : half2_t{p1[b >> 1][0], p1[b >> 1][0]};
+    const half8_t fa = dequant8_f16(aw[s], sa);
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, dequant8_f16(w0[s], s0), acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, dequant8_f16(w1[s], s1), acc1, 0, 0, 0);
+  }
+}
+
+// Operands of one 128-wide K chunk (used for a last chunk when K / 128 is odd): lane group g
+// takes K elements [32g, 32g + 32) of the chunk, 16 B of codes and 2 scale bytes.
 struct DecodeChunk {
   uint4 a, w0, w1;
   uint32_t as, ws0, ws1;
 };
 
-__device__ __forceinline__ void decode_load(const uint8_t* ac, const uint8_t* asc, bool arow, const uint8_t* wc0,
-                                            const uint8_t* wsc0, const uint8_t* wc1, const uint8_t* wsc1, int c,
-                                            DecodeChunk& d) {
-  d.w0 = *reinterpret_cast<const uint4*>(wc0 + c * 64);
-  d.w1 = *reinterpret_cast<const uint4*>(wc1 + c * 64);
-  d.ws0 = *reinterpret_cast<const uint16_t*>(wsc0 + c * 8);
-  d.ws1 = *reinterpret_cast<const uint16_t*>(wsc1 + c * 8);
-  if (arow) {
-    d.a = *reinterpret_cast<const uint4*>(ac + c * 64);
-    d.as = *reinterpret_cast<const uint16_t*>(asc + c * 8);
-  } else {
-    d.a = make_uint4(0, 0, 0, 0);
-    d.as = 0;
-  }
+__device__ __forceinline__ void decode_chunk_load(const uint8_t* ac, const uint8_t* asc, const uint8_t* wc0,
+                                                  const uint8_t* wsc0, const uint8_t* wc1, const uint8_t* wsc1,
+                                                  DecodeChunk& d) {
+  d.w0 = *reinterpret_cast<const uint4*>(wc0);
+  d.w1 = *reinterpret_cast<const uint4*>(wc1);
+  d.ws0 = *reinterpret_cast<const uint16_t*>(wsc0);
+  d.ws1 = *reinterpret_cast<const uint16_t*>(wsc1);
+  d.a = *reinterpret_cast<const uint4*>(ac);
+  d.as = *reinterpret_cast<const uint16_t*>(asc);
 }
 
-// 4 MFMA 16x16x32 steps per W row group; one dequantized A fragment serves both groups.
-__device__ __forceinline__ void decode_mma(const DecodeChunk& d, f32x4_t& acc0, f32x4_t& acc1) {
+__device__ __forceinline__ void decode_chunk_mma(const DecodeChunk& d, f32x4_t& acc0, f32x4_t& acc1) {
   const half2_t pa0 = pair_of_byte(d.as, 0), pa1 = pair_of_byte(d.as, 1);
   const half2_t p00 = pair_of_byte(d.ws0, 0), p01 = pair_of_byte(d.ws0, 1);
   const half2_t p10 = pair_of_byte(d.ws1, 0), p11 = pair_of_byte(d.ws1, 1);
@@ -489,91 +532,224 @@ __device__ __forceinline__ void decode_mma(const DecodeChunk& d, f32x4_t& acc0, 
   }
 }
 
-// M <= 16 tokens: memory-bound streaming of W, split along K over the whole machine.
-// Workgroup (x, y) owns W rows [32x, 32x + 32) and K chunks [y nc / S, (y+1) nc / S); its 4
-// wavefronts split that range further, keep four chunks of loads in flight each, and reduce
-// their 16x16 tiles (token x W row) through LDS in a fixed order.  The workgroup's fp32
-// partial is written to the workspace; gemm_decode_reduce sums the S partials in order.
+// M <= 16 tokens: memory-bound streaming of W in one launch.  Workgroup x owns W rows
+// [32x, 32x + 32) (two 16-row MFMA groups) and the whole K range; wavefront w takes the
+// 256-wide K stages w, w + 4, w + 8, ... (so a workgroup's loads in flight cover contiguous
+// bytes of each row; the last wavefront also takes a final 128-wide chunk), keeps
+// kDecodeDepth stages of loads in flight per lane, and the 4 wavefronts reduce their 16x16
+// tiles (token x W row) through LDS in a fixed order before the global scales are applied
+// and Y is stored.  Token rows past M load row M - 1 (their outputs are not stored).
 constexpr int kDecodeThreads = 256;
 constexpr int kDecodeWaves = kDecodeThreads / 64;
 constexpr int kDecodeRows = 32;             // W rows per workgroup: two 16-row MFMA groups
-constexpr int kDecodeMaxSplit = 32;
+constexpr int kDecodeDepth = 4;             // 256-wide stages in flight per lane
 
-__global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(GemmArgs g, float* __restrict__ partial) {
+__global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(GemmArgs g) {
   __shared__ f32x4_t red[kDecodeWaves][2][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave is uniform: made explicit so that the stage loop's exits are scalar branches.
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int rr = lane & 15, grp = lane >> 4;
   const int n0 = blockIdx.x * kDecodeRows;
-  const int split = blockIdx.y, nsplit = gridDim.y;
   const int64_t kb = (int64_t)g.K / 2, ks = (int64_t)g.K / 16;
-  const int nchunks = g.K / 128;
-  const int s0 = split * nchunks / nsplit, s1 = (split + 1) * nchunks / nsplit;
-  const int c0 = s0 + wave * (s1 - s0) / kDecodeWaves, c1 = s0 + (wave + 1) * (s1 - s0) / kDecodeWaves;
+  const int nchunks = g.K / 128, nst = nchunks / 2;
+  const int cnt = wave < nst ? (nst - wave + kDecodeWaves - 1) / kDecodeWaves : 0;   // this wave's stages
 
   const int wr0 = min(n0 + rr, g.N - 1), wr1 = min(n0 + 16 + rr, g.N - 1);
-  const bool arow = rr < g.M;
-  const uint8_t* ac = g.a_codes + (arow ? rr : 0) * kb + grp * 16;
-  const uint8_t* asc = g.a_scales + (arow ? rr : 0) * ks + grp * 2;
-  const uint8_t* wc0 = g.w_codes + wr0 * kb + grp * 16;
-  const uint8_t* wsc0 = g.w_scales + wr0 * ks + grp * 2;
-  const uint8_t* wc1 = g.w_codes + wr1 * kb + grp * 16;
-  const uint8_t* wsc1 = g.w_scales + wr1 * ks + grp * 2;
+  const int ar = min(rr, g.M - 1);
+  const uint8_t* ac = g.a_codes + ar * kb + grp * 32;
+  const uint8_t* asc = g.a_scales + ar * ks + grp * 4;
+  const uint8_t* wc0 = g.w_codes + wr0 * kb + grp * 32;
+  const uint8_t* wsc0 = g.w_scales + wr0 * ks + grp * 4;
+  const uint8_t* wc1 = g.w_codes + wr1 * kb + grp * 32;
+  const uint8_t* wsc1 = g.w_scales + wr1 * ks + grp * 4;
 
-  // Four chunks in flight per lane: chunk c is multiplied while c+1..c+3 are loading.
+  // kDecodeDepth stages in flight per lane: the i-th stage is multiplied while i+1..i+3 are
+  // loading.  Indices past the wave's last stage reload that stage (a cache hit), unused:
+  // up to 4 such reloads per wavefront.
   f32x4_t acc0 = f32x4_t{}, acc1 = f32x4_t{};
-  DecodeChunk q0, q1, q2, q3;
-  if (c0 + 0 < c1) decode_load(ac, asc, arow, wc0, wsc0, wc1, wsc1, c0 + 0, q0);
-  if (c0 + 1 < c1) decode_load(ac, asc, arow, wc0, wsc0, wc1, wsc1, c0 + 1, q1);
-  if (c0 + 2 < c1) decode_load(ac, asc, arow, wc0, wsc0, wc1, wsc1, c0 + 2, q2);
-  if (c0 + 3 < c1) decode_load(ac, asc, arow, wc0, wsc0, wc1, wsc1, c0 + 3, q3);
-  for (int c = c0; c < c1; c += 4) {
-    decode_mma(q0, acc0, acc1);
-    if (c + 4 < c1) decode_load(ac, asc, arow, wc0, wsc0, wc1, wsc1, c + 4, q0);
-    if (c + 1 >= c1) break;
-    decode_mma(q1, acc0, acc1);
-    if (c + 5 < c1) decode_load(ac, asc, arow, wc0, wsc0, wc1, wsc1, c + 5, q1);
-    if (c + 2 >= c1) break;
-    decode_mma(q2, acc0, acc1);
-    if (c + 6 < c1) decode_load(ac, asc, arow, wc0, wsc0, wc1, wsc1, c + 6, q2);
-    if (c + 3 >= c1) break;
-    decode_mma(q3, acc0, acc1);
-    if (c + 7 < c1) decode_load(ac, asc, arow, wc0, wsc0, wc1, wsc1, c + 7, q3);
+  if (cnt > 0) {
+    const int last = wave + kDecodeWaves * (cnt - 1);
+    auto st = [&](int i) { return min(wave + kDecodeWaves * i, last); };
+    DecodeStage q0, q1, q2, q3;
+    decode_stage_load(ac, asc, wc0, wsc0, wc1, wsc1, st(0), q0);
+    decode_stage_load(ac, asc, wc0, wsc0, wc1, wsc1, st(1), q1);
+    decode_stage_load(ac, asc, wc0, wsc0, wc1, wsc1, st(2), q2);
+    decode_stage_load(ac, asc, wc0, wsc0, wc1, wsc1, st(3), q3);
+    // Whole groups of 4 stages (no exit inside, so every load is issued where it stands),
+    // then the 0..3 stages left, already loaded.
+    int i = 0;
+    // The scheduling barriers keep each stage's loads after the multiply that frees its
+    // registers and before the next one: hoisted loads would make the in-order wait for the
+    // oldest stage also wait for the newest.
+    for (; i + kDecodeDepth <= cnt; i += kDecodeDepth) {
+      decode_stage_mma(q0, acc0, acc1);
+      __builtin_amdgcn_sched_barrier(0);
+      decode_stage_load(ac, asc, wc0, wsc0, wc1, wsc1, st(i + 4), q0);
+      __builtin_amdgcn_sched_barrier(0);
+      decode_stage_mma(q1, acc0, acc1);
+      __builtin_amdgcn_sched_barrier(0);
+      decode_stage_load(ac, asc, wc0, wsc0, wc1, wsc1, st(i + 5), q1);
+      __builtin_amdgcn_sched_barrier(0);
+      decode_stage_mma(q2, acc0, acc1);
+      __builtin_amdgcn_sched_barrier(0);
+      decode_stage_load(ac, asc, wc0, wsc0, wc1, wsc1, st(i + 6), q2);
+      __builtin_amdgcn_sched_barrier(0);
+      decode_stage_mma(q3, acc0, acc1);
+      __builtin_amdgcn_sched_barrier(0);
+      decode_stage_load(ac, asc, wc0, wsc0, wc1, wsc1, st(i + 7), q3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int left = cnt - i;
+    if (left > 0) decode_stage_mma(q0, acc0, acc1);
+    if (left > 1) decode_stage_mma(q1, acc0, acc1);
+    if (left > 2) decode_stage_mma(q2, acc0, acc1);
+  }
+  if ((nchunks & 1) && wave == kDecodeWaves - 1) {
+    const int c = nchunks - 1;   // last 128-wide chunk: lane group g takes its 16 B at g * 16
+    DecodeChunk d;
+    decode_chunk_load(g.a_codes + ar * kb + c * 64 + grp * 16, g.a_scales + ar * ks + c * 8 + grp * 2,
+                      g.w_codes + wr0 * kb + c * 64 + grp * 16, g.w_scales + wr0 * ks + c * 8 + grp * 2,
+                      g.w_codes + wr1 * kb + c * 64 + grp * 16, g.w_scales + wr1 * ks + c * 8 + grp * 2, d);
+    decode_chunk_mma(d, acc0, acc1);
   }
   red[wave][0][lane] = acc0;
   red[wave][1][lane] = acc1;
   __syncthreads();
   if (wave < 2) {
+    // D[m][n] of a 16x16 tile sits in lane n + 16 (m / 4), register m % 4.
     f32x4_t sum = f32x4_t{};
     for (int w = 0; w < kDecodeWaves; ++w) sum += red[w][wave][lane];
     const int n = n0 + 16 * wave + rr;
     if (n < g.N) {
+      const float sw = g.w_globals[segment_of(n, g.seg)];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int m = 4 * grp + q;
-        if (m < g.M) partial[((int64_t)split * g.M + m) * g.N + n] = sum[q];
+        if (m < g.M) store_out(g, m, n, (sum[q] * g.a_global[g.a_per_row ? m : 0]) * sw);
       }
     }
   }
 }
 
-// Y[m, n] = ((sum over splits, in order, of the partials) * s_gA[m]) * s_gW[seg(n)].
-__global__ __launch_bounds__(256) void gemm_decode_reduce(GemmArgs g, const float* __restrict__ partial, int nsplit) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)g.M * g.N) return;
-  const int m = (int)(idx / g.N), n = (int)(idx - (int64_t)m * g.N);
-  float acc = 0.0f;
-  for (int s = 0; s < nsplit; ++s) acc += partial[(int64_t)s * g.M * g.N + idx];
-  store_out(g, m, n, (acc * g.a_global[g.a_per_row ? m : 0]) * g.w_globals[segment_of(n, g.seg)]);
+// M <= 16 tokens, K a multiple of 256: the same work as gemm_decode_kernel, but every load
+// is a whole 128-byte line copied straight into LDS (8 rows x 128 B per wavefront
+// instruction), which moves the same bytes with a third of the memory requests of the
+// register loads (16 rows x 64 B, and 16-byte scale pieces).  Each wavefront owns a private
+// LDS region: a ring of kDlDepth stages (codes of the 32 W rows and 16 token rows of one
+// 256-wide K stage) and two blocks of scale bytes (8 stages each); it waits for its own
+// copies with explicit counts, so no barrier is needed until the final reduction.  Inside a
+// 1 KB chunk of 8 rows, 16-byte piece p of row i sits in slot p ^ i.
+constexpr int kDlDepth = 4;                         // 256-wide stages in flight per wavefront
+constexpr int kDlChunks = 6;                        // 1 KB chunks: W rows 0-31, then token rows 0-15
+constexpr int kDlStageBytes = kDlChunks * 1024;     // codes of one stage
+constexpr int kDlScaleBytes = kDlChunks * 1024;     // scale bytes of 8 stages
+constexpr int kDlWaveBytes = kDlDepth * kDlStageBytes + 2 * kDlScaleBytes;
+constexpr int kDlRedOffset = kDecodeWaves * kDlWaveBytes;
+constexpr int kDlLds = kDlRedOffset + kDecodeWaves * 2 * 64 * 16;
+
+// s_waitcnt immediate that waits for at most n outstanding vector memory operations.
+constexpr int vmcnt_imm(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
+
+__device__ __forceinline__ int dl_slot(int i, int p) { return i * 128 + ((p ^ i) << 4); }
+
+// Copies for one chunk: 8 rows (row_of(i) -> byte offset of that row from base) x 128 B at col.
+__device__ __forceinline__ void dl_copy_chunk(const uint8_t* base, uint32_t row_off, uint32_t col, int lane,
+                                              const uint8_t* dst) {
+  const int i = lane >> 3, p = (lane & 7) ^ i;
+  copy16_to_lds(base, row_off + col + p * 16, dst);
 }
 
-// Number of K splits for the decode path: about 8 workgroups per CU, at most one split per
-// 128-wide K chunk.
-int decode_splits(int64_t N, int64_t K, int cus) {
-  const int64_t groups = (N + kDecodeRows - 1) / kDecodeRows;
-  int64_t s = (8 * (int64_t)cus + groups - 1) / groups;
-  if (s > K / 128) s = K / 128;
-  if (s > kDecodeMaxSplit) s = kDecodeMaxSplit;
-  return (int)(s < 1 ? 1 : s);
+__global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(GemmArgs g) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int rr = lane & 15, grp = lane >> 4, i8 = lane >> 3;
+  const int n0 = blockIdx.x * kDecodeRows;
+  const uint32_t kb = (uint32_t)g.K / 2, ks = (uint32_t)g.K / 16;
+  const int nst = g.K / 256;
+  const int s0 = wave * nst / kDecodeWaves, cnt = (wave + 1) * nst / kDecodeWaves - s0;
+  uint8_t* region = lds + wave * kDlWaveBytes;
+
+  // Per-lane row offsets of the rows this lane copies (row i8 of each chunk), clamped.
+  uint32_t row_codes[kDlChunks], row_scales[kDlChunks];
+#pragma unroll
+  for (int c = 0; c < kDlChunks; ++c) {
+    const int r = c < 4 ? min(8 * c + i8, g.N - 1 - n0) : min(8 * (c - 4) + i8, g.M - 1);
+    row_codes[c] = (uint32_t)r * kb;
+    row_scales[c] = (uint32_t)r * ks;
+  }
+  const uint8_t* wcb = g.w_codes + (size_t)n0 * kb;
+  const uint8_t* wsb = g.w_scales + (size_t)n0 * ks;
+  const uint32_t last_piece = ks - 16;
+  auto copy_codes = [&](int t) {      // stage t of this wavefront (clamped to its last)
+    const uint32_t col = (uint32_t)(s0 + min(t, cnt - 1)) * 128;
+    uint8_t* dst = region + (t % kDlDepth) * kDlStageBytes;
+#pragma unroll
+    for (int c = 0; c < kDlChunks; ++c)
+      dl_copy_chunk(c < 4 ? wcb : g.a_codes, row_codes[c], col, lane, dst + c * 1024);
+  };
+  auto copy_scales = [&](int b) {     // scale bytes of stages 8b .. 8b + 7 of this wavefront
+    const uint32_t col = (uint32_t)(s0 + 8 * b) * 16;
+    uint8_t* dst = region + kDlDepth * kDlStageBytes + (b & 1) * kDlScaleBytes;
+    const uint32_t p16 = (uint32_t)(((lane & 7) ^ i8) * 16);
+#pragma unroll
+    for (int c = 0; c < kDlChunks; ++c)   // pieces past the row's end (never read) clamped in bounds
+      copy16_to_lds(c < 4 ? wsb : g.a_scales, row_scales[c] + min(col + p16, last_piece), dst + c * 1024);
+  };
+
+  f32x4_t acc0 = f32x4_t{}, acc1 = f32x4_t{};
+  if (cnt > 0) {
+    copy_scales(0);
+#pragma unroll
+    for (int t = 0; t < kDlDepth; ++t) copy_codes(t);
+    const int iw = rr & 7;
+    for (int t = 0; t < cnt; ++t) {
+      // Stage t's copies (and its scale block) are older than the 6 (kDlDepth - 1) copies of
+      // the next stages: at most that many may still be in flight.
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDlChunks * (kDlDepth - 1)));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      const uint8_t* cs = region + (t % kDlDepth) * kDlStageBytes;
+      const uint8_t* ss = region + kDlDepth * kDlStageBytes + ((t >> 3) & 1) * kDlScaleBytes;
+      const int q = t & 7;
+      const int c0 = rr >> 3;               // chunk of W row rr (group 0); +2 for group 1; +4 tokens
+      DecodeStage d;
+      d.w00 = *reinterpret_cast<const uint4*>(cs + c0 * 1024 + dl_slot(iw, 2 * grp));
+      d.w01 = *reinterpret_cast<const uint4*>(cs + c0 * 1024 + dl_slot(iw, 2 * grp + 1));
+      d.w10 = *reinterpret_cast<const uint4*>(cs + (c0 + 2) * 1024 + dl_slot(iw, 2 * grp));
+      d.w11 = *reinterpret_cast<const uint4*>(cs + (c0 + 2) * 1024 + dl_slot(iw, 2 * grp + 1));
+      d.a0 = *reinterpret_cast<const uint4*>(cs + (c0 + 4) * 1024 + dl_slot(iw, 2 * grp));
+      d.a1 = *reinterpret_cast<const uint4*>(cs + (c0 + 4) * 1024 + dl_slot(iw, 2 * grp + 1));
+      d.ws0 = *reinterpret_cast<const uint32_t*>(ss + c0 * 1024 + dl_slot(iw, q) + 4 * grp);
+      d.ws1 = *reinterpret_cast<const uint32_t*>(ss + (c0 + 2) * 1024 + dl_slot(iw, q) + 4 * grp);
+      d.as = *reinterpret_cast<const uint32_t*>(ss + (c0 + 4) * 1024 + dl_slot(iw, q) + 4 * grp);
+      decode_stage_mma(d, acc0, acc1);
+      __builtin_amdgcn_sched_barrier(0);
+      // The slot just read is refilled with stage t + kDlDepth (its reads are complete: the
+      // MFMAs above consumed them); a scale block is refilled once its 8 stages are done.
+      copy_codes(t + kDlDepth);
+      if (((t + kDlDepth) & 7) == 0) copy_scales((t + kDlDepth) >> 3);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  asm volatile("" ::: "memory");
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(lds + kDlRedOffset);
+  red[(wave * 2 + 0) * 64 + lane] = acc0;
+  red[(wave * 2 + 1) * 64 + lane] = acc1;
+  __syncthreads();
+  if (wave < 2) {
+    // D[m][n] of a 16x16 tile sits in lane n + 16 (m / 4), register m % 4.
+    f32x4_t sum = f32x4_t{};
+    for (int w = 0; w < kDecodeWaves; ++w) sum += red[(w * 2 + wave) * 64 + lane];
+    const int n = n0 + 16 * wave + rr;
+    if (n < g.N) {
+      const float sw = g.w_globals[segment_of(n, g.seg)];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = 4 * grp + q;
+        if (m < g.M) store_out(g, m, n, (sum[q] * g.a_global[g.a_per_row ? m : 0]) * sw);
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------------ plain kernel
@@ -605,24 +781,17 @@ __global__ __launch_bounds__(256) void gemm_plain_kernel(GemmArgs g) {
 }  // namespace
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  // the decode path keeps one fp32 partial of Y per K split
-  if (M < 1 || M > 16 || K % 128 != 0) return 0;
-  return (size_t)kDecodeMaxSplit * M * N * sizeof(float);
-}
-
-int device_cus() {
-  static int cus[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cus[dev] && hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 256;
-  return cus[dev];
+  (void)M;
+  (void)N;
+  (void)K;
+  return 0;   // no path needs device scratch
 }
 
 int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
                 const float* a_global, int a_global_per_row, const uint8_t* w_codes, const uint8_t* w_scales,
                 const float* w_globals, const SegmentTable& seg, void* y, int y_dtype, int64_t ldy, void* workspace,
                 hipStream_t stream) {
+  (void)workspace;
   if (M == 0 || N == 0) return NVFP4_OK;
   GemmArgs g;
   g.M = (int32_t)M;
@@ -643,12 +812,19 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
   if (K % 128 != 0 || (M > 16 && (K % BK != 0 || K >= (1 << 24)))) {
     const int64_t total = M * N;
     gemm_plain_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(g);
+  } else if (M <= 16 && K % 256 == 0) {
+    static bool dl_attr[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return NVFP4_ERR_HIP;
+    if (!dl_attr[dev]) {
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_decode_lds_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kDlLds) != hipSuccess)
+        return NVFP4_ERR_HIP;
+      dl_attr[dev] = true;
+    }
+    gemm_decode_lds_kernel<<<(unsigned)((N + kDecodeRows - 1) / kDecodeRows), kDecodeThreads, kDlLds, stream>>>(g);
   } else if (M <= 16) {
-    const int nsplit = decode_splits(N, K, device_cus());
-    float* partial = static_cast<float*>(workspace);
-    const dim3 grid((unsigned)((N + kDecodeRows - 1) / kDecodeRows), (unsigned)nsplit);
-    gemm_decode_kernel<<<grid, kDecodeThreads, 0, stream>>>(g, partial);
-    gemm_decode_reduce<<<(unsigned)((M * N + 255) / 256), 256, 0, stream>>>(g, partial, nsplit);
+    gemm_decode_kernel<<<(unsigned)((N + kDecodeRows - 1) / kDecodeRows), kDecodeThreads, 0, stream>>>(g);
   } else {
     // The 146 KB of dynamic LDS exceed the default limit; raise it once per device.
     static bool attr_set[64] = {};

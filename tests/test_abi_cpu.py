@@ -88,6 +88,7 @@ def test_gemm_argument_errors(nv):
     assert g(nv, ldy=16) == 1
     assert g(nv, a=None) == 1
     assert g(nv, w=MIS) == 1
+    assert g(nv, sa=MIS) == 1 and g(nv, sw=A16 + 4) == 1    # scales must be 16-byte aligned
     assert g(nv, gw=None) == 1
     assert g(nv, dt=3) == 1
     assert g(nv, pr=2) == 1

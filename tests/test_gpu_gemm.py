@@ -146,6 +146,44 @@ def test_ragged_shapes(M, N, K, a_mode):
         assert_gemm_close(y, Y, T, f"{M}x{N}x{K} {a_mode} {dt}")
 
 
+# Decode path (M <= 16, K a multiple of 128): odd chunk counts (a last 128-wide chunk after
+# the 256-wide stages; K = 128 has no stage at all), per-wave stage splits of unequal length,
+# N not a multiple of the 32-row workgroup, N = 1.
+@pytest.mark.parametrize("M,N,K", [(3, 100, 384), (16, 33, 128), (7, 1, 640), (1, 4097, 1152),
+                                   (16, 64, 2048), (2, 96, 2304), (16, 200, 4224)])
+@pytest.mark.parametrize("a_mode", ["per_tensor", "per_row"])
+def test_decode_ragged(M, N, K, a_mode):
+    x = workloads.activation(33, M, M, K, outlier_frac=0.02)
+    w = workloads.weight(33, 2000 + N, N, K)
+    a, q, oa, ow = _quant_pair(x, w, a_mode)
+    Y, T = ref.gemm(oa, ow)
+    for dt in (torch.float32, torch.bfloat16):
+        y = nv().gemm(a, q, dt)
+        assert_gemm_close(y, Y, T, f"decode {M}x{N}x{K} {a_mode} {dt}")
+
+
+def test_decode_fused_segments():
+    M, K, widths = 4, 640, (40, 8, 100)
+    xg = to_gpu(workloads.activation(34, 0, M, K))
+    a = nv().quantize(xg, "per_row")
+    oa = ref.quantize(xg.float().cpu().numpy(), ref.PER_ROW)
+    gq, oq = [], []
+    for i, n in enumerate(widths):
+        wg = to_gpu(workloads.weight(34, 10 + i, n, K, sigma=0.02 * (i + 1)))
+        gq.append(nv().quantize(wg))
+        oq.append(ref.quantize(wg.float().cpu().numpy()))
+    y = nv().gemm_fused_segments(a, torch.cat([q.codes for q in gq]), torch.cat([q.scales for q in gq]), widths,
+                                 torch.cat([q.global_scale for q in gq]), torch.float32)
+    Y, T = ref.fused_segments(oa, oq)
+    assert_gemm_close(y, Y, T, "decode fused")
+
+
+def test_decode_deterministic():
+    d = workloads.DECODE
+    a, w, _, _ = _quant_pair(d.x(16), d.w()[:512])
+    assert torch.equal(nv().gemm(a, w), nv().gemm(a, w))
+
+
 def test_output_row_pitch():
     x = workloads.activation(32, 0, 40, 256)
     w = workloads.weight(32, 1, 96, 256)
