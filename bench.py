@@ -146,7 +146,7 @@ def _bytes_quantize(rows: int, cols: int, in_bytes: int = 2) -> float:
     return rows * cols * (in_bytes + 0.5 + 1.0 / 16)
 
 
-def bench_prefill(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: int = 4):
+def bench_prefill(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: int = 8):
     p = workloads.PREFILL
     dev = torch.device("cuda:0")
     x0 = torch.from_numpy(p.x()).to(dev).to(torch.bfloat16)

@@ -89,15 +89,26 @@ __global__ __launch_bounds__(kThreads) void amax_partial_kernel(const T* __restr
   const int64_t chunks = cols / kElemsPer16B<T>;
   uint32_t m = 0;
   if (ldx == cols) {
+    // With a grid that is a multiple of 8, the workgroups of XCD x (blockIdx % 8, dispatch is
+    // round-robin over the 8 XCDs) read the x-th eighth of the tensor, in increasing address
+    // order; the encoder reads the same eighth on the same XCD in decreasing order, so its
+    // first reads hit what this pass left in that XCD's L2.
     const uint4* p = reinterpret_cast<const uint4*>(x);
     const int64_t total = rows * chunks;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t lo = 0, hi = total, stride = (int64_t)gridDim.x * kThreads;
     int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    for (; i + 3 * stride < total; i += 4 * stride) {
+    if ((gridDim.x & 7) == 0) {
+      const int xcd = blockIdx.x & 7;
+      lo = total * xcd / 8;
+      hi = total * (xcd + 1) / 8;
+      stride = (int64_t)(gridDim.x >> 3) * kThreads;
+      i = lo + (int64_t)(blockIdx.x >> 3) * kThreads + threadIdx.x;
+    }
+    for (; i + 3 * stride < hi; i += 4 * stride) {
       const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
       m = max(m, max(max(max_abs_bits(a, x), max_abs_bits(b, x)), max(max_abs_bits(c, x), max_abs_bits(d, x))));
     }
-    for (; i < total; i += stride) m = max(m, max_abs_bits(p[i], x));
+    for (; i < hi; i += stride) m = max(m, max_abs_bits(p[i], x));
   } else {
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
       const uint4* row = reinterpret_cast<const uint4*>(x + r * ldx);
@@ -218,6 +229,35 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const T* __restrict__ 
   }
   const uint32_t total = rows * bpr;
   const bool dense = ldx == (int64_t)bpr * 16;
+  if (MODE == kPerTensor && dense && (gridDim.x & 7) == 0) {
+    // The x-th eighth of the tensor on XCD x, in decreasing order (see amax_partial_kernel).
+    const uint32_t xcd = blockIdx.x & 7;
+    const uint32_t lo = (uint32_t)((uint64_t)total * xcd / 8), hi = (uint32_t)((uint64_t)total * (xcd + 1) / 8);
+    const uint32_t stride = (gridDim.x >> 3) * kThreads;
+    uint32_t k = (blockIdx.x >> 3) * kThreads + threadIdx.x;    // distance from the top of the eighth
+    for (; k + stride < hi - lo; k += 2 * stride) {
+      const uint32_t i0 = hi - 1 - k, i1 = i0 - stride;
+      const uint4* p0 = block_src<T, MODE>(x, i0, bpr, ldx, true, div_bpr);
+      const uint4* p1 = block_src<T, MODE>(x, i1, bpr, ldx, true, div_bpr);
+      uint4 w0[NC], w1[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        w0[c] = p0[c];
+        w1[c] = p1[c];
+      }
+      encode_one<T, MODE>(x, i0, bpr, ldx, true, div_bpr, codes, scales, global_scale, sg, w0);
+      encode_one<T, MODE>(x, i1, bpr, ldx, true, div_bpr, codes, scales, global_scale, sg, w1);
+    }
+    if (k < hi - lo) {
+      const uint32_t i0 = hi - 1 - k;
+      const uint4* p0 = block_src<T, MODE>(x, i0, bpr, ldx, true, div_bpr);
+      uint4 w0[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) w0[c] = p0[c];
+      encode_one<T, MODE>(x, i0, bpr, ldx, true, div_bpr, codes, scales, global_scale, sg, w0);
+    }
+    return;
+  }
   const uint32_t stride = gridDim.x * kThreads;
   uint32_t i = blockIdx.x * kThreads + threadIdx.x;
   for (; i + stride < total; i += 2 * stride) {
