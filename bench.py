@@ -282,6 +282,38 @@ def bench_fused(nv, steps: int, warmup: int, settle_s: float = 0.0):
             "frac_mfma_f16": flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS}
 
 
+def bench_nvfp4_out(nv, steps: int, warmup: int, settle_s: float = 0.0):
+    """The prefill GEMM with its output quantized to NVFP4 in the same launch (for the next
+    linear layer), under a calibrated output global scale, beside the same GEMM with bf16
+    output."""
+    p = workloads.PREFILL
+    dev = torch.device("cuda:0")
+    a = nv.quantize(torch.from_numpy(p.x()).to(dev).to(torch.bfloat16))
+    w = nv.quantize(torch.from_numpy(p.w()).to(dev).to(torch.bfloat16))
+    y = nv.gemm(a, w, torch.bfloat16)
+    y_global = (y.float().abs().max() / 2688.0).reshape(1)   # calibration (offline)
+    q = nv.gemm_nvfp4_out(a, w.codes, w.scales, (p.N,), w.global_scale, y_global)
+    out = {}
+    for name, fn in (("bf16_out", lambda i: nv.gemm(a, w, torch.bfloat16, out=y)),
+                     ("nvfp4_out", lambda i: nv.gemm_nvfp4_out(a, w.codes, w.scales, (p.N,), w.global_scale,
+                                                               y_global, out=q))):
+        _settle(fn, settle_s)
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        evs = [_events(2) for _ in range(steps)]
+        for i in range(steps):
+            evs[i][0].record()
+            fn(i)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        out[name] = {"gemm_ms": ms, "gemm_tflops": p.flops / (ms * 1e-3) / 1e12,
+                     "frac_mfma_f16": p.flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                     "output_bytes": p.M * p.N * 2 if name == "bf16_out" else p.M * p.N * (0.5 + 1 / 16)}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -289,7 +321,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--settle-s", type=float, default=1.0,
                     help="seconds of untimed steps before the warmup steps, for steady clocks")
-    ap.add_argument("--workload", choices=["prefill", "decode", "fused"], default="prefill")
+    ap.add_argument("--workload", choices=["prefill", "decode", "fused", "nvfp4_out"], default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=TRAFFIC_JSON,
                     help="HBM bytes per GEMM launch measured with rocprofv3 counters")
@@ -311,6 +343,10 @@ def main() -> int:
     copy_calibration(args.copy_calibration_mb)
     if args.workload == "decode":
         print(json.dumps({"workload": "decode", "results": bench_decode(nv, args.steps, args.warmup, args.settle_s)}))
+        return 0
+    if args.workload == "nvfp4_out":
+        print(json.dumps({"workload": "nvfp4_out", "results": bench_nvfp4_out(nv, args.steps, args.warmup,
+                                                                              args.settle_s)}))
         return 0
     if args.workload == "fused":
         print(json.dumps({"workload": "fused", "results": bench_fused(nv, args.steps, args.warmup, args.settle_s)}))

@@ -8,7 +8,8 @@
  *   2. the block-scaled 4-bit x 4-bit GEMM Y = A . W^T with FP32 accumulation;
  *   3. the fused-module GEMM in which several separately calibrated modules share one
  *      launch and each column segment keeps its own weight global scale (the repair of the
- *      global-scale mismatch).
+ *      global-scale mismatch);
+ *   4. the GEMM whose output leaves already quantized to NVFP4 for the next linear layer.
  *
  * Sources: the element format (E2M1 values, one E4M3 scale per 16-element block) is from
  * "NVFP4 W4A4 Quantization Compresses 27B Hybrid Models" (thevalue.engineering), section
@@ -130,6 +131,31 @@ int nvfp4_gemm_fused_segments(int64_t M, int64_t K,
                               const float* w_globals,
                               void* y, int y_dtype, int64_t ldy,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The (fused-module) GEMM with its output quantized to NVFP4 for the next linear layer, in
+ * the same launch: Y is never written in bf16 or fp32.  For every output element the fp32
+ * value y = (acc * a_global[m or 0]) * w_globals[seg(n)] is the one nvfp4_gemm_fused_segments
+ * would store as fp32 for the same shape; each 16-column block of an output row is then
+ * encoded exactly as nvfp4_quantize in NVFP4_SCALE_GIVEN mode encodes it under
+ * y_global[0] (block max -> E4M3 scale -> E2M1 round-to-nearest-even).  The output global
+ * scale is given (a calibrated, static scale): a dynamic per-tensor scale would need the
+ * whole output before the first block could be encoded.  Format and encoding as for
+ * nvfp4_quantize (sources in the file header).
+ *   N = sum of seg_n, a multiple of 16; K a multiple of 128, and for M > 16 a multiple of
+ *   256 below 2^24 (other shapes: NVFP4_ERR_UNSUPPORTED).
+ *   y_global      device [1], in: finite and > 0.
+ *   y_codes       out [M, N/2], 16-byte aligned; y_scales out [M, N/16], 16-byte aligned.
+ *   Other arguments as in nvfp4_gemm_fused_segments (one segment: a plain GEMM).
+ */
+int nvfp4_gemm_nvfp4_out(int64_t M, int64_t K,
+                         const uint8_t* a_codes, const uint8_t* a_scales,
+                         const float* a_global, int a_global_per_row,
+                         int num_segments, const int64_t* seg_n,
+                         const uint8_t* w_codes, const uint8_t* w_scales,
+                         const float* w_globals,
+                         const float* y_global, uint8_t* y_codes, uint8_t* y_scales,
+                         void* stream);
 
 size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 

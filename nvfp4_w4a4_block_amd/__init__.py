@@ -10,6 +10,8 @@ Entry points (same names as the C ABI):
   gemm(a, w, out_dtype)                  -> Y = A . W^T
   gemm_fused_segments(a, w, widths, w_globals, out_dtype)
                                          -> Y with one weight global scale per segment
+  gemm_nvfp4_out(a, w_codes, w_scales, widths, w_globals, y_global)
+                                         -> Y quantized to NVFP4 under a given global scale
 """
 from __future__ import annotations
 
@@ -21,7 +23,7 @@ from typing import Sequence
 import torch
 
 __all__ = [
-    "NVFP4Tensor", "NVFP4Error", "quantize", "gemm", "gemm_fused_segments", "library_path", "lib",
+    "NVFP4Tensor", "NVFP4Error", "quantize", "gemm", "gemm_fused_segments", "gemm_nvfp4_out", "library_path", "lib",
     "PER_TENSOR", "PER_ROW", "GIVEN", "MAX_SEGMENTS", "EXPORTED_SYMBOLS",
 ]
 
@@ -34,7 +36,7 @@ _F32, _BF16 = 0, 1
 MAX_SEGMENTS = 64
 EXPORTED_SYMBOLS = (
     "nvfp4_quantize", "nvfp4_quantize_workspace_size", "nvfp4_gemm", "nvfp4_gemm_fused_segments",
-    "nvfp4_gemm_workspace_size", "nvfp4_status_string", "nvfp4_version",
+    "nvfp4_gemm_nvfp4_out", "nvfp4_gemm_workspace_size", "nvfp4_status_string", "nvfp4_version",
 )
 
 
@@ -55,6 +57,8 @@ def _load() -> ctypes.CDLL:
     L.nvfp4_gemm.restype = i32
     L.nvfp4_gemm_fused_segments.argtypes = [i64, i64, p, p, p, i32, i32, p, p, p, p, p, i32, i64, p, sz, p]
     L.nvfp4_gemm_fused_segments.restype = i32
+    L.nvfp4_gemm_nvfp4_out.argtypes = [i64, i64, p, p, p, i32, i32, p, p, p, p, p, p, p, p]
+    L.nvfp4_gemm_nvfp4_out.restype = i32
     L.nvfp4_gemm_workspace_size.argtypes = [i64, i64, i64]
     L.nvfp4_gemm_workspace_size.restype = sz
     L.nvfp4_status_string.argtypes = [i32]
@@ -196,3 +200,27 @@ def gemm_fused_segments(a: NVFP4Tensor, w_codes: torch.Tensor, w_scales: torch.T
                                        _stream(dev))
     _check(st, "nvfp4_gemm_fused_segments")
     return y
+
+
+def gemm_nvfp4_out(a: NVFP4Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, seg_widths: Sequence[int],
+                   w_globals: torch.Tensor, y_global: torch.Tensor,
+                   out: NVFP4Tensor | None = None) -> NVFP4Tensor:
+    """(Fused-module) GEMM whose output is quantized to NVFP4 in the same launch, under the
+    given output global scale y_global (fp32 GPU tensor of one element).  With one segment
+    it is a plain GEMM.  Returns NVFP4Tensor(codes [M, N/2], scales [M, N/16], y_global)."""
+    M, K = a.rows, a.cols
+    N = int(sum(seg_widths))
+    _require(w_codes.shape == (N, K // 2) and w_scales.shape == (N, K // 16), "bad weight shapes")
+    _require(y_global.dtype == torch.float32 and y_global.is_cuda and y_global.numel() == 1, "y_global: fp32 [1]")
+    dev = a.codes.device
+    if out is None:
+        out = NVFP4Tensor(torch.empty((M, N // 2), dtype=torch.uint8, device=dev),
+                          torch.empty((M, N // 16), dtype=torch.uint8, device=dev), y_global)
+    per_row = int(a.global_scale.numel() == M and M != 1)
+    widths = (ctypes.c_int64 * len(seg_widths))(*[int(v) for v in seg_widths])
+    st = lib.nvfp4_gemm_nvfp4_out(M, K, _ptr(a.codes), _ptr(a.scales), _ptr(a.global_scale), per_row,
+                                  len(seg_widths), ctypes.cast(widths, ctypes.c_void_p), _ptr(w_codes),
+                                  _ptr(w_scales), _ptr(w_globals), _ptr(y_global), _ptr(out.codes),
+                                  _ptr(out.scales), _stream(dev))
+    _check(st, "nvfp4_gemm_nvfp4_out")
+    return out

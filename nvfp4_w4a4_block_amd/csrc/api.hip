@@ -120,4 +120,33 @@ int nvfp4_gemm_fused_segments(int64_t M, int64_t K, const uint8_t* a_codes, cons
                      y, y_dtype, ldy, workspace, static_cast<hipStream_t>(stream));
 }
 
+int nvfp4_gemm_nvfp4_out(int64_t M, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+                         const float* a_global, int a_global_per_row, int num_segments, const int64_t* seg_n,
+                         const uint8_t* w_codes, const uint8_t* w_scales, const float* w_globals,
+                         const float* y_global, uint8_t* y_codes, uint8_t* y_scales, void* stream) {
+  if (num_segments < 1 || !seg_n) return NVFP4_ERR_INVALID_ARG;
+  if (num_segments > NVFP4_MAX_SEGMENTS) return NVFP4_ERR_UNSUPPORTED;
+  SegmentTable seg{};
+  seg.count = num_segments;
+  int64_t N = 0;
+  for (int i = 0; i < num_segments; ++i) {
+    if (seg_n[i] <= 0) return NVFP4_ERR_INVALID_ARG;
+    seg.bound[i] = (int32_t)N;
+    N += seg_n[i];
+    if (N > INT32_MAX) return NVFP4_ERR_UNSUPPORTED;
+  }
+  seg.bound[num_segments] = (int32_t)N;
+  if (N % 16 != 0) return NVFP4_ERR_INVALID_ARG;
+  // y is not written on this path; check_gemm_common's output checks get a stand-in.
+  int st = check_gemm_common(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales,
+                             y_codes, NVFP4_BF16, N);
+  if (st != NVFP4_OK || M == 0) return st;
+  if (!w_globals || !aligned(w_globals, 4) || !y_global || !aligned(y_global, 4)) return NVFP4_ERR_INVALID_ARG;
+  if (!y_codes || !y_scales || !aligned(y_codes, 16) || !aligned(y_scales, 16)) return NVFP4_ERR_INVALID_ARG;
+  if ((uint64_t)M * (uint64_t)(N / 2) >= (1ull << 31)) return NVFP4_ERR_UNSUPPORTED;
+  QuantOut q{y_global, y_codes, y_scales};
+  return launch_gemm(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales, w_globals, seg,
+                     nullptr, NVFP4_BF16, N, nullptr, static_cast<hipStream_t>(stream), &q);
+}
+
 }  // extern "C"

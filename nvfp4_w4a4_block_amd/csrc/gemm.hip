@@ -45,7 +45,20 @@ struct GemmArgs {
   int32_t y_vec;      // y and its row pitch allow 16-byte stores
   int64_t ldy;
   SegmentTable seg;
+  int32_t q_out;      // write NVFP4 (q_codes, q_scales under q_global[0]) instead of y
+  const float* q_global;
+  uint8_t* q_codes;
+  uint8_t* q_scales;
 };
+
+// One 16-column block of output row m (columns n .. n+15, all valid) as NVFP4: the same
+// encoder as the quantizer, under the given global scale.
+__device__ __forceinline__ void store_block_nvfp4(const GemmArgs& g, int m, int n, const float (&v)[16]) {
+  uint32_t sb, lo, hi;
+  encode_block(v, g.q_global[0], sb, lo, hi);
+  *reinterpret_cast<uint2*>(g.q_codes + (int64_t)m * (g.N / 2) + n / 2) = make_uint2(lo, hi);
+  g.q_scales[(int64_t)m * (g.N / 16) + n / 16] = (uint8_t)sb;
+}
 
 __device__ __forceinline__ int segment_of(int n, const SegmentTable& seg) {
   int s = 0;
@@ -287,7 +300,7 @@ __device__ __forceinline__ void prefill_stage(const GemmArgs& g, uint8_t* lds, i
 // One T x T output tile (T = 256 or 128) on 4 waves in a 2 x 2 grid, each wave T/2 x T/2 as
 // (T/64) x (T/64) MFMA 32x32x16 f16 tiles, over the whole K range in 256-deep stages
 // double-buffered in LDS.
-template <int T>
+template <int T, bool QOUT>
 __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, int m0, int n0) {
   using C = TileCfg<T>;
   constexpr int F = C::F;
@@ -349,6 +362,49 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
   float sw[F];
 #pragma unroll
   for (int j = 0; j < F; ++j) sw[j] = col_scale[wn + 32 * j + r];
+  if constexpr (QOUT) {
+    // NVFP4 output: the scaled fp32 results go through LDS in passes of 128 tile rows (row
+    // pitch T + 8 floats, so the two row groups one write touches use disjoint banks); then
+    // each thread encodes whole 16-column blocks of a row.
+    constexpr int kQPitch = T + 8;
+    constexpr int kQPasses = T / 128;
+    constexpr int kBlocksPerRow = T / 16;
+    float* out = reinterpret_cast<float*>(lds);
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < kQPasses; ++p) {
+      if (wm == 128 * p || kQPasses == 1) {
+#pragma unroll
+        for (int i = 0; i < F; ++i)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int tr = wm + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);   // row in the tile
+            const float sam = row_scale[tr];
+#pragma unroll
+            for (int j = 0; j < F; ++j) out[(tr - 128 * p) * kQPitch + wn + 32 * j + r] = (acc[i][j][q] * sam) * sw[j];
+          }
+      }
+      __syncthreads();
+      for (int b = threadIdx.x; b < 128 * kBlocksPerRow; b += kPrefillThreads) {
+        const int lr = b / kBlocksPerRow, cb = b % kBlocksPerRow;
+        const int m = m0 + 128 * p + lr, n = n0 + 16 * cb;
+        if (m < g.M && n < g.N) {
+          float v[16];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float4 f = *reinterpret_cast<const float4*>(out + lr * kQPitch + 16 * cb + 4 * e);
+            v[4 * e] = f.x;
+            v[4 * e + 1] = f.y;
+            v[4 * e + 2] = f.z;
+            v[4 * e + 3] = f.w;
+          }
+          store_block_nvfp4(g, m, n, v);
+        }
+      }
+      if (p + 1 < kQPasses) __syncthreads();
+    }
+    return;
+  }
   if (!g.y_bf16) {
     // fp32: each store instruction covers 128 contiguous bytes of two rows; store directly.
 #pragma unroll
@@ -434,16 +490,17 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
 // compute 128 x 128 tiles over columns [n_split, N).  Peeling the last tile columns into
 // small tiles keeps the final dispatch round from running a few large tiles on a mostly
 // idle GPU.
+template <bool QOUT>
 __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(GemmArgs g, int n_split, int tiles_big) {
   extern __shared__ __align__(16) uint8_t lds[];
   if ((int)blockIdx.x < tiles_big) {
     int tm, tn;
     tile_coords(blockIdx.x, (g.M + 255) / 256, (n_split + 255) / 256, tm, tn);
-    prefill_tile<256>(g, lds, tm * 256, tn * 256);
+    prefill_tile<256, QOUT>(g, lds, tm * 256, tn * 256);
   } else {
     int tm, tn;
     tile_coords(blockIdx.x - tiles_big, (g.M + 127) / 128, (g.N - n_split + 127) / 128, tm, tn);
-    prefill_tile<128>(g, lds, tm * 128, n_split + tn * 128);
+    prefill_tile<128, QOUT>(g, lds, tm * 128, n_split + tn * 128);
   }
 }
 
@@ -532,6 +589,46 @@ __device__ __forceinline__ void decode_chunk_mma(const DecodeChunk& d, f32x4_t& 
   }
 }
 
+// Epilogue of the decode kernels: the 4 wavefronts' 16x16 tiles (red[(wave * 2 + group) * 64 +
+// lane]) are summed in a fixed order, scaled (y = (sum * s_gA[m]) * s_gW[seg(n)]) and stored; for
+// NVFP4 output the scaled values of the 16 x 32 tile go through qy (16 x 32 floats of LDS) and
+// each of the first 32 threads encodes one 16-column block.
+constexpr int kDecodeRowsE = 32;
+__device__ __forceinline__ void decode_epilogue(const GemmArgs& g, const f32x4_t* red, float* qy, int wave, int lane,
+                                                int n0) {
+  const int rr = lane & 15, grp = lane >> 4;
+  __syncthreads();
+  if (wave < 2) {
+    // D[m][n] of a 16x16 tile sits in lane n + 16 (m / 4), register m % 4.
+    f32x4_t sum = f32x4_t{};
+    for (int w = 0; w < 4; ++w) sum += red[(w * 2 + wave) * 64 + lane];
+    const int n = n0 + 16 * wave + rr;
+    const float sw = n < g.N ? g.w_globals[segment_of(n, g.seg)] : 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int m = 4 * grp + q;
+      const float v = m < g.M && n < g.N ? (sum[q] * g.a_global[g.a_per_row ? m : 0]) * sw : 0.0f;
+      if (g.q_out)
+        qy[m * kDecodeRowsE + 16 * wave + rr] = v;
+      else if (m < g.M && n < g.N)
+        store_out(g, m, n, v);
+    }
+  }
+  if (g.q_out) {
+    __syncthreads();
+    const int t = (int)threadIdx.x;
+    if (t < 32) {
+      const int m = t >> 1, n = n0 + 16 * (t & 1);
+      if (m < g.M && n < g.N) {
+        float v[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = qy[m * kDecodeRowsE + 16 * (t & 1) + e];
+        store_block_nvfp4(g, m, n, v);
+      }
+    }
+  }
+}
+
 // M <= 16 tokens: memory-bound streaming of W in one launch.  Workgroup x owns W rows
 // [32x, 32x + 32) (two 16-row MFMA groups) and the whole K range; wavefront w takes the
 // 256-wide K stages w, w + 4, w + 8, ... (so a workgroup's loads in flight cover contiguous
@@ -545,7 +642,8 @@ constexpr int kDecodeRows = 32;             // W rows per workgroup: two 16-row 
 constexpr int kDecodeDepth = 4;             // 256-wide stages in flight per lane
 
 __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(GemmArgs g) {
-  __shared__ f32x4_t red[kDecodeWaves][2][64];
+  __shared__ f32x4_t red[kDecodeWaves * 2 * 64];
+  __shared__ float qy[16 * kDecodeRows];
   // wave is uniform: made explicit so that the stage loop's exits are scalar branches.
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int rr = lane & 15, grp = lane >> 4;
@@ -612,23 +710,9 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(GemmArgs g)
                       g.w_codes + wr1 * kb + c * 64 + grp * 16, g.w_scales + wr1 * ks + c * 8 + grp * 2, d);
     decode_chunk_mma(d, acc0, acc1);
   }
-  red[wave][0][lane] = acc0;
-  red[wave][1][lane] = acc1;
-  __syncthreads();
-  if (wave < 2) {
-    // D[m][n] of a 16x16 tile sits in lane n + 16 (m / 4), register m % 4.
-    f32x4_t sum = f32x4_t{};
-    for (int w = 0; w < kDecodeWaves; ++w) sum += red[w][wave][lane];
-    const int n = n0 + 16 * wave + rr;
-    if (n < g.N) {
-      const float sw = g.w_globals[segment_of(n, g.seg)];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = 4 * grp + q;
-        if (m < g.M) store_out(g, m, n, (sum[q] * g.a_global[g.a_per_row ? m : 0]) * sw);
-      }
-    }
-  }
+  red[(wave * 2 + 0) * 64 + lane] = acc0;
+  red[(wave * 2 + 1) * 64 + lane] = acc1;
+  decode_epilogue(g, red, qy, wave, lane, n0);
 }
 
 // M <= 16 tokens, K a multiple of 256: the same work as gemm_decode_kernel, but every load
@@ -735,21 +819,7 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(GemmArg
   f32x4_t* red = reinterpret_cast<f32x4_t*>(lds + kDlRedOffset);
   red[(wave * 2 + 0) * 64 + lane] = acc0;
   red[(wave * 2 + 1) * 64 + lane] = acc1;
-  __syncthreads();
-  if (wave < 2) {
-    // D[m][n] of a 16x16 tile sits in lane n + 16 (m / 4), register m % 4.
-    f32x4_t sum = f32x4_t{};
-    for (int w = 0; w < kDecodeWaves; ++w) sum += red[(w * 2 + wave) * 64 + lane];
-    const int n = n0 + 16 * wave + rr;
-    if (n < g.N) {
-      const float sw = g.w_globals[segment_of(n, g.seg)];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = 4 * grp + q;
-        if (m < g.M) store_out(g, m, n, (sum[q] * g.a_global[g.a_per_row ? m : 0]) * sw);
-      }
-    }
-  }
+  decode_epilogue(g, red, reinterpret_cast<float*>(lds), wave, lane, n0);
 }
 
 // ------------------------------------------------------------------ plain kernel
@@ -790,9 +860,11 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
                 const float* a_global, int a_global_per_row, const uint8_t* w_codes, const uint8_t* w_scales,
                 const float* w_globals, const SegmentTable& seg, void* y, int y_dtype, int64_t ldy, void* workspace,
-                hipStream_t stream) {
+                hipStream_t stream, const QuantOut* qout) {
   (void)workspace;
   if (M == 0 || N == 0) return NVFP4_OK;
+  const bool plain = K % 128 != 0 || (M > 16 && (K % BK != 0 || K >= (1 << 24)));
+  if (qout && (plain || N % 16 != 0)) return NVFP4_ERR_UNSUPPORTED;
   GemmArgs g;
   g.M = (int32_t)M;
   g.N = (int32_t)N;
@@ -809,7 +881,11 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
   g.ldy = ldy;
   g.y_vec = reinterpret_cast<uintptr_t>(y) % 16 == 0 && (ldy * (g.y_bf16 ? 2 : 4)) % 16 == 0;
   g.seg = seg;
-  if (K % 128 != 0 || (M > 16 && (K % BK != 0 || K >= (1 << 24)))) {
+  g.q_out = qout != nullptr;
+  g.q_global = qout ? qout->global : nullptr;
+  g.q_codes = qout ? qout->codes : nullptr;
+  g.q_scales = qout ? qout->scales : nullptr;
+  if (plain) {
     const int64_t total = M * N;
     gemm_plain_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(g);
   } else if (M <= 16 && K % 256 == 0) {
@@ -832,7 +908,9 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return NVFP4_ERR_HIP;
     if (!attr_set[dev]) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_prefill_kernel),
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_prefill_kernel<false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kPrefillLds) != hipSuccess ||
+          hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_prefill_kernel<true>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, kPrefillLds) != hipSuccess)
         return NVFP4_ERR_HIP;
       if (hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -851,8 +929,12 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
     }
     const int64_t big = tm * ((n_split + 255) / 256);
     const int64_t small = peel ? ((M + 127) / 128) * ((N - n_split + 127) / 128) : 0;
-    gemm_prefill_kernel<<<(unsigned)(big + small), kPrefillThreads, kPrefillLds, stream>>>(g, (int)n_split,
-                                                                                          (int)big);
+    if (g.q_out)
+      gemm_prefill_kernel<true><<<(unsigned)(big + small), kPrefillThreads, kPrefillLds, stream>>>(g, (int)n_split,
+                                                                                               (int)big);
+    else
+      gemm_prefill_kernel<false><<<(unsigned)(big + small), kPrefillThreads, kPrefillLds, stream>>>(g, (int)n_split,
+                                                                                                (int)big);
   }
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }

@@ -47,10 +47,21 @@ struct SegmentTable {
   int32_t bound[NVFP4_MAX_SEGMENTS + 1];   // column offsets; bound[0] = 0, bound[count] = N
 };
 
+// NVFP4 output of the GEMM (quantized for the next linear layer under a given global
+// scale): codes [M, N/2], scale bytes [M, N/16], both row-major and contiguous.
+struct QuantOut {
+  const float* global;
+  uint8_t* codes;
+  uint8_t* scales;
+};
+
+// With qout set, y is unused and the result is written as NVFP4 instead; then N % 16 == 0 and
+// the shape must be one the MFMA kernels take (NVFP4_ERR_UNSUPPORTED otherwise).
 int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
                 const float* a_global, int a_global_per_row, const uint8_t* w_codes,
                 const uint8_t* w_scales, const float* w_globals, const SegmentTable& seg,
-                void* y, int y_dtype, int64_t ldy, void* workspace, hipStream_t stream);
+                void* y, int y_dtype, int64_t ldy, void* workspace, hipStream_t stream,
+                const QuantOut* qout = nullptr);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 }  // namespace nvfp4

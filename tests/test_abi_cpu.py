@@ -152,3 +152,18 @@ def test_m0_is_only_set_for_lds_copies(tmp_path):
     # global_load_lds reads M0 implicitly: each one must follow its own M0 write.
     loads = [i for i, l in enumerate(code) if l.startswith("global_load_lds")]
     assert all(code[i - 1].startswith("s_mov_b32 m0,") for i in loads)
+
+
+def test_nvfp4_out_argument_errors(nv):
+    f = nv.lib.nvfp4_gemm_nvfp4_out
+    w16 = (ctypes.c_int64 * 1)(16)
+    w40 = (ctypes.c_int64 * 1)(40)
+
+    def call(M=32, K=256, widths=w16, n=1, gy=A16, yc=A16, ys=A16):
+        return f(M, K, A16, A16, A16, 0, n, ctypes.cast(widths, ctypes.c_void_p), A16, A16, A16, gy, yc, ys, None)
+
+    assert call(widths=w40) == 1                   # N not a multiple of 16
+    assert call(gy=None) == 1 and call(yc=None) == 1 and call(ys=A16 + 8) == 1
+    assert call(K=272) == 2                        # K not a multiple of 128: no kernel takes it
+    assert call(M=32, K=384) == 2                  # M > 16 needs K % 256 == 0
+    assert call(M=0) == 0                          # empty product: a no-op
