@@ -39,6 +39,16 @@ notes of this repository):
   R8 Dequantized value = E2M1(code) * E4M3(s_j) * s_g (exact in float64).
   R9 A tensor (per-tensor mode) or row (per-row mode) holding a NaN or an infinity has a
      non-finite global scale; its codes and scales are unspecified and not compared.
+
+FP8 KV-cache codec (the pages' second serving finding: calibrated FP8 key-value cache scales
+are performance-free -- paper abstract; "Quantizing All Layers Reveals Recurrent Memory Is
+Robust" (freegardner), "The Calibrated Cache That Ships for Free"; "NVFP4 W4A4 Quantization
+Compresses 27B Hybrid Models", "Efficiency Gains and Serving Optimization"):
+  R10 FP8 is the OCP E4M3FN byte of R2; one calibrated scale s per tensor (K and V each),
+      given by the caller.
+  R11 Quantize: byte = sign | E4M3_RNE_SAT(fl32(|x| / s)) (the binary32 quotient, then R6);
+      +-inf saturates to +-448, NaN gives 0x7F | sign.
+  R12 Dequantize: fl32(E4M3(byte) * s) (one binary32 rounding), NaN for 0x7F/0xFF.
 """
 from __future__ import annotations
 
@@ -259,3 +269,26 @@ def fused_shared_scale(a: NVFP4, segments: list[NVFP4], shared: float, a_rows=No
 def nvfp4_bytes(rows: int, cols: int, global_scales: int = 1) -> int:
     """Storage of one NVFP4 tensor: 4-bit codes + one byte per 16 elements + fp32 scales."""
     return rows * cols // 2 + rows * cols // BLOCK + 4 * global_scales
+
+
+# ------------------------------------------------------------------------------ FP8 KV cache
+
+def fp8_kv_quantize(x, scale: float) -> np.ndarray:
+    """FP8 (E4M3FN) bytes of x under the calibrated per-tensor scale s (R10, R11): the
+    binary32 quotient x / s, rounded to the nearest E4M3 value (ties to even), saturating at
+    448; the sign bit is copied (so -0 gives 0x80); NaN gives 0x7F with the sign."""
+    x32 = np.asarray(x, dtype=F32)
+    t = (x32 / F32(scale)).astype(F32)                      # IEEE binary32 division
+    sign = np.where(np.signbit(t), 0x80, 0).astype(np.uint8)
+    a = np.abs(t).astype(F64)
+    nan = np.isnan(a)
+    mag = e4m3_rne_sat(np.where(nan, 0.0, a))
+    mag = np.where(nan, 0x7F, mag).astype(np.uint8)
+    return (mag | sign).astype(np.uint8)
+
+
+def fp8_kv_dequantize(q, scale: float) -> np.ndarray:
+    """fl32(E4M3(byte) * s) (R12): the product of two binary32 numbers is exact in float64,
+    so one rounding to float32 gives the binary32 product."""
+    v = e4m3_decode(np.asarray(q, dtype=np.uint8))
+    return (v * F64(F32(scale))).astype(F32)
