@@ -314,6 +314,38 @@ def bench_nvfp4_out(nv, steps: int, warmup: int, settle_s: float = 0.0):
     return out
 
 
+def bench_kv_fp8(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: int = 6):
+    """FP8 KV-cache codec on a K (or V) cache of 32768 tokens x 8 heads x 128 dims in bf16
+    (64 MiB), rotating copies (6 x 64 MiB > the 256 MB MALL); scale calibrated as max|K| / 448.
+    Algorithmic bytes: 3 per element each way (2 B bf16 + 1 B FP8)."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(12)
+    k0 = (torch.randn(32768, 1024, generator=g) * torch.linspace(0.2, 3.0, 1024)).to(torch.bfloat16).to(dev)
+    ks = [k0] + [k0.roll(i + 1, dims=0).contiguous() for i in range(rotate - 1)]
+    s = (k0.float().abs().max() / 448.0).reshape(1)
+    qs = [nv.fp8_kv_quantize(k, s) for k in ks]
+    ys = [torch.empty_like(k0) for _ in range(rotate)]
+    n = k0.numel()
+    out = {"elements": n, "scale": float(s.item())}
+    for name, fn in (("quantize", lambda i: nv.fp8_kv_quantize(ks[i % rotate], s, out=qs[i % rotate])),
+                     ("dequantize", lambda i: nv.fp8_kv_dequantize(qs[i % rotate], s, torch.bfloat16,
+                                                                 out=ys[i % rotate]))):
+        _settle(fn, settle_s)
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        evs = [_events(2) for _ in range(steps)]
+        for i in range(steps):
+            evs[i][0].record()
+            fn(i)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+        gbs = 3.0 * n / (us * 1e-6) / 1e9
+        out[name] = {"us": us, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,7 +353,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--settle-s", type=float, default=1.0,
                     help="seconds of untimed steps before the warmup steps, for steady clocks")
-    ap.add_argument("--workload", choices=["prefill", "decode", "fused", "nvfp4_out"], default="prefill")
+    ap.add_argument("--workload", choices=["prefill", "decode", "fused", "nvfp4_out", "kv_fp8"], default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=TRAFFIC_JSON,
                     help="HBM bytes per GEMM launch measured with rocprofv3 counters")
@@ -343,6 +375,9 @@ def main() -> int:
     copy_calibration(args.copy_calibration_mb)
     if args.workload == "decode":
         print(json.dumps({"workload": "decode", "results": bench_decode(nv, args.steps, args.warmup, args.settle_s)}))
+        return 0
+    if args.workload == "kv_fp8":
+        print(json.dumps({"workload": "kv_fp8", "results": bench_kv_fp8(nv, args.steps, args.warmup, args.settle_s)}))
         return 0
     if args.workload == "nvfp4_out":
         print(json.dumps({"workload": "nvfp4_out", "results": bench_nvfp4_out(nv, args.steps, args.warmup,

@@ -9,7 +9,8 @@
  *   3. the fused-module GEMM in which several separately calibrated modules share one
  *      launch and each column segment keeps its own weight global scale (the repair of the
  *      global-scale mismatch);
- *   4. the GEMM whose output leaves already quantized to NVFP4 for the next linear layer.
+ *   4. the GEMM whose output leaves already quantized to NVFP4 for the next linear layer;
+ *   5. the FP8 (E4M3) key-value cache codec with calibrated per-tensor scales.
  *
  * Sources: the element format (E2M1 values, one E4M3 scale per 16-element block) is from
  * "NVFP4 W4A4 Quantization Compresses 27B Hybrid Models" (thevalue.engineering), section
@@ -158,6 +159,26 @@ int nvfp4_gemm_nvfp4_out(int64_t M, int64_t K,
                          void* stream);
 
 size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/*
+ * FP8 key-value cache codec with a calibrated per-tensor scale (the pages' second serving
+ * finding: calibrated FP8 KV-cache scales are performance-free -- paper abstract;
+ * "Quantizing All Layers Reveals Recurrent Memory Is Robust", "The Calibrated Cache That
+ * Ships for Free"; "NVFP4 W4A4 Quantization Compresses 27B Hybrid Models", "Efficiency Gains
+ * and Serving Optimization").  FP8 is the OCP E4M3FN byte of the file header; the tensor is
+ * treated as n contiguous elements (e.g. a K or V cache flattened).
+ *   quantize:   q[i] = sign | E4M3_RNE_SAT(fl32(|x[i]| / scale[0])) (round to nearest even,
+ *               saturating at 448; +-inf -> +-448; NaN -> 0x7F).
+ *   dequantize: y[i] = fl32(E4M3(q[i]) * scale[0]) as y_dtype (bf16: round to nearest even);
+ *               0x7F / 0xFF -> NaN.
+ *   x             [n] of x_dtype, 16-byte aligned.   q   [n] bytes, 8-byte aligned.
+ *   y             [n] of y_dtype, 16-byte aligned.   scale device [1], finite and > 0.
+ *   n >= 0        n == 0 is a no-op.
+ */
+int nvfp4_fp8_kv_quantize(const void* x, int x_dtype, int64_t n, const float* scale, uint8_t* q,
+                          void* stream);
+int nvfp4_fp8_kv_dequantize(const uint8_t* q, int64_t n, const float* scale, void* y, int y_dtype,
+                            void* stream);
 
 /* Static description of a status code. */
 const char* nvfp4_status_string(int status);

@@ -12,6 +12,8 @@ Entry points (same names as the C ABI):
                                          -> Y with one weight global scale per segment
   gemm_nvfp4_out(a, w_codes, w_scales, widths, w_globals, y_global)
                                          -> Y quantized to NVFP4 under a given global scale
+  fp8_kv_quantize(x, scale) / fp8_kv_dequantize(q, scale, out_dtype)
+                                         -> FP8 (E4M3) KV-cache codec, calibrated scale
 """
 from __future__ import annotations
 
@@ -23,7 +25,8 @@ from typing import Sequence
 import torch
 
 __all__ = [
-    "NVFP4Tensor", "NVFP4Error", "quantize", "gemm", "gemm_fused_segments", "gemm_nvfp4_out", "library_path", "lib",
+    "NVFP4Tensor", "NVFP4Error", "quantize", "gemm", "gemm_fused_segments", "gemm_nvfp4_out", "fp8_kv_quantize", "fp8_kv_dequantize",
+    "library_path", "lib",
     "PER_TENSOR", "PER_ROW", "GIVEN", "MAX_SEGMENTS", "EXPORTED_SYMBOLS",
 ]
 
@@ -36,7 +39,8 @@ _F32, _BF16 = 0, 1
 MAX_SEGMENTS = 64
 EXPORTED_SYMBOLS = (
     "nvfp4_quantize", "nvfp4_quantize_workspace_size", "nvfp4_gemm", "nvfp4_gemm_fused_segments",
-    "nvfp4_gemm_nvfp4_out", "nvfp4_gemm_workspace_size", "nvfp4_status_string", "nvfp4_version",
+    "nvfp4_gemm_nvfp4_out", "nvfp4_gemm_workspace_size", "nvfp4_fp8_kv_quantize", "nvfp4_fp8_kv_dequantize",
+    "nvfp4_status_string", "nvfp4_version",
 )
 
 
@@ -46,7 +50,7 @@ def library_path() -> str:
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} is not built; run `python -m nvfp4_w4a4_block_amd.build`")
+        raise ImportError(f"{_LIB_PATH} is not built; run `python nvfp4_w4a4_block_amd/build.py`")
     L = ctypes.CDLL(_LIB_PATH)
     p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     L.nvfp4_quantize.argtypes = [p, i32, i64, i64, i64, p, p, p, i32, p, sz, p]
@@ -59,6 +63,10 @@ def _load() -> ctypes.CDLL:
     L.nvfp4_gemm_fused_segments.restype = i32
     L.nvfp4_gemm_nvfp4_out.argtypes = [i64, i64, p, p, p, i32, i32, p, p, p, p, p, p, p, p]
     L.nvfp4_gemm_nvfp4_out.restype = i32
+    L.nvfp4_fp8_kv_quantize.argtypes = [p, i32, i64, p, p, p]
+    L.nvfp4_fp8_kv_quantize.restype = i32
+    L.nvfp4_fp8_kv_dequantize.argtypes = [p, i64, p, p, i32, p]
+    L.nvfp4_fp8_kv_dequantize.restype = i32
     L.nvfp4_gemm_workspace_size.argtypes = [i64, i64, i64]
     L.nvfp4_gemm_workspace_size.restype = sz
     L.nvfp4_status_string.argtypes = [i32]
@@ -224,3 +232,28 @@ def gemm_nvfp4_out(a: NVFP4Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor
                                   _ptr(out.scales), _stream(dev))
     _check(st, "nvfp4_gemm_nvfp4_out")
     return out
+
+
+def fp8_kv_quantize(x: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """FP8 (E4M3FN) bytes of a contiguous bf16/fp32 GPU tensor under the calibrated scale
+    (fp32 GPU tensor of one element); the result has x's shape, dtype uint8."""
+    _require(x.is_cuda and x.is_contiguous() and x.dtype in (torch.bfloat16, torch.float32), "x: contiguous bf16/fp32 GPU")
+    _require(scale.dtype == torch.float32 and scale.is_cuda and scale.numel() == 1, "scale: fp32 [1]")
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
+    _require(q.shape == x.shape and q.dtype == torch.uint8 and q.is_contiguous(), "bad out tensor")
+    st = lib.nvfp4_fp8_kv_quantize(_ptr(x), _BF16 if x.dtype == torch.bfloat16 else _F32, x.numel(), _ptr(scale),
+                                   _ptr(q), _stream(x.device))
+    _check(st, "nvfp4_fp8_kv_quantize")
+    return q
+
+
+def fp8_kv_dequantize(q: torch.Tensor, scale: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                      out: torch.Tensor | None = None) -> torch.Tensor:
+    """Values fl32(E4M3(q) * scale) of FP8 bytes, as bf16 or fp32 (same shape as q)."""
+    _require(q.is_cuda and q.is_contiguous() and q.dtype == torch.uint8, "q: contiguous uint8 GPU")
+    _require(scale.dtype == torch.float32 and scale.is_cuda and scale.numel() == 1, "scale: fp32 [1]")
+    y = torch.empty(q.shape, dtype=out_dtype, device=q.device) if out is None else out
+    _require(y.shape == q.shape and y.dtype == out_dtype and y.is_contiguous(), "bad out tensor")
+    st = lib.nvfp4_fp8_kv_dequantize(_ptr(q), q.numel(), _ptr(scale), _ptr(y), _y_dtype(out_dtype), _stream(q.device))
+    _check(st, "nvfp4_fp8_kv_dequantize")
+    return y

@@ -1,6 +1,7 @@
 """Build ``libnvfp4.so`` (the HIP kernels and the C ABI) for gfx950 with hipcc, in-tree.
 
-Run ``python -m nvfp4_w4a4_block_amd.build``.  The library lands next to this file.
+Run ``python nvfp4_w4a4_block_amd/build.py`` (as a script: importing the package would load the
+library this builds).  The library lands next to this file.
 """
 from __future__ import annotations
 
@@ -11,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvfp4.so")
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "kv_fp8.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -149,4 +149,18 @@ int nvfp4_gemm_nvfp4_out(int64_t M, int64_t K, const uint8_t* a_codes, const uin
                      nullptr, NVFP4_BF16, N, nullptr, static_cast<hipStream_t>(stream), &q);
 }
 
+int nvfp4_fp8_kv_quantize(const void* x, int x_dtype, int64_t n, const float* scale, uint8_t* q, void* stream) {
+  if (n < 0 || (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16)) return NVFP4_ERR_INVALID_ARG;
+  if (n == 0) return NVFP4_OK;
+  if (!x || !scale || !q || !aligned(x, 16) || !aligned(scale, 4) || !aligned(q, 8)) return NVFP4_ERR_INVALID_ARG;
+  return launch_kv_quantize(x, x_dtype, n, scale, q, static_cast<hipStream_t>(stream));
+}
+
+int nvfp4_fp8_kv_dequantize(const uint8_t* q, int64_t n, const float* scale, void* y, int y_dtype, void* stream) {
+  if (n < 0 || (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16)) return NVFP4_ERR_INVALID_ARG;
+  if (n == 0) return NVFP4_OK;
+  if (!q || !scale || !y || !aligned(q, 8) || !aligned(scale, 4) || !aligned(y, 16)) return NVFP4_ERR_INVALID_ARG;
+  return launch_kv_dequantize(q, n, scale, y, y_dtype, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

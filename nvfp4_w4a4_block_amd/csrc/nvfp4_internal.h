@@ -64,4 +64,8 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
                 const QuantOut* qout = nullptr);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+// FP8 KV-cache codec launchers (kv_fp8.hip).
+int launch_kv_quantize(const void* x, int x_dtype, int64_t n, const float* scale, uint8_t* q, hipStream_t stream);
+int launch_kv_dequantize(const uint8_t* q, int64_t n, const float* scale, void* y, int y_dtype, hipStream_t stream);
+
 }  // namespace nvfp4

@@ -47,7 +47,7 @@ Compresses 27B Hybrid Models", "Efficiency Gains and Serving Optimization"):
   R10 FP8 is the OCP E4M3FN byte of R2; one calibrated scale s per tensor (K and V each),
       given by the caller.
   R11 Quantize: byte = sign | E4M3_RNE_SAT(fl32(|x| / s)) (the binary32 quotient, then R6);
-      +-inf saturates to +-448, NaN gives 0x7F | sign.
+      +-inf saturates to +-448, NaN gives 0x7F (the sign of a NaN quotient is not portable).
   R12 Dequantize: fl32(E4M3(byte) * s) (one binary32 rounding), NaN for 0x7F/0xFF.
 """
 from __future__ import annotations
@@ -276,15 +276,14 @@ def nvfp4_bytes(rows: int, cols: int, global_scales: int = 1) -> int:
 def fp8_kv_quantize(x, scale: float) -> np.ndarray:
     """FP8 (E4M3FN) bytes of x under the calibrated per-tensor scale s (R10, R11): the
     binary32 quotient x / s, rounded to the nearest E4M3 value (ties to even), saturating at
-    448; the sign bit is copied (so -0 gives 0x80); NaN gives 0x7F with the sign."""
+    448; the sign bit is copied (so -0 gives 0x80); NaN gives 0x7F."""
     x32 = np.asarray(x, dtype=F32)
     t = (x32 / F32(scale)).astype(F32)                      # IEEE binary32 division
     sign = np.where(np.signbit(t), 0x80, 0).astype(np.uint8)
     a = np.abs(t).astype(F64)
     nan = np.isnan(a)
     mag = e4m3_rne_sat(np.where(nan, 0.0, a))
-    mag = np.where(nan, 0x7F, mag).astype(np.uint8)
-    return (mag | sign).astype(np.uint8)
+    return np.where(nan, 0x7F, mag | sign).astype(np.uint8)
 
 
 def fp8_kv_dequantize(q, scale: float) -> np.ndarray:

@@ -167,3 +167,13 @@ def test_nvfp4_out_argument_errors(nv):
     assert call(K=272) == 2                        # K not a multiple of 128: no kernel takes it
     assert call(M=32, K=384) == 2                  # M > 16 needs K % 256 == 0
     assert call(M=0) == 0                          # empty product: a no-op
+
+
+def test_fp8_kv_argument_errors(nv):
+    q, d = nv.lib.nvfp4_fp8_kv_quantize, nv.lib.nvfp4_fp8_kv_dequantize
+    assert q(A16, 1, -1, A16, A16, None) == 1 and q(A16, 7, 16, A16, A16, None) == 1
+    assert q(MIS, 1, 16, A16, A16, None) == 1 and q(A16, 1, 16, None, A16, None) == 1
+    assert q(A16, 1, 16, A16, A16 + 4, None) == 1          # q must be 8-byte aligned
+    assert d(A16, 16, A16, A16 + 8, 1, None) == 1          # y must be 16-byte aligned
+    assert d(A16, 16, A16, A16, 5, None) == 1
+    assert q(None, 1, 0, None, None, None) == 0 and d(None, 0, None, None, 0, None) == 0
