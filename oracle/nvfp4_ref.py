@@ -49,6 +49,23 @@ Compresses 27B Hybrid Models", "Efficiency Gains and Serving Optimization"):
   R11 Quantize: byte = sign | E4M3_RNE_SAT(fl32(|x| / s)) (the binary32 quotient, then R6);
       +-inf saturates to +-448, NaN gives 0x7F (the sign of a NaN quotient is not portable).
   R12 Dequantize: fl32(E4M3(byte) * s) (one binary32 rounding), NaN for 0x7F/0xFF.
+
+Gated DeltaNet gate epilogue (the two gate projections of a GDN block, one controlling how
+much of the recurrent state decays per step and one how strongly it is written; their
+parameterization squashes GEMM error -- paper abstract, finding (ii); "Why Gated DeltaNet
+Survives 4-Bit Quantization" (kipquest), "The deep dive"; "Quantizing All Layers Reveals
+Recurrent Memory Is Robust" (freegardner), "The Gates That Were Supposed to Break": the
+gates use softplus, exponential and sigmoid; the deep dive's scope paragraph: the decay is
+parameterized in log space through softplus and exponential):
+  R13 The fused GDN input projection ends with two segments of equal width H (one column
+      per value head): the write-strength projection b, then the decay projection a.  Per
+      head h: write strength beta = sigmoid(y_b) = 1 / (1 + e^-y_b); log-space decay
+      g = -exp(A_log[h]) * softplus(y_a + dt_bias[h]), softplus(z) = ln(1 + e^z); decay
+      factor alpha = e^g in (0, 1].  A_log and dt_bias are per-head float32 parameters.
+      (The pages name the functions but print no formula; this is the standard Gated
+      DeltaNet / Mamba-2 gate parameterization that matches their description.)
+  R14 The gates take the GEMM's float32 output value y (global scales applied, R8 and the
+      fused-segment repair) before any output rounding; g and beta are float32.
 """
 from __future__ import annotations
 
@@ -291,3 +308,44 @@ def fp8_kv_dequantize(q, scale: float) -> np.ndarray:
     so one rounding to float32 gives the binary32 product."""
     v = e4m3_decode(np.asarray(q, dtype=np.uint8))
     return (v * F64(F32(scale))).astype(F32)
+
+
+# ------------------------------------------------------------------------------ GDN gates
+
+def sigmoid(y) -> np.ndarray:
+    """1 / (1 + e^-y) in float64 (R13), in the form that never overflows: e^-|y| is at most
+    1, and for y < 0 the value is e^y / (1 + e^y)."""
+    y = np.asarray(y, dtype=F64)
+    e = np.exp(-np.abs(y))
+    return np.where(y >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def softplus(z) -> np.ndarray:
+    """ln(1 + e^z) in float64 (R13), as max(z, 0) + ln(1 + e^-|z|), which is the same
+    number without overflow for large z or loss of e^z for very negative z."""
+    z = np.asarray(z, dtype=F64)
+    return np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+
+
+def gdn_gates(y_b, y_a, a_log, dt_bias):
+    """R13: (g, beta) for pre-activations y_b, y_a of shape [M, H] and per-head A_log,
+    dt_bias of shape [H]: beta = sigmoid(y_b), g = -exp(A_log) * softplus(y_a + dt_bias).
+    Float64 throughout; the parameters are float32 values widened exactly."""
+    a_log = np.asarray(a_log, dtype=F32).astype(F64)
+    dt = np.asarray(dt_bias, dtype=F32).astype(F64)
+    beta = sigmoid(y_b)
+    g = -np.exp(a_log)[None, :] * softplus(np.asarray(y_a, dtype=F64) + dt[None, :])
+    return g, beta
+
+
+def fused_gdn_gates(a: NVFP4, segments: list[NVFP4], a_log, dt_bias, a_rows=None):
+    """The fused GDN input projection with its gate epilogue (R13, R14): Y and T over all
+    segments exactly as ``fused_segments``, and (g, beta) from the last two segments, which
+    must have equal widths H (b, then a)."""
+    if len(segments) < 2 or segments[-1].rows != segments[-2].rows:
+        raise ValueError("the last two segments must be the two gate projections of equal width")
+    Y, T = fused_segments(a, segments, a_rows)
+    H = segments[-1].rows
+    N = Y.shape[1]
+    g, beta = gdn_gates(Y[:, N - 2 * H:N - H], Y[:, N - H:], a_log, dt_bias)
+    return Y, T, g, beta

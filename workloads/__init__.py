@@ -185,6 +185,16 @@ class Fused:
     def w(self, i: int) -> np.ndarray:
         return weight(self.seed, 1 + i, self.widths[i], self.K, sigma=self.sigmas[i])
 
+    def gate_params(self) -> tuple[np.ndarray, np.ndarray]:
+        """Per-head parameters of the two gate segments (one head per column of the last
+        two widths): A_log ~ U(0, ln 16) and dt_bias ~ U(-6.9, -2.25), float32.  The pages
+        give no trained values; these ranges put the per-step decay of the synthetic heads
+        anywhere from nearly none to strong."""
+        h = self.widths[-1]
+        a_log = rng(self.seed, 100).uniform(0.0, np.log(16.0), h).astype(np.float32)
+        dt_bias = rng(self.seed, 101).uniform(-6.9, -2.25, h).astype(np.float32)
+        return a_log, dt_bias
+
 
 @dataclass(frozen=True)
 class Launch:
