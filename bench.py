@@ -314,6 +314,76 @@ def bench_nvfp4_out(nv, steps: int, warmup: int, settle_s: float = 0.0):
     return out
 
 
+def _mean_ms(fn, steps: int, warmup: int, settle_s: float) -> float:
+    """Mean duration of fn(i) between events on the current stream, after settling and warmup."""
+    _settle(fn, settle_s)
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    evs = [_events(2) for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        fn(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+
+
+def _rel_rms(got: torch.Tensor, want: torch.Tensor) -> float:
+    d = got.double() - want.double()
+    return float(torch.linalg.vector_norm(d) / torch.linalg.vector_norm(want.double()))
+
+
+def bench_gdn_gates(nv, steps: int, warmup: int, settle_s: float = 0.0):
+    """The fused GDN input projection (M = 8192, K = 5120, six segments) with the gate epilogue
+    in the same launch, beside the same launch without it; and the error compression of the
+    gates on these synthetic inputs: relative RMS error of the NVFP4 path's gate
+    pre-activations, write strength beta and decay factor e^g against the same quantities from
+    the unquantized bf16 operands (fp64 GEMM and gate functions in PyTorch: a measurement
+    reference, not part of the path)."""
+    f = workloads.FUSED
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(f.x()).to(dev).to(torch.bfloat16)
+    ws = [torch.from_numpy(f.w(i)).to(dev).to(torch.bfloat16) for i in range(len(f.widths))]
+    qs = [nv.quantize(w) for w in ws]
+    codes = torch.cat([q.codes for q in qs])
+    scales = torch.cat([q.scales for q in qs])
+    gl = torch.cat([q.global_scale for q in qs])
+    a_log_np, dt_np = f.gate_params()
+    a_log, dt = torch.from_numpy(a_log_np).to(dev), torch.from_numpy(dt_np).to(dev)
+    a = nv.quantize(x)
+    H = f.widths[-1]
+    y = torch.empty((f.M, f.N), dtype=torch.bfloat16, device=dev)
+    g = torch.empty((f.M, H), dtype=torch.float32, device=dev)
+    beta = torch.empty_like(g)
+    out = {}
+    for name, fn in (("fused", lambda i: nv.gemm_fused_segments(a, codes, scales, f.widths, gl, torch.bfloat16,
+                                                                 out=y)),
+                     ("fused_gates", lambda i: nv.gemm_fused_gdn_gates(a, codes, scales, f.widths, gl, a_log, dt,
+                                                                       torch.bfloat16, out=y, g_out=g,
+                                                                       beta_out=beta))):
+        ms = _mean_ms(fn, steps, warmup, settle_s)
+        flops = 2.0 * f.M * f.N * f.K
+        out[name] = {"gemm_ms": ms, "gemm_tflops": flops / (ms * 1e-3) / 1e12,
+                     "frac_mfma_f16": flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS}
+    # Error compression: fp32 pre-activations from the same kernel, against unquantized ones.
+    y32, g, beta = nv.gemm_fused_gdn_gates(a, codes, scales, f.widths, gl, a_log, dt, torch.float32)
+    wb, wa = ws[-2].double(), ws[-1].double()
+    xd = x.double()
+    yb_ref, ya_ref = xd @ wb.T, xd @ wa.T
+    beta_ref = torch.sigmoid(yb_ref)
+    g_ref = -torch.exp(a_log.double()) * torch.nn.functional.softplus(ya_ref + dt.double())
+    N = f.N
+    out["error_compression"] = {
+        "write_strength": {"preactivation": _rel_rms(y32[:, N - 2 * H:N - H], yb_ref), "beta": _rel_rms(beta, beta_ref)},
+        "decay": {"preactivation": _rel_rms(y32[:, N - H:], ya_ref), "decay_factor": _rel_rms(torch.exp(g.double()),
+                                                                                              torch.exp(g_ref)),
+                  "log_decay": _rel_rms(g, g_ref)},
+        "reference": "unquantized bf16 X and W, fp64 GEMM and gate functions",
+    }
+    return out
+
+
 def bench_kv_fp8(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: int = 6):
     """FP8 KV-cache codec on a K (or V) cache of 32768 tokens x 8 heads x 128 dims in bf16
     (64 MiB), rotating copies (6 x 64 MiB > the 256 MB MALL); scale calibrated as max|K| / 448.
@@ -353,7 +423,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--settle-s", type=float, default=1.0,
                     help="seconds of untimed steps before the warmup steps, for steady clocks")
-    ap.add_argument("--workload", choices=["prefill", "decode", "fused", "nvfp4_out", "kv_fp8"], default="prefill")
+    ap.add_argument("--workload", choices=["prefill", "decode", "fused", "nvfp4_out", "kv_fp8", "gdn_gates"],
+                    default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=TRAFFIC_JSON,
                     help="HBM bytes per GEMM launch measured with rocprofv3 counters")
@@ -378,6 +449,10 @@ def main() -> int:
         return 0
     if args.workload == "kv_fp8":
         print(json.dumps({"workload": "kv_fp8", "results": bench_kv_fp8(nv, args.steps, args.warmup, args.settle_s)}))
+        return 0
+    if args.workload == "gdn_gates":
+        print(json.dumps({"workload": "gdn_gates", "results": bench_gdn_gates(nv, args.steps, args.warmup,
+                                                                              args.settle_s)}))
         return 0
     if args.workload == "nvfp4_out":
         print(json.dumps({"workload": "nvfp4_out", "results": bench_nvfp4_out(nv, args.steps, args.warmup,

@@ -10,7 +10,9 @@
  *      launch and each column segment keeps its own weight global scale (the repair of the
  *      global-scale mismatch);
  *   4. the GEMM whose output leaves already quantized to NVFP4 for the next linear layer;
- *   5. the FP8 (E4M3) key-value cache codec with calibrated per-tensor scales.
+ *   5. the FP8 (E4M3) key-value cache codec with calibrated per-tensor scales;
+ *   6. the fused Gated DeltaNet input projection whose two gate segments leave as the
+ *      write strength and the log-space decay, in the same launch.
  *
  * Sources: the element format (E2M1 values, one E4M3 scale per 16-element block) is from
  * "NVFP4 W4A4 Quantization Compresses 27B Hybrid Models" (thevalue.engineering), section
@@ -157,6 +159,38 @@ int nvfp4_gemm_nvfp4_out(int64_t M, int64_t K,
                          const float* w_globals,
                          const float* y_global, uint8_t* y_codes, uint8_t* y_scales,
                          void* stream);
+
+/*
+ * The fused Gated DeltaNet (GDN) input projection with its gate epilogue, in one launch.  The
+ * GDN block has two gate projections, one setting how strongly the recurrent state is written
+ * and one how much of it decays per step; the write strength goes through a sigmoid and the
+ * decay is parameterized in log space through softplus and exponential ("Why Gated DeltaNet
+ * Survives 4-Bit Quantization" (kipquest), "The deep dive", incl. its scope paragraph;
+ * "Quantizing All Layers Reveals Recurrent Memory Is Robust" (freegardner), "The Gates That
+ * Were Supposed to Break").  The pages print no formula; this is the standard GDN gate
+ * parameterization that matches their description.
+ * The last two segments are the gate projections, of equal width H (one column per value
+ * head): the write-strength projection b, then the decay projection a.  Y is written exactly
+ * as nvfp4_gemm_fused_segments writes it (all N columns, gate pre-activations included); in
+ * addition, from each gate column's fp32 value y (before any rounding to y_dtype), for row m
+ * and head j:
+ *   beta[m, j] = 1 / (1 + exp(-y_b[m, j]))                           (write strength)
+ *   g[m, j]    = -exp(a_log[j]) * softplus(y_a[m, j] + dt_bias[j])   (log decay; decay = e^g)
+ * with softplus(z) = ln(1 + e^z), evaluated in fp32 without overflow.
+ *   2 <= num_segments <= NVFP4_MAX_SEGMENTS, seg_n[num_segments-2] == seg_n[num_segments-1] = H.
+ *   a_log, dt_bias  device [H] fp32, 4-byte aligned (per-head parameters).
+ *   g, beta         device out [M, H] fp32, row-major, contiguous, 4-byte aligned.
+ *   Other arguments as in nvfp4_gemm_fused_segments.
+ */
+int nvfp4_gemm_fused_gdn_gates(int64_t M, int64_t K,
+                               const uint8_t* a_codes, const uint8_t* a_scales,
+                               const float* a_global, int a_global_per_row,
+                               int num_segments, const int64_t* seg_n,
+                               const uint8_t* w_codes, const uint8_t* w_scales,
+                               const float* w_globals,
+                               void* y, int y_dtype, int64_t ldy,
+                               const float* a_log, const float* dt_bias, float* g, float* beta,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 

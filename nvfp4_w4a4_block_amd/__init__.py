@@ -14,6 +14,10 @@ Entry points (same names as the C ABI):
                                          -> Y quantized to NVFP4 under a given global scale
   fp8_kv_quantize(x, scale) / fp8_kv_dequantize(q, scale, out_dtype)
                                          -> FP8 (E4M3) KV-cache codec, calibrated scale
+  gemm_fused_gdn_gates(a, w_codes, w_scales, widths, w_globals, a_log, dt_bias, out_dtype)
+                                         -> (Y, g, beta): fused GDN input projection whose
+                                            last two segments leave as log decay and
+                                            write strength
 """
 from __future__ import annotations
 
@@ -25,7 +29,8 @@ from typing import Sequence
 import torch
 
 __all__ = [
-    "NVFP4Tensor", "NVFP4Error", "quantize", "gemm", "gemm_fused_segments", "gemm_nvfp4_out", "fp8_kv_quantize", "fp8_kv_dequantize",
+    "NVFP4Tensor", "NVFP4Error", "quantize", "gemm", "gemm_fused_segments", "gemm_nvfp4_out", "gemm_fused_gdn_gates",
+    "fp8_kv_quantize", "fp8_kv_dequantize",
     "library_path", "lib",
     "PER_TENSOR", "PER_ROW", "GIVEN", "MAX_SEGMENTS", "EXPORTED_SYMBOLS",
 ]
@@ -39,7 +44,7 @@ _F32, _BF16 = 0, 1
 MAX_SEGMENTS = 64
 EXPORTED_SYMBOLS = (
     "nvfp4_quantize", "nvfp4_quantize_workspace_size", "nvfp4_gemm", "nvfp4_gemm_fused_segments",
-    "nvfp4_gemm_nvfp4_out", "nvfp4_gemm_workspace_size", "nvfp4_fp8_kv_quantize", "nvfp4_fp8_kv_dequantize",
+    "nvfp4_gemm_nvfp4_out", "nvfp4_gemm_fused_gdn_gates", "nvfp4_gemm_workspace_size", "nvfp4_fp8_kv_quantize", "nvfp4_fp8_kv_dequantize",
     "nvfp4_status_string", "nvfp4_version",
 )
 
@@ -63,6 +68,9 @@ def _load() -> ctypes.CDLL:
     L.nvfp4_gemm_fused_segments.restype = i32
     L.nvfp4_gemm_nvfp4_out.argtypes = [i64, i64, p, p, p, i32, i32, p, p, p, p, p, p, p, p]
     L.nvfp4_gemm_nvfp4_out.restype = i32
+    L.nvfp4_gemm_fused_gdn_gates.argtypes = [i64, i64, p, p, p, i32, i32, p, p, p, p, p, i32, i64, p, p, p, p,
+                                             p, sz, p]
+    L.nvfp4_gemm_fused_gdn_gates.restype = i32
     L.nvfp4_fp8_kv_quantize.argtypes = [p, i32, i64, p, p, p]
     L.nvfp4_fp8_kv_quantize.restype = i32
     L.nvfp4_fp8_kv_dequantize.argtypes = [p, i64, p, p, i32, p]
@@ -232,6 +240,40 @@ def gemm_nvfp4_out(a: NVFP4Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor
                                   _ptr(out.scales), _stream(dev))
     _check(st, "nvfp4_gemm_nvfp4_out")
     return out
+
+
+def gemm_fused_gdn_gates(a: NVFP4Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
+                         seg_widths: Sequence[int], w_globals: torch.Tensor, a_log: torch.Tensor,
+                         dt_bias: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                         out: torch.Tensor | None = None, g_out: torch.Tensor | None = None,
+                         beta_out: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Fused GDN input projection with the gate epilogue in the same launch.  The last two
+    segments (equal widths H) are the write-strength and decay projections; a_log and dt_bias
+    are fp32 GPU tensors [H].  Returns (Y [M, N] as gemm_fused_segments writes it, g [M, H]
+    fp32 log decay, beta [M, H] fp32 write strength)."""
+    M, K = a.rows, a.cols
+    N = int(sum(seg_widths))
+    _require(len(seg_widths) >= 2 and seg_widths[-1] == seg_widths[-2], "the last two segments are the gates")
+    H = int(seg_widths[-1])
+    _require(w_codes.shape == (N, K // 2) and w_scales.shape == (N, K // 16), "bad fused weight shapes")
+    for t, name in ((a_log, "a_log"), (dt_bias, "dt_bias")):
+        _require(t.is_cuda and t.dtype == torch.float32 and t.is_contiguous() and t.numel() == H, f"{name}: fp32 [H]")
+    dev = a.codes.device
+    y = _out_tensor(M, N, out_dtype, dev, out)
+    g = _out_tensor(M, H, torch.float32, dev, g_out)
+    beta = _out_tensor(M, H, torch.float32, dev, beta_out)
+    _require(g.is_contiguous() and beta.is_contiguous(), "g and beta must be contiguous")
+    per_row = int(a.global_scale.numel() == M and M != 1)
+    widths = (ctypes.c_int64 * len(seg_widths))(*[int(v) for v in seg_widths])
+    ws_bytes = lib.nvfp4_gemm_workspace_size(M, N, K)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev) if ws_bytes else None
+    st = lib.nvfp4_gemm_fused_gdn_gates(M, K, _ptr(a.codes), _ptr(a.scales), _ptr(a.global_scale), per_row,
+                                        len(seg_widths), ctypes.cast(widths, ctypes.c_void_p), _ptr(w_codes),
+                                        _ptr(w_scales), _ptr(w_globals), _ptr(y), _y_dtype(out_dtype),
+                                        y.stride(0) if M > 0 else N, _ptr(a_log), _ptr(dt_bias), _ptr(g),
+                                        _ptr(beta), _ptr(ws), ws_bytes, _stream(dev))
+    _check(st, "nvfp4_gemm_fused_gdn_gates")
+    return y, g, beta
 
 
 def fp8_kv_quantize(x: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:

@@ -27,6 +27,23 @@ int check_gemm_common(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, c
   return NVFP4_OK;
 }
 
+// Column offsets of the fused segments and their total width N.
+int make_segments(int num_segments, const int64_t* seg_n, SegmentTable& seg, int64_t& N) {
+  if (num_segments < 1 || !seg_n) return NVFP4_ERR_INVALID_ARG;
+  if (num_segments > NVFP4_MAX_SEGMENTS) return NVFP4_ERR_UNSUPPORTED;
+  seg = SegmentTable{};
+  seg.count = num_segments;
+  N = 0;
+  for (int i = 0; i < num_segments; ++i) {
+    if (seg_n[i] <= 0) return NVFP4_ERR_INVALID_ARG;
+    seg.bound[i] = (int32_t)N;
+    N += seg_n[i];
+    if (N > INT32_MAX) return NVFP4_ERR_UNSUPPORTED;
+  }
+  seg.bound[num_segments] = (int32_t)N;
+  return NVFP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -98,20 +115,12 @@ int nvfp4_gemm_fused_segments(int64_t M, int64_t K, const uint8_t* a_codes, cons
                               const int64_t* seg_n, const uint8_t* w_codes, const uint8_t* w_scales,
                               const float* w_globals, void* y, int y_dtype, int64_t ldy, void* workspace,
                               size_t workspace_bytes, void* stream) {
-  if (num_segments < 1 || !seg_n) return NVFP4_ERR_INVALID_ARG;
-  if (num_segments > NVFP4_MAX_SEGMENTS) return NVFP4_ERR_UNSUPPORTED;
-  SegmentTable seg{};
-  seg.count = num_segments;
+  SegmentTable seg;
   int64_t N = 0;
-  for (int i = 0; i < num_segments; ++i) {
-    if (seg_n[i] <= 0) return NVFP4_ERR_INVALID_ARG;
-    seg.bound[i] = (int32_t)N;
-    N += seg_n[i];
-    if (N > INT32_MAX) return NVFP4_ERR_UNSUPPORTED;
-  }
-  seg.bound[num_segments] = (int32_t)N;
-  int st = check_gemm_common(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales, y,
-                             y_dtype, ldy);
+  int st = make_segments(num_segments, seg_n, seg, N);
+  if (st != NVFP4_OK) return st;
+  st = check_gemm_common(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales, y, y_dtype,
+                         ldy);
   if (st != NVFP4_OK || M == 0) return st;
   if (!w_globals || !aligned(w_globals, 4)) return NVFP4_ERR_INVALID_ARG;
   const size_t need = gemm_workspace_bytes(M, N, K);
@@ -124,22 +133,14 @@ int nvfp4_gemm_nvfp4_out(int64_t M, int64_t K, const uint8_t* a_codes, const uin
                          const float* a_global, int a_global_per_row, int num_segments, const int64_t* seg_n,
                          const uint8_t* w_codes, const uint8_t* w_scales, const float* w_globals,
                          const float* y_global, uint8_t* y_codes, uint8_t* y_scales, void* stream) {
-  if (num_segments < 1 || !seg_n) return NVFP4_ERR_INVALID_ARG;
-  if (num_segments > NVFP4_MAX_SEGMENTS) return NVFP4_ERR_UNSUPPORTED;
-  SegmentTable seg{};
-  seg.count = num_segments;
+  SegmentTable seg;
   int64_t N = 0;
-  for (int i = 0; i < num_segments; ++i) {
-    if (seg_n[i] <= 0) return NVFP4_ERR_INVALID_ARG;
-    seg.bound[i] = (int32_t)N;
-    N += seg_n[i];
-    if (N > INT32_MAX) return NVFP4_ERR_UNSUPPORTED;
-  }
-  seg.bound[num_segments] = (int32_t)N;
+  int st = make_segments(num_segments, seg_n, seg, N);
+  if (st != NVFP4_OK) return st;
   if (N % 16 != 0) return NVFP4_ERR_INVALID_ARG;
   // y is not written on this path; check_gemm_common's output checks get a stand-in.
-  int st = check_gemm_common(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales,
-                             y_codes, NVFP4_BF16, N);
+  st = check_gemm_common(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales, y_codes,
+                         NVFP4_BF16, N);
   if (st != NVFP4_OK || M == 0) return st;
   if (!w_globals || !aligned(w_globals, 4) || !y_global || !aligned(y_global, 4)) return NVFP4_ERR_INVALID_ARG;
   if (!y_codes || !y_scales || !aligned(y_codes, 16) || !aligned(y_scales, 16)) return NVFP4_ERR_INVALID_ARG;
@@ -147,6 +148,32 @@ int nvfp4_gemm_nvfp4_out(int64_t M, int64_t K, const uint8_t* a_codes, const uin
   QuantOut q{y_global, y_codes, y_scales};
   return launch_gemm(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales, w_globals, seg,
                      nullptr, NVFP4_BF16, N, nullptr, static_cast<hipStream_t>(stream), &q);
+}
+
+int nvfp4_gemm_fused_gdn_gates(int64_t M, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+                               const float* a_global, int a_global_per_row, int num_segments,
+                               const int64_t* seg_n, const uint8_t* w_codes, const uint8_t* w_scales,
+                               const float* w_globals, void* y, int y_dtype, int64_t ldy, const float* a_log,
+                               const float* dt_bias, float* g, float* beta, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  SegmentTable seg;
+  int64_t N = 0;
+  int st = make_segments(num_segments, seg_n, seg, N);
+  if (st != NVFP4_OK) return st;
+  if (num_segments < 2 || seg_n[num_segments - 1] != seg_n[num_segments - 2]) return NVFP4_ERR_INVALID_ARG;
+  st = check_gemm_common(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales, y, y_dtype,
+                         ldy);
+  if (st != NVFP4_OK || M == 0) return st;
+  if (!w_globals || !aligned(w_globals, 4)) return NVFP4_ERR_INVALID_ARG;
+  if (!a_log || !dt_bias || !g || !beta || !aligned(a_log, 4) || !aligned(dt_bias, 4) || !aligned(g, 4) ||
+      !aligned(beta, 4))
+    return NVFP4_ERR_INVALID_ARG;
+  const size_t need = gemm_workspace_bytes(M, N, K);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_ERR_WORKSPACE;
+  const int64_t H = seg_n[num_segments - 1];
+  GateOut gates{(int32_t)(N - 2 * H), (int32_t)H, a_log, dt_bias, g, beta};
+  return launch_gemm(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales, w_globals, seg,
+                     y, y_dtype, ldy, workspace, static_cast<hipStream_t>(stream), nullptr, &gates);
 }
 
 int nvfp4_fp8_kv_quantize(const void* x, int x_dtype, int64_t n, const float* scale, uint8_t* q, void* stream) {

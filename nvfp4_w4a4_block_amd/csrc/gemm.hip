@@ -49,7 +49,18 @@ struct GemmArgs {
   const float* q_global;
   uint8_t* q_codes;
   uint8_t* q_scales;
+  int32_t gate_n0;    // GDN gates (when gate_h > 0): see store_gate
+  int32_t gate_h;
+  const float* gate_a_log;
+  const float* gate_dt_bias;
+  float* gate_g;
+  float* gate_beta;
 };
+
+// Epilogue modes of the MFMA kernels.
+constexpr int kEpiStore = 0;   // Y in fp32 or bf16
+constexpr int kEpiNvfp4 = 1;   // Y as NVFP4 under a given global scale
+constexpr int kEpiGates = 2;   // Y, and the GDN gates of the last two segments
 
 // One 16-column block of output row m (columns n .. n+15, all valid) as NVFP4: the same
 // encoder as the quantizer, under the given global scale.
@@ -71,6 +82,25 @@ __device__ __forceinline__ void store_out(const GemmArgs& g, int m, int n, float
     static_cast<uint16_t*>(g.y)[(int64_t)m * g.ldy + n] = f32_to_bf16_rne(v);
   else
     static_cast<float*>(g.y)[(int64_t)m * g.ldy + n] = v;
+}
+
+// The Gated DeltaNet gates of one fp32 output value y at row m, column n >= gate_n0 (the two
+// gate projections end the fused GDN input projection; "Why Gated DeltaNet Survives 4-Bit
+// Quantization", "The deep dive": the write strength goes through a sigmoid, the decay is
+// parameterized in log space through softplus and exponential).  Column gate_n0 + j is head j
+// of the write strength, beta = 1 / (1 + e^-y); column gate_n0 + gate_h + j is head j of the
+// decay, g = -e^A_log[j] * softplus(y + dt_bias[j]) with softplus(z) = max(z, 0) + ln(1 + e^-|z|),
+// which overflows nowhere.
+__device__ __forceinline__ void store_gate(const GemmArgs& g, int m, int n, float y) {
+  const int c = n - g.gate_n0;
+  if (c < g.gate_h) {
+    g.gate_beta[(int64_t)m * g.gate_h + c] = 1.0f / (1.0f + expf(-y));
+  } else {
+    const int j = c - g.gate_h;
+    const float z = y + g.gate_dt_bias[j];
+    const float sp = fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)));
+    g.gate_g[(int64_t)m * g.gate_h + j] = -expf(g.gate_a_log[j]) * sp;
+  }
 }
 
 // Byte k of a dword as an fp16 scale pair (E4M3 * 2^-8 in both halves).
@@ -300,7 +330,7 @@ __device__ __forceinline__ void prefill_stage(const GemmArgs& g, uint8_t* lds, i
 // One T x T output tile (T = 256 or 128) on 4 waves in a 2 x 2 grid, each wave T/2 x T/2 as
 // (T/64) x (T/64) MFMA 32x32x16 f16 tiles, over the whole K range in 256-deep stages
 // double-buffered in LDS.
-template <int T, bool QOUT>
+template <int T, int EPI>
 __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, int m0, int n0) {
   using C = TileCfg<T>;
   constexpr int F = C::F;
@@ -362,48 +392,65 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
   float sw[F];
 #pragma unroll
   for (int j = 0; j < F; ++j) sw[j] = col_scale[wn + 32 * j + r];
-  if constexpr (QOUT) {
-    // NVFP4 output: the scaled fp32 results go through LDS in passes of 128 tile rows (row
-    // pitch T + 8 floats, so the two row groups one write touches use disjoint banks); then
-    // each thread encodes whole 16-column blocks of a row.
+  if constexpr (EPI == kEpiNvfp4 || EPI == kEpiGates) {
+    // The scaled fp32 results go through LDS in passes of 128 tile rows (row pitch T + 8
+    // floats, so the two row groups one write touches use disjoint banks).  NVFP4 output: each
+    // thread then encodes whole 16-column blocks of a row.  Gates: the tile's gate columns are
+    // read back, one value per thread and step; tiles without gate columns skip this.
     constexpr int kQPitch = T + 8;
     constexpr int kQPasses = T / 128;
     constexpr int kBlocksPerRow = T / 16;
     float* out = reinterpret_cast<float*>(lds);
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < kQPasses; ++p) {
-      if (wm == 128 * p || kQPasses == 1) {
-#pragma unroll
-        for (int i = 0; i < F; ++i)
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int tr = wm + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);   // row in the tile
-            const float sam = row_scale[tr];
-#pragma unroll
-            for (int j = 0; j < F; ++j) out[(tr - 128 * p) * kQPitch + wn + 32 * j + r] = (acc[i][j][q] * sam) * sw[j];
-          }
-      }
-      __syncthreads();
-      for (int b = threadIdx.x; b < 128 * kBlocksPerRow; b += kPrefillThreads) {
-        const int lr = b / kBlocksPerRow, cb = b % kBlocksPerRow;
-        const int m = m0 + 128 * p + lr, n = n0 + 16 * cb;
-        if (m < g.M && n < g.N) {
-          float v[16];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float4 f = *reinterpret_cast<const float4*>(out + lr * kQPitch + 16 * cb + 4 * e);
-            v[4 * e] = f.x;
-            v[4 * e + 1] = f.y;
-            v[4 * e + 2] = f.z;
-            v[4 * e + 3] = f.w;
-          }
-          store_block_nvfp4(g, m, n, v);
-        }
-      }
-      if (p + 1 < kQPasses) __syncthreads();
+    int c0 = 0, c1 = 0;
+    if constexpr (EPI == kEpiGates) {
+      c0 = max(n0, g.gate_n0);
+      c1 = min(n0 + T, g.N);
     }
-    return;
+    if (EPI == kEpiNvfp4 || c0 < c1) {
+      __syncthreads();
+#pragma unroll
+      for (int p = 0; p < kQPasses; ++p) {
+        if (wm == 128 * p || kQPasses == 1) {
+#pragma unroll
+          for (int i = 0; i < F; ++i)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+              const int tr = wm + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);   // row in the tile
+              const float sam = row_scale[tr];
+#pragma unroll
+              for (int j = 0; j < F; ++j)
+                out[(tr - 128 * p) * kQPitch + wn + 32 * j + r] = (acc[i][j][q] * sam) * sw[j];
+            }
+        }
+        __syncthreads();
+        if constexpr (EPI == kEpiNvfp4) {
+          for (int b = threadIdx.x; b < 128 * kBlocksPerRow; b += kPrefillThreads) {
+            const int lr = b / kBlocksPerRow, cb = b % kBlocksPerRow;
+            const int m = m0 + 128 * p + lr, n = n0 + 16 * cb;
+            if (m < g.M && n < g.N) {
+              float v[16];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float4 f = *reinterpret_cast<const float4*>(out + lr * kQPitch + 16 * cb + 4 * e);
+                v[4 * e] = f.x;
+                v[4 * e + 1] = f.y;
+                v[4 * e + 2] = f.z;
+                v[4 * e + 3] = f.w;
+              }
+              store_block_nvfp4(g, m, n, v);
+            }
+          }
+        } else {
+          for (int lr = wave; lr < 128; lr += kPrefillThreads / 64) {
+            const int m = m0 + 128 * p + lr;
+            if (m >= g.M) break;
+            for (int n = c0 + lane; n < c1; n += 64) store_gate(g, m, n, out[lr * kQPitch + (n - n0)]);
+          }
+        }
+        if (p + 1 < kQPasses) __syncthreads();
+      }
+    }
+    if constexpr (EPI == kEpiNvfp4) return;
   }
   if (!g.y_bf16) {
     // fp32: each store instruction covers 128 contiguous bytes of two rows; store directly.
@@ -490,17 +537,17 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
 // compute 128 x 128 tiles over columns [n_split, N).  Peeling the last tile columns into
 // small tiles keeps the final dispatch round from running a few large tiles on a mostly
 // idle GPU.
-template <bool QOUT>
+template <int EPI>
 __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(GemmArgs g, int n_split, int tiles_big) {
   extern __shared__ __align__(16) uint8_t lds[];
   if ((int)blockIdx.x < tiles_big) {
     int tm, tn;
     tile_coords(blockIdx.x, (g.M + 255) / 256, (n_split + 255) / 256, tm, tn);
-    prefill_tile<256, QOUT>(g, lds, tm * 256, tn * 256);
+    prefill_tile<256, EPI>(g, lds, tm * 256, tn * 256);
   } else {
     int tm, tn;
     tile_coords(blockIdx.x - tiles_big, (g.M + 127) / 128, (g.N - n_split + 127) / 128, tm, tn);
-    prefill_tile<128, QOUT>(g, lds, tm * 128, n_split + tn * 128);
+    prefill_tile<128, EPI>(g, lds, tm * 128, n_split + tn * 128);
   }
 }
 
@@ -592,8 +639,10 @@ __device__ __forceinline__ void decode_chunk_mma(const DecodeChunk& d, f32x4_t& 
 // Epilogue of the decode kernels: the 4 wavefronts' 16x16 tiles (red[(wave * 2 + group) * 64 +
 // lane]) are summed in a fixed order, scaled (y = (sum * s_gA[m]) * s_gW[seg(n)]) and stored; for
 // NVFP4 output the scaled values of the 16 x 32 tile go through qy (16 x 32 floats of LDS) and
-// each of the first 32 threads encodes one 16-column block.
+// each of the first 32 threads encodes one 16-column block.  GATES: gate columns also get
+// their gates from the same fp32 value.
 constexpr int kDecodeRowsE = 32;
+template <bool GATES>
 __device__ __forceinline__ void decode_epilogue(const GemmArgs& g, const f32x4_t* red, float* qy, int wave, int lane,
                                                 int n0) {
   const int rr = lane & 15, grp = lane >> 4;
@@ -612,6 +661,9 @@ __device__ __forceinline__ void decode_epilogue(const GemmArgs& g, const f32x4_t
         qy[m * kDecodeRowsE + 16 * wave + rr] = v;
       else if (m < g.M && n < g.N)
         store_out(g, m, n, v);
+      if constexpr (GATES) {
+        if (m < g.M && n < g.N && n >= g.gate_n0) store_gate(g, m, n, v);
+      }
     }
   }
   if (g.q_out) {
@@ -641,6 +693,7 @@ constexpr int kDecodeWaves = kDecodeThreads / 64;
 constexpr int kDecodeRows = 32;             // W rows per workgroup: two 16-row MFMA groups
 constexpr int kDecodeDepth = 4;             // 256-wide stages in flight per lane
 
+template <bool GATES>
 __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(GemmArgs g) {
   __shared__ f32x4_t red[kDecodeWaves * 2 * 64];
   __shared__ float qy[16 * kDecodeRows];
@@ -712,7 +765,7 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(GemmArgs g)
   }
   red[(wave * 2 + 0) * 64 + lane] = acc0;
   red[(wave * 2 + 1) * 64 + lane] = acc1;
-  decode_epilogue(g, red, qy, wave, lane, n0);
+  decode_epilogue<GATES>(g, red, qy, wave, lane, n0);
 }
 
 // M <= 16 tokens, K a multiple of 256: the same work as gemm_decode_kernel, but every load
@@ -743,6 +796,7 @@ __device__ __forceinline__ void dl_copy_chunk(const uint8_t* base, uint32_t row_
   copy16_to_lds(base, row_off + col + p * 16, dst);
 }
 
+template <bool GATES>
 __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(GemmArgs g) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -819,7 +873,7 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(GemmArg
   f32x4_t* red = reinterpret_cast<f32x4_t*>(lds + kDlRedOffset);
   red[(wave * 2 + 0) * 64 + lane] = acc0;
   red[(wave * 2 + 1) * 64 + lane] = acc1;
-  decode_epilogue(g, red, reinterpret_cast<float*>(lds), wave, lane, n0);
+  decode_epilogue<GATES>(g, red, reinterpret_cast<float*>(lds), wave, lane, n0);
 }
 
 // ------------------------------------------------------------------ plain kernel
@@ -845,7 +899,9 @@ __global__ __launch_bounds__(256) void gemm_plain_kernel(GemmArgs g) {
       acc = __builtin_fmaf(e2m1_value(ca >> 4) * sa, e2m1_value(cw >> 4) * sw, acc);
     }
   }
-  store_out(g, m, n, (acc * g.a_global[g.a_per_row ? m : 0]) * g.w_globals[segment_of(n, g.seg)]);
+  const float v = (acc * g.a_global[g.a_per_row ? m : 0]) * g.w_globals[segment_of(n, g.seg)];
+  store_out(g, m, n, v);
+  if (g.gate_h > 0 && n >= g.gate_n0) store_gate(g, m, n, v);
 }
 
 }  // namespace
@@ -860,11 +916,12 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
                 const float* a_global, int a_global_per_row, const uint8_t* w_codes, const uint8_t* w_scales,
                 const float* w_globals, const SegmentTable& seg, void* y, int y_dtype, int64_t ldy, void* workspace,
-                hipStream_t stream, const QuantOut* qout) {
+                hipStream_t stream, const QuantOut* qout, const GateOut* gates) {
   (void)workspace;
   if (M == 0 || N == 0) return NVFP4_OK;
   const bool plain = K % 128 != 0 || (M > 16 && (K % BK != 0 || K >= (1 << 24)));
   if (qout && (plain || N % 16 != 0)) return NVFP4_ERR_UNSUPPORTED;
+  if (qout && gates) return NVFP4_ERR_INVALID_ARG;
   GemmArgs g;
   g.M = (int32_t)M;
   g.N = (int32_t)N;
@@ -885,6 +942,13 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
   g.q_global = qout ? qout->global : nullptr;
   g.q_codes = qout ? qout->codes : nullptr;
   g.q_scales = qout ? qout->scales : nullptr;
+  g.gate_n0 = gates ? gates->n0 : (int32_t)N;
+  g.gate_h = gates ? gates->h : 0;
+  g.gate_a_log = gates ? gates->a_log : nullptr;
+  g.gate_dt_bias = gates ? gates->dt_bias : nullptr;
+  g.gate_g = gates ? gates->g : nullptr;
+  g.gate_beta = gates ? gates->beta : nullptr;
+  const bool gated = gates != nullptr;
   if (plain) {
     const int64_t total = M * N;
     gemm_plain_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(g);
@@ -893,14 +957,24 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return NVFP4_ERR_HIP;
     if (!dl_attr[dev]) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_decode_lds_kernel),
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_decode_lds_kernel<false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kDlLds) != hipSuccess ||
+          hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_decode_lds_kernel<true>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, kDlLds) != hipSuccess)
         return NVFP4_ERR_HIP;
       dl_attr[dev] = true;
     }
-    gemm_decode_lds_kernel<<<(unsigned)((N + kDecodeRows - 1) / kDecodeRows), kDecodeThreads, kDlLds, stream>>>(g);
+    const unsigned grid = (unsigned)((N + kDecodeRows - 1) / kDecodeRows);
+    if (gated)
+      gemm_decode_lds_kernel<true><<<grid, kDecodeThreads, kDlLds, stream>>>(g);
+    else
+      gemm_decode_lds_kernel<false><<<grid, kDecodeThreads, kDlLds, stream>>>(g);
   } else if (M <= 16) {
-    gemm_decode_kernel<<<(unsigned)((N + kDecodeRows - 1) / kDecodeRows), kDecodeThreads, 0, stream>>>(g);
+    const unsigned grid = (unsigned)((N + kDecodeRows - 1) / kDecodeRows);
+    if (gated)
+      gemm_decode_kernel<true><<<grid, kDecodeThreads, 0, stream>>>(g);
+    else
+      gemm_decode_kernel<false><<<grid, kDecodeThreads, 0, stream>>>(g);
   } else {
     // The 146 KB of dynamic LDS exceed the default limit; raise it once per device.
     static bool attr_set[64] = {};
@@ -908,9 +982,11 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return NVFP4_ERR_HIP;
     if (!attr_set[dev]) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_prefill_kernel<false>),
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_prefill_kernel<kEpiStore>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, kPrefillLds) != hipSuccess ||
-          hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_prefill_kernel<true>),
+          hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_prefill_kernel<kEpiNvfp4>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kPrefillLds) != hipSuccess ||
+          hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_prefill_kernel<kEpiGates>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, kPrefillLds) != hipSuccess)
         return NVFP4_ERR_HIP;
       if (hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -929,12 +1005,13 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
     }
     const int64_t big = tm * ((n_split + 255) / 256);
     const int64_t small = peel ? ((M + 127) / 128) * ((N - n_split + 127) / 128) : 0;
+    const unsigned grid = (unsigned)(big + small);
     if (g.q_out)
-      gemm_prefill_kernel<true><<<(unsigned)(big + small), kPrefillThreads, kPrefillLds, stream>>>(g, (int)n_split,
-                                                                                               (int)big);
+      gemm_prefill_kernel<kEpiNvfp4><<<grid, kPrefillThreads, kPrefillLds, stream>>>(g, (int)n_split, (int)big);
+    else if (gated)
+      gemm_prefill_kernel<kEpiGates><<<grid, kPrefillThreads, kPrefillLds, stream>>>(g, (int)n_split, (int)big);
     else
-      gemm_prefill_kernel<false><<<(unsigned)(big + small), kPrefillThreads, kPrefillLds, stream>>>(g, (int)n_split,
-                                                                                                (int)big);
+      gemm_prefill_kernel<kEpiStore><<<grid, kPrefillThreads, kPrefillLds, stream>>>(g, (int)n_split, (int)big);
   }
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }

@@ -55,13 +55,27 @@ struct QuantOut {
   uint8_t* scales;
 };
 
+// Gated DeltaNet gates computed from the GEMM's fp32 output in the same launch: columns
+// [n0, n0 + h) are the write-strength projection (beta = sigmoid(y)), columns [n0 + h, N) the
+// decay projection (g = -exp(a_log[j]) * softplus(y + dt_bias[j]) for head j); g and beta are
+// [M, h] fp32, row-major and contiguous; n0 + 2h == N.
+struct GateOut {
+  int32_t n0;
+  int32_t h;
+  const float* a_log;
+  const float* dt_bias;
+  float* g;
+  float* beta;
+};
+
 // With qout set, y is unused and the result is written as NVFP4 instead; then N % 16 == 0 and
-// the shape must be one the MFMA kernels take (NVFP4_ERR_UNSUPPORTED otherwise).
+// the shape must be one the MFMA kernels take (NVFP4_ERR_UNSUPPORTED otherwise).  With gates
+// set, y is written as usual and the gates as well; qout and gates are not combined.
 int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
                 const float* a_global, int a_global_per_row, const uint8_t* w_codes,
                 const uint8_t* w_scales, const float* w_globals, const SegmentTable& seg,
                 void* y, int y_dtype, int64_t ldy, void* workspace, hipStream_t stream,
-                const QuantOut* qout = nullptr);
+                const QuantOut* qout = nullptr, const GateOut* gates = nullptr);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 // FP8 KV-cache codec launchers (kv_fp8.hip).

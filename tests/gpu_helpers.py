@@ -75,3 +75,35 @@ def assert_gemm_close(y: torch.Tensor, Y: np.ndarray, T: np.ndarray, what: str =
     assert bad.size == 0, (f"{what}: {len(bad)} elements out of tolerance, first {bad[:3].tolist()}, "
                            f"max err/T {worst:.3g}")
     return worst
+
+
+def gate_bounds(Y: np.ndarray, T: np.ndarray, H: int, a_log, dt_bias, g_o: np.ndarray, beta_o: np.ndarray):
+    """Allowed |error| of the kernel's (g, beta) against the oracle's, derived from the
+    arithmetic: the kernel's fp32 pre-activation y is within e = 1e-4 * T of the exact one (the
+    GEMM bound), which moves each gate by at most the function's largest slope on [y - e, y + e]
+    times e (for the decay, plus the fp32 rounding of z = y + dt_bias); the fp32 evaluation of
+    exp, log1p, the division and the products adds a few ulps (2e-6 relative); results below
+    the fp32 normal range (2^-126) are absolute."""
+    N = Y.shape[1]
+    yb, ya = Y[:, N - 2 * H:N - H], Y[:, N - H:]
+    eb, ea = 1e-4 * T[:, N - 2 * H:N - H], 1e-4 * T[:, N - H:]
+    near0 = np.where(np.abs(yb) <= eb, 0.0, np.abs(yb) - eb)     # the point nearest 0
+    slope = ref.sigmoid(near0) * ref.sigmoid(-near0)               # s (1 - s), without cancellation
+    bound_beta = slope * eb + 2e-6 * np.abs(beta_o) + 2.0 ** -126
+    al = np.asarray(a_log, np.float32).astype(np.float64)[None, :]
+    z = ya + np.asarray(dt_bias, np.float32).astype(np.float64)[None, :]
+    ez = ea + 2.0 ** -23 * np.abs(z)
+    bound_g = np.exp(al) * ref.sigmoid(z + ez) * ez + 2e-6 * np.abs(g_o) + np.exp(al) * 2.0 ** -126
+    return bound_g, bound_beta
+
+
+def assert_gates_close(g: torch.Tensor, beta: torch.Tensor, Y: np.ndarray, T: np.ndarray, H: int, a_log, dt_bias,
+                       g_o: np.ndarray, beta_o: np.ndarray, what: str = "") -> None:
+    bg, bb = gate_bounds(Y, T, H, a_log, dt_bias, g_o, beta_o)
+    gh = g.cpu().numpy().astype(np.float64)
+    bh = beta.cpu().numpy().astype(np.float64)
+    for name, got, want, bound in (("g", gh, g_o, bg), ("beta", bh, beta_o, bb)):
+        err = np.abs(got - want)
+        bad = np.argwhere(~(err <= bound))
+        assert bad.size == 0, (f"{what} {name}: {len(bad)} out of tolerance, first {bad[:3].tolist()} "
+                               f"got {got[tuple(bad[0])]} want {want[tuple(bad[0])]}")

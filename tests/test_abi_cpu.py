@@ -177,3 +177,21 @@ def test_fp8_kv_argument_errors(nv):
     assert d(A16, 16, A16, A16 + 8, 1, None) == 1          # y must be 16-byte aligned
     assert d(A16, 16, A16, A16, 5, None) == 1
     assert q(None, 1, 0, None, None, None) == 0 and d(None, 0, None, None, 0, None) == 0
+
+
+def test_gdn_gates_argument_errors(nv):
+    f = nv.lib.nvfp4_gemm_fused_gdn_gates
+    w3 = (ctypes.c_int64 * 3)(64, 48, 48)
+    w_uneq = (ctypes.c_int64 * 3)(64, 48, 32)
+    w1 = (ctypes.c_int64 * 1)(48)
+
+    def call(M=32, K=256, widths=w3, n=3, al=A16, dt=A16, gg=A16, beta=A16, y=A16):
+        return f(M, K, A16, A16, A16, 0, n, ctypes.cast(widths, ctypes.c_void_p), A16, A16, A16, y, 1, 160,
+                 al, dt, gg, beta, None, 0, None)
+
+    assert call(widths=w_uneq) == 1                # the two gate segments differ in width
+    assert call(widths=w1, n=1) == 1               # fewer than two segments
+    assert call(al=None) == 1 and call(dt=None) == 1 and call(gg=None) == 1 and call(beta=None) == 1
+    assert call(gg=A16 + 2) == 1 and call(beta=A16 + 1) == 1 and call(al=A16 + 2) == 1
+    assert call(y=None) == 1
+    assert call(M=0) == 0                          # empty product: a no-op
