@@ -91,15 +91,22 @@ __device__ __forceinline__ void store_out(const GemmArgs& g, int m, int n, float
 // of the write strength, beta = 1 / (1 + e^-y); column gate_n0 + gate_h + j is head j of the
 // decay, g = -e^A_log[j] * softplus(y + dt_bias[j]) with softplus(z) = max(z, 0) + ln(1 + e^-|z|),
 // which overflows nowhere.
+__device__ __forceinline__ float gate_write_strength(float y) { return 1.0f / (1.0f + expf(-y)); }
+
+// e_alog = e^A_log[j] of the head, dt = dt_bias[j].
+__device__ __forceinline__ float gate_log_decay(float y, float e_alog, float dt) {
+  const float z = y + dt;
+  const float sp = fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)));
+  return -e_alog * sp;
+}
+
 __device__ __forceinline__ void store_gate(const GemmArgs& g, int m, int n, float y) {
   const int c = n - g.gate_n0;
   if (c < g.gate_h) {
-    g.gate_beta[(int64_t)m * g.gate_h + c] = 1.0f / (1.0f + expf(-y));
+    g.gate_beta[(int64_t)m * g.gate_h + c] = gate_write_strength(y);
   } else {
     const int j = c - g.gate_h;
-    const float z = y + g.gate_dt_bias[j];
-    const float sp = fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)));
-    g.gate_g[(int64_t)m * g.gate_h + j] = -expf(g.gate_a_log[j]) * sp;
+    g.gate_g[(int64_t)m * g.gate_h + j] = gate_log_decay(y, expf(g.gate_a_log[j]), g.gate_dt_bias[j]);
   }
 }
 
@@ -441,10 +448,23 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
             }
           }
         } else {
-          for (int lr = wave; lr < 128; lr += kPrefillThreads / 64) {
-            const int m = m0 + 128 * p + lr;
-            if (m >= g.M) break;
-            for (int n = c0 + lane; n < c1; n += 64) store_gate(g, m, n, out[lr * kQPitch + (n - n0)]);
+          // One gate segment at a time, so that a wavefront evaluates one function; a lane
+          // keeps its column's head parameters in registers across the rows.
+          for (int sg = 0; sg < 2; ++sg) {
+            const int sb = g.gate_n0 + sg * g.gate_h;
+            const int hi = min(c1, sb + g.gate_h);
+            for (int n = max(c0, sb) + lane; n < hi; n += 64) {
+              const int j = n - sb;
+              const float e_alog = sg ? expf(g.gate_a_log[j]) : 0.0f;
+              const float dt = sg ? g.gate_dt_bias[j] : 0.0f;
+              float* dst = (sg ? g.gate_g : g.gate_beta) + j;
+              for (int lr = wave; lr < 128; lr += kPrefillThreads / 64) {
+                const int m = m0 + 128 * p + lr;
+                if (m >= g.M) break;
+                const float y = out[lr * kQPitch + (n - n0)];
+                dst[(int64_t)m * g.gate_h] = sg ? gate_log_decay(y, e_alog, dt) : gate_write_strength(y);
+              }
+            }
           }
         }
         if (p + 1 < kQPasses) __syncthreads();
