@@ -66,6 +66,21 @@ parameterized in log space through softplus and exponential):
       DeltaNet / Mamba-2 gate parameterization that matches their description.)
   R14 The gates take the GEMM's float32 output value y (global scales applied, R8 and the
       fused-segment repair) before any output rounding; g and beta are float32.
+
+Lossy NVFP4 -> MXFP4 re-encoding (the pages' format is NVFP4 only -- "NVFP4 W4A4
+Quantization Compresses 27B Hybrid Models", "Challenging the Recurrence Fragility
+Assumption"; MXFP4 is the OCP Microscaling (MX) v1.0 format that gfx950's scaled FP4 matrix
+instructions take; its definition here follows that published specification):
+  R15 MXFP4: E2M1 codes (R1, packed as R7) with one E8M0 scale byte per 32 consecutive
+      elements of a row (value 2^(byte - 127); 0xFF is NaN and never produced); the NVFP4
+      tensor's float32 global scale is carried over unchanged and stays a multiplier.
+  R16 A 32-element block (two NVFP4 blocks) is re-encoded from its exact NVFP4 values
+      v = E2M1 * E4M3 (global scale left out): shared exponent e = floor(log2(max|v|)) - 2
+      (2 = exponent of E2M1's largest power of two), scale 2^e, element magnitude
+      E2M1_RNE_SAT(|v| / 2^e) (R6: ties to even, saturating at 6), the sign bit copied from
+      the NVFP4 code.  A block of zeros gets scale byte 0 and magnitude 0.
+  R17 The MXFP4 GEMM is the same contraction as R8's with the MXFP4 values
+      E2M1 * 2^(byte - 127) * s_g.
 """
 from __future__ import annotations
 
@@ -349,3 +364,73 @@ def fused_gdn_gates(a: NVFP4, segments: list[NVFP4], a_log, dt_bias, a_rows=None
     N = Y.shape[1]
     g, beta = gdn_gates(Y[:, N - 2 * H:N - H], Y[:, N - H:], a_log, dt_bias)
     return Y, T, g, beta
+
+
+# ------------------------------------------------------------------------------ MXFP4 (lossy)
+
+MX_BLOCK = 32                      # elements per E8M0 scale (R15)
+E2M1_EMAX = 2                      # exponent of E2M1's largest power of two, 4 = 2^2 (R16)
+
+
+@dataclass
+class MXFP4:
+    """An MXFP4 tensor: codes [R, C/2] (as NVFP4), E8M0 scale bytes [R, C/32], float32
+    global scale of shape (1,) or (R,) carried over from the NVFP4 tensor."""
+    codes: np.ndarray
+    scales: np.ndarray
+    global_scale: np.ndarray
+    rows: int
+    cols: int
+
+    def global_per_row(self) -> np.ndarray:
+        g = np.asarray(self.global_scale, dtype=F32).reshape(-1)
+        return np.broadcast_to(g if g.size == self.rows else g[:1], (self.rows,))
+
+
+def e8m0_decode(b) -> np.ndarray:
+    """2^(byte - 127) as float64; 0xFF is NaN (R15)."""
+    b = np.asarray(b).astype(np.int64)
+    return np.where(b == 0xFF, np.nan, np.exp2((b - 127).astype(F64)))
+
+
+def mxfp4_from_nvfp4(t: NVFP4) -> MXFP4:
+    """R16: re-encode each 32-element block of an NVFP4 tensor to MXFP4 (lossy)."""
+    if t.cols % MX_BLOCK:
+        raise ValueError("cols must be a multiple of 32")
+    R, C = t.rows, t.cols
+    code = unpack_codes(t.codes)
+    v = e2m1_decode(code) * np.repeat(e4m3_decode(t.scales), BLOCK, axis=1)   # exact
+    blocks = np.abs(v).reshape(R, C // MX_BLOCK, MX_BLOCK)
+    amax = blocks.max(axis=2) if C else np.zeros((R, 0))
+    # floor(log2(amax)) from the binary exponent: amax = m * 2^ex with 0.5 <= m < 1.
+    _, ex = np.frexp(amax)
+    shared = ex.astype(np.int64) - 1 - E2M1_EMAX
+    zero = amax == 0
+    shared = np.where(zero, -127, shared)
+    q = blocks / np.exp2(shared.astype(F64))[:, :, None]                    # exact (power of 2)
+    mag = e2m1_rne_sat(q).reshape(R, C)
+    mag = np.where(np.repeat(zero, MX_BLOCK, axis=1), 0, mag)
+    sign = (code >> 3) & 1
+    out = ((sign << 3) | mag).astype(np.uint8)
+    scales = (shared + 127).astype(np.uint8)
+    return MXFP4(pack_codes(out), scales, np.asarray(t.global_scale, F32).copy(), R, C)
+
+
+def mx_dequantize(t: MXFP4, rows=None) -> np.ndarray:
+    """R17: float64 values E2M1(code) * 2^(byte - 127) * s_g (exact)."""
+    codes, scales, g = t.codes, t.scales, t.global_per_row()
+    if rows is not None:
+        rows = np.asarray(rows)
+        codes, scales, g = codes[rows], scales[rows], g[rows]
+    v = e2m1_decode(unpack_codes(codes))
+    s = np.repeat(e8m0_decode(scales), MX_BLOCK, axis=1)
+    return v * s * g.astype(F64)[:, None]
+
+
+def mx_gemm(a: MXFP4, w: MXFP4, a_rows=None):
+    """Y = A^ . W^T in float64 for MXFP4 operands, and T = |A^| . |W^|^T (R17)."""
+    if a.cols != w.cols:
+        raise ValueError("K mismatch")
+    A = mx_dequantize(a, a_rows)
+    W = mx_dequantize(w)
+    return A @ W.T, np.abs(A) @ np.abs(W).T
