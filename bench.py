@@ -384,6 +384,49 @@ def bench_gdn_gates(nv, steps: int, warmup: int, settle_s: float = 0.0):
     return out
 
 
+MFMA_FP4_PEAK_TFLOPS = 10100.0   # MI355X dense FP4 / FP6
+
+
+def bench_mxfp4(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: int = 8):
+    """The lossy MXFP4 variant at the prefill shape: per step, the NVFP4 quantize of X, its
+    re-encoding to MXFP4 and the scaled-FP4 MFMA GEMM (W re-encoded offline), beside the NVFP4
+    GEMM; and the variant's error against the NVFP4 GEMM's output."""
+    p = workloads.PREFILL
+    dev = torch.device("cuda:0")
+    xs = [torch.from_numpy(p.x()).to(dev).to(torch.bfloat16)]
+    for i in range(1, rotate):
+        xs.append(torch.roll(xs[0], shifts=i, dims=0))
+    w = nv.quantize(torch.from_numpy(p.w()).to(dev).to(torch.bfloat16))
+    wm = nv.to_mxfp4(w)
+    a = nv.quantize(xs[0])
+    am = nv.to_mxfp4(a)
+    y = torch.empty((p.M, p.N), dtype=torch.bfloat16, device=dev)
+    out = {}
+    out["mx_gemm_ms"] = _mean_ms(lambda i: nv.mxfp4_gemm(am, wm.codes, wm.scales, (p.N,), wm.global_scale,
+                                                          torch.bfloat16, out=y), steps, warmup, settle_s)
+    out["nvfp4_gemm_ms"] = _mean_ms(lambda i: nv.gemm(a, w, torch.bfloat16, out=y), steps, warmup, settle_s)
+    out["reencode_a_us"] = 1e3 * _mean_ms(lambda i: nv.to_mxfp4(a, out=am), steps, warmup, 0.0)
+
+    def step(i):
+        nv.quantize(xs[i % rotate], out=a)
+        nv.to_mxfp4(a, out=am)
+        nv.mxfp4_gemm(am, wm.codes, wm.scales, (p.N,), wm.global_scale, torch.bfloat16, out=y)
+
+    out["step_ms"] = _mean_ms(step, steps, warmup, settle_s)
+    for k in ("mx_gemm", "nvfp4_gemm"):
+        out[k + "_tflops"] = p.flops / (out[k + "_ms"] * 1e-3) / 1e12
+    out["mx_gemm_frac_fp4_peak"] = out["mx_gemm_tflops"] / MFMA_FP4_PEAK_TFLOPS
+    out["step_tflops"] = p.flops / (out["step_ms"] * 1e-3) / 1e12
+    # Error of the variant against the NVFP4 GEMM (whose output matches the exact product to
+    # 1e-4 of sum |a w|), both in fp32 on the same quantized X.
+    a = nv.quantize(xs[0])
+    ymx = nv.mxfp4_gemm(nv.to_mxfp4(a), wm.codes, wm.scales, (p.N,), wm.global_scale, torch.float32)
+    ynv = nv.gemm(a, w, torch.float32)
+    out["rel_rms_error_vs_nvfp4"] = _rel_rms(ymx, ynv)
+    out["reencode_bytes_per_element"] = 0.5 + 1 / 16 + 0.5 + 1 / 32
+    return out
+
+
 def bench_kv_fp8(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: int = 6):
     """FP8 KV-cache codec on a K (or V) cache of 32768 tokens x 8 heads x 128 dims in bf16
     (64 MiB), rotating copies (6 x 64 MiB > the 256 MB MALL); scale calibrated as max|K| / 448.
@@ -423,7 +466,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--settle-s", type=float, default=1.0,
                     help="seconds of untimed steps before the warmup steps, for steady clocks")
-    ap.add_argument("--workload", choices=["prefill", "decode", "fused", "nvfp4_out", "kv_fp8", "gdn_gates"],
+    ap.add_argument("--workload", choices=["prefill", "decode", "fused", "nvfp4_out", "kv_fp8", "gdn_gates", "mxfp4"],
                     default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=TRAFFIC_JSON,
@@ -449,6 +492,9 @@ def main() -> int:
         return 0
     if args.workload == "kv_fp8":
         print(json.dumps({"workload": "kv_fp8", "results": bench_kv_fp8(nv, args.steps, args.warmup, args.settle_s)}))
+        return 0
+    if args.workload == "mxfp4":
+        print(json.dumps({"workload": "mxfp4", "results": bench_mxfp4(nv, args.steps, args.warmup, args.settle_s)}))
         return 0
     if args.workload == "gdn_gates":
         print(json.dumps({"workload": "gdn_gates", "results": bench_gdn_gates(nv, args.steps, args.warmup,

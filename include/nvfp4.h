@@ -12,7 +12,9 @@
  *   4. the GEMM whose output leaves already quantized to NVFP4 for the next linear layer;
  *   5. the FP8 (E4M3) key-value cache codec with calibrated per-tensor scales;
  *   6. the fused Gated DeltaNet input projection whose two gate segments leave as the
- *      write strength and the log-space decay, in the same launch.
+ *      write strength and the log-space decay, in the same launch;
+ *   7. a lossy variant: NVFP4 re-encoded to MXFP4 and multiplied with gfx950's native scaled
+ *      FP4 matrix instructions.
  *
  * Sources: the element format (E2M1 values, one E4M3 scale per 16-element block) is from
  * "NVFP4 W4A4 Quantization Compresses 27B Hybrid Models" (thevalue.engineering), section
@@ -193,6 +195,46 @@ int nvfp4_gemm_fused_gdn_gates(int64_t M, int64_t K,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/*
+ * Lossy re-encoding of an NVFP4 tensor to MXFP4, the block-scaled 4-bit format that gfx950's
+ * scaled FP4 matrix instructions take: E2M1 codes with one E8M0 scale (a power of two,
+ * 2^(byte - 127)) per 32 consecutive elements of a row (OCP Microscaling (MX) specification
+ * v1.0).  Each 32-element block (two NVFP4 blocks) is re-encoded from its exact NVFP4 values
+ * v = E2M1 * E4M3 (the NVFP4 element format: "NVFP4 W4A4 Quantization Compresses 27B Hybrid
+ * Models", "Challenging the Recurrence Fragility Assumption"), leaving the tensor's global
+ * scale aside (it stays the multiplier of the MXFP4 tensor, unchanged):
+ *   e = floor(log2(max |v|)) - 2 (the MX specification's shared exponent for E2M1),
+ *   mx_scales byte = e + 127,  magnitude = E2M1_RNE_SAT(|v| / 2^e),  sign bit kept;
+ *   a block of zeros gets byte 0 and magnitude 0.
+ * Lossy by design: the E4M3 mantissa of each block scale is dropped and both 16-element halves
+ * share one power-of-two scale.
+ *   cols > 0 and a multiple of 32; rows >= 0 (0 is a no-op).
+ *   codes     [rows, cols/2] NVFP4 codes, 16-byte aligned;  scales [rows, cols/16] E4M3, 2-byte aligned.
+ *   mx_codes  out [rows, cols/2], 16-byte aligned (may be codes itself: in place);
+ *   mx_scales out [rows, cols/32] E8M0 bytes.
+ */
+int nvfp4_to_mxfp4(int64_t rows, int64_t cols, const uint8_t* codes, const uint8_t* scales,
+                   uint8_t* mx_codes, uint8_t* mx_scales, void* stream);
+
+/*
+ * The (fused-module) GEMM on MXFP4 operands with the scaled FP4 MFMA (fp32 accumulation):
+ *   Y[m, n] = (sum_k E2M1(a_mk) 2^(sa_m,k/32 - 127) E2M1(w_nk) 2^(sw_n,k/32 - 127))
+ *             * a_global[m or 0] * w_globals[seg(n)],
+ * stored as fp32 or bf16 (round to nearest even).  Operands as nvfp4_to_mxfp4 writes them;
+ * the global scales are the NVFP4 tensors' own.  With the operands re-encoded from NVFP4 this
+ * is a lossy variant of nvfp4_gemm_fused_segments.
+ *   K a multiple of 256 below 2^24 (other K: NVFP4_ERR_UNSUPPORTED); any M >= 0 (tuned for
+ *   M > 16).  a_scales [M, K/32], w_scales [N, K/32], 16-byte aligned.
+ *   Other arguments as in nvfp4_gemm_fused_segments (one segment: a plain GEMM).
+ */
+int nvfp4_mxfp4_gemm(int64_t M, int64_t K,
+                     const uint8_t* a_codes, const uint8_t* a_scales,
+                     const float* a_global, int a_global_per_row,
+                     int num_segments, const int64_t* seg_n,
+                     const uint8_t* w_codes, const uint8_t* w_scales,
+                     const float* w_globals,
+                     void* y, int y_dtype, int64_t ldy, void* stream);
 
 /*
  * FP8 key-value cache codec with a calibrated per-tensor scale (the pages' second serving

@@ -18,6 +18,9 @@ Entry points (same names as the C ABI):
                                          -> (Y, g, beta): fused GDN input projection whose
                                             last two segments leave as log decay and
                                             write strength
+  to_mxfp4(a) / mxfp4_gemm(a_mx, w_codes, w_scales, widths, w_globals, out_dtype)
+                                         -> lossy MXFP4 re-encoding and the GEMM on gfx950's
+                                            scaled FP4 MFMA
 """
 from __future__ import annotations
 
@@ -29,7 +32,7 @@ from typing import Sequence
 import torch
 
 __all__ = [
-    "NVFP4Tensor", "NVFP4Error", "quantize", "gemm", "gemm_fused_segments", "gemm_nvfp4_out", "gemm_fused_gdn_gates",
+    "NVFP4Tensor", "NVFP4Error", "quantize", "gemm", "gemm_fused_segments", "gemm_nvfp4_out", "gemm_fused_gdn_gates", "MXFP4Tensor", "to_mxfp4", "mxfp4_gemm",
     "fp8_kv_quantize", "fp8_kv_dequantize",
     "library_path", "lib",
     "PER_TENSOR", "PER_ROW", "GIVEN", "MAX_SEGMENTS", "EXPORTED_SYMBOLS",
@@ -44,7 +47,8 @@ _F32, _BF16 = 0, 1
 MAX_SEGMENTS = 64
 EXPORTED_SYMBOLS = (
     "nvfp4_quantize", "nvfp4_quantize_workspace_size", "nvfp4_gemm", "nvfp4_gemm_fused_segments",
-    "nvfp4_gemm_nvfp4_out", "nvfp4_gemm_fused_gdn_gates", "nvfp4_gemm_workspace_size", "nvfp4_fp8_kv_quantize", "nvfp4_fp8_kv_dequantize",
+    "nvfp4_gemm_nvfp4_out", "nvfp4_gemm_fused_gdn_gates", "nvfp4_to_mxfp4", "nvfp4_mxfp4_gemm",
+    "nvfp4_gemm_workspace_size", "nvfp4_fp8_kv_quantize", "nvfp4_fp8_kv_dequantize",
     "nvfp4_status_string", "nvfp4_version",
 )
 
@@ -71,6 +75,10 @@ def _load() -> ctypes.CDLL:
     L.nvfp4_gemm_fused_gdn_gates.argtypes = [i64, i64, p, p, p, i32, i32, p, p, p, p, p, i32, i64, p, p, p, p,
                                              p, sz, p]
     L.nvfp4_gemm_fused_gdn_gates.restype = i32
+    L.nvfp4_to_mxfp4.argtypes = [i64, i64, p, p, p, p, p]
+    L.nvfp4_to_mxfp4.restype = i32
+    L.nvfp4_mxfp4_gemm.argtypes = [i64, i64, p, p, p, i32, i32, p, p, p, p, p, i32, i64, p]
+    L.nvfp4_mxfp4_gemm.restype = i32
     L.nvfp4_fp8_kv_quantize.argtypes = [p, i32, i64, p, p, p]
     L.nvfp4_fp8_kv_quantize.restype = i32
     L.nvfp4_fp8_kv_dequantize.argtypes = [p, i64, p, p, i32, p]
@@ -274,6 +282,58 @@ def gemm_fused_gdn_gates(a: NVFP4Tensor, w_codes: torch.Tensor, w_scales: torch.
                                         _ptr(beta), _ptr(ws), ws_bytes, _stream(dev))
     _check(st, "nvfp4_gemm_fused_gdn_gates")
     return y, g, beta
+
+
+@dataclass
+class MXFP4Tensor:
+    """codes uint8 [rows, cols/2] (E2M1, as NVFP4), scales uint8 [rows, cols/32] (E8M0),
+    global_scale float32 [1] or [rows] (the NVFP4 tensor's), all on one GPU."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    global_scale: torch.Tensor
+
+    @property
+    def rows(self) -> int:
+        return self.codes.shape[0]
+
+    @property
+    def cols(self) -> int:
+        return self.codes.shape[1] * 2
+
+
+def to_mxfp4(t: NVFP4Tensor, out: MXFP4Tensor | None = None) -> MXFP4Tensor:
+    """Lossy re-encoding of an NVFP4 tensor to MXFP4 (E8M0 scale per 32 elements); the global
+    scale tensor is shared with the input."""
+    R, C = t.rows, t.cols
+    _require(C % 32 == 0, "cols must be a multiple of 32")
+    _require(t.codes.is_contiguous() and t.scales.is_contiguous(), "contiguous NVFP4 tensor")
+    dev = t.codes.device
+    if out is None:
+        out = MXFP4Tensor(torch.empty((R, C // 2), dtype=torch.uint8, device=dev),
+                          torch.empty((R, C // 32), dtype=torch.uint8, device=dev), t.global_scale)
+    _require(out.codes.shape == (R, C // 2) and out.scales.shape == (R, C // 32), "bad out tensor")
+    st = lib.nvfp4_to_mxfp4(R, C, _ptr(t.codes), _ptr(t.scales), _ptr(out.codes), _ptr(out.scales), _stream(dev))
+    _check(st, "nvfp4_to_mxfp4")
+    return out
+
+
+def mxfp4_gemm(a: MXFP4Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, seg_widths: Sequence[int],
+               w_globals: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """(Fused-module) GEMM on MXFP4 operands with the scaled FP4 MFMA: W = concatenation of the
+    segments' MXFP4 codes [N, K/2] and E8M0 scales [N, K/32], one global scale per segment."""
+    M, K = a.rows, a.cols
+    N = int(sum(seg_widths))
+    _require(w_codes.shape == (N, K // 2) and w_scales.shape == (N, K // 32), "bad MXFP4 weight shapes")
+    dev = a.codes.device
+    y = _out_tensor(M, N, out_dtype, dev, out)
+    per_row = int(a.global_scale.numel() == M and M != 1)
+    widths = (ctypes.c_int64 * len(seg_widths))(*[int(v) for v in seg_widths])
+    st = lib.nvfp4_mxfp4_gemm(M, K, _ptr(a.codes), _ptr(a.scales), _ptr(a.global_scale), per_row, len(seg_widths),
+                              ctypes.cast(widths, ctypes.c_void_p), _ptr(w_codes), _ptr(w_scales), _ptr(w_globals),
+                              _ptr(y), _y_dtype(out_dtype), y.stride(0) if M > 0 else N, _stream(dev))
+    _check(st, "nvfp4_mxfp4_gemm")
+    return y
 
 
 def fp8_kv_quantize(x: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:

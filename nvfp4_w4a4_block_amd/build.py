@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvfp4.so")
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "kv_fp8.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "kv_fp8.hip", "mxfp4.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -176,6 +176,33 @@ int nvfp4_gemm_fused_gdn_gates(int64_t M, int64_t K, const uint8_t* a_codes, con
                      y, y_dtype, ldy, workspace, static_cast<hipStream_t>(stream), nullptr, &gates);
 }
 
+int nvfp4_to_mxfp4(int64_t rows, int64_t cols, const uint8_t* codes, const uint8_t* scales, uint8_t* mx_codes,
+                   uint8_t* mx_scales, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 32 != 0) return NVFP4_ERR_INVALID_ARG;
+  if (rows == 0) return NVFP4_OK;
+  if (!codes || !scales || !mx_codes || !mx_scales || !aligned(codes, 16) || !aligned(mx_codes, 16) ||
+      !aligned(scales, 2))
+    return NVFP4_ERR_INVALID_ARG;
+  return launch_mx_reencode(rows, cols, codes, scales, mx_codes, mx_scales, static_cast<hipStream_t>(stream));
+}
+
+int nvfp4_mxfp4_gemm(int64_t M, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                     int a_global_per_row, int num_segments, const int64_t* seg_n, const uint8_t* w_codes,
+                     const uint8_t* w_scales, const float* w_globals, void* y, int y_dtype, int64_t ldy,
+                     void* stream) {
+  SegmentTable seg;
+  int64_t N = 0;
+  int st = make_segments(num_segments, seg_n, seg, N);
+  if (st != NVFP4_OK) return st;
+  st = check_gemm_common(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales, y, y_dtype,
+                         ldy);
+  if (st != NVFP4_OK || M == 0) return st;
+  if (K % 32 != 0) return NVFP4_ERR_INVALID_ARG;
+  if (!w_globals || !aligned(w_globals, 4)) return NVFP4_ERR_INVALID_ARG;
+  return launch_mx_gemm(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales, w_globals, seg, y,
+                        y_dtype, ldy, static_cast<hipStream_t>(stream));
+}
+
 int nvfp4_fp8_kv_quantize(const void* x, int x_dtype, int64_t n, const float* scale, uint8_t* q, void* stream) {
   if (n < 0 || (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16)) return NVFP4_ERR_INVALID_ARG;
   if (n == 0) return NVFP4_OK;

@@ -158,12 +158,19 @@ __device__ __forceinline__ void copy16_to_lds(const uint8_t* base, uint32_t off,
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "s"(dst) : "memory");
 }
 
+// The same with 4 B per lane (lane l lands at lds_dst + 4 l: 256 B per wavefront).
+__device__ __forceinline__ void copy4_to_lds(const uint8_t* base, uint32_t off, const uint8_t* lds_dst) {
+  const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds_dst);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(off), "s"(base), "s"(dst) : "memory");
+}
+
 // Enqueue the copy of K step kt of both operands straight into LDS (no registers): each
 // wavefront-wide load writes 1 KB of consecutive LDS (8 rows of codes, or 64 rows of scales).
 // Rows past the end of A or W are clamped to the last row.  Addresses are a per-tile base in
 // scalar registers plus a 32-bit per-lane offset, row * row pitch + segment, with row < 256 and
-// the pitch < 2^23 (K < 2^24), so 24-bit multiplies serve.
-template <int T>
+// the pitch < 2^23 (K < 2^24), so 24-bit multiplies serve.  MX: the operands are MXFP4, whose
+// 8 E8M0 bytes per row per K step land in the scale area with a row pitch of 8 B (4 B per lane).
+template <int T, bool MX = false>
 __device__ __forceinline__ void load_stage_lds(const GemmArgs& g, int m0, int n0, int kt, uint8_t* stage) {
   using C = TileCfg<T>;
   const int lane = threadIdx.x & 63;
@@ -182,19 +189,33 @@ __device__ __forceinline__ void load_stage_lds(const GemmArgs& g, int m0, int n0
     copy16_to_lds(ac, __umul24(min(row, ra), kb) + seg, stage + chunk * 1024);
     copy16_to_lds(wc, __umul24(min(row, rw), kb) + seg, stage + C::kCodeTile + chunk * 1024);
   }
+  if constexpr (MX) {
+    const uint32_t kx = (uint32_t)g.K / 32;
+    const uint8_t* ax = g.a_scales + (size_t)m0 * kx + (size_t)kt * 8;
+    const uint8_t* wx = g.w_scales + (size_t)n0 * kx + (size_t)kt * 8;
 #pragma unroll
-  for (int j = 0; j < T / 256; ++j) {
-    const int chunk = j * 4 + wave;                  // 1 KB chunk = 64 rows x 16 B
-    const int row = chunk * 64 + lane;
-    copy16_to_lds(as, __umul24(min(row, ra), ks), stage + 2 * C::kCodeTile + chunk * 1024);
-    copy16_to_lds(ws, __umul24(min(row, rw), ks), stage + 2 * C::kCodeTile + C::kScaleTile + chunk * 1024);
-  }
-  if (T / 256 == 0) {   // 128-row tiles: 128 rows x 16 B = 2 KB per operand, half the waves each
-    const int row = (wave & 1) * 64 + lane;
-    if (wave < 2)
-      copy16_to_lds(as, __umul24(min(row, ra), ks), stage + 2 * C::kCodeTile + (wave & 1) * 1024);
-    else
-      copy16_to_lds(ws, __umul24(min(row, rw), ks), stage + 2 * C::kCodeTile + C::kScaleTile + (wave & 1) * 1024);
+    for (int j = 0; j < T / 128; ++j) {
+      const int chunk = j * 4 + wave;                // 256 B chunk = 32 rows x 8 B
+      const int row = chunk * 32 + (lane >> 1);
+      const uint32_t half = (uint32_t)(lane & 1) * 4;
+      copy4_to_lds(ax, __umul24(min(row, ra), kx) + half, stage + 2 * C::kCodeTile + chunk * 256);
+      copy4_to_lds(wx, __umul24(min(row, rw), kx) + half, stage + 2 * C::kCodeTile + C::kScaleTile + chunk * 256);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < T / 256; ++j) {
+      const int chunk = j * 4 + wave;                // 1 KB chunk = 64 rows x 16 B
+      const int row = chunk * 64 + lane;
+      copy16_to_lds(as, __umul24(min(row, ra), ks), stage + 2 * C::kCodeTile + chunk * 1024);
+      copy16_to_lds(ws, __umul24(min(row, rw), ks), stage + 2 * C::kCodeTile + C::kScaleTile + chunk * 1024);
+    }
+    if (T / 256 == 0) {   // 128-row tiles: 128 rows x 16 B = 2 KB per operand, half the waves each
+      const int row = (wave & 1) * 64 + lane;
+      if (wave < 2)
+        copy16_to_lds(as, __umul24(min(row, ra), ks), stage + 2 * C::kCodeTile + (wave & 1) * 1024);
+      else
+        copy16_to_lds(ws, __umul24(min(row, rw), ks), stage + 2 * C::kCodeTile + C::kScaleTile + (wave & 1) * 1024);
+    }
   }
 }
 
@@ -334,18 +355,140 @@ __device__ __forceinline__ void prefill_stage(const GemmArgs& g, uint8_t* lds, i
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// ------------------------------------------------------------------ MXFP4 operands
+
+// Registers one wave carries through the K loop of a T x T tile whose operands are MXFP4
+// (E2M1 codes with one E8M0 scale per 32 elements).
+template <int T>
+struct MxRegs {
+  static constexpr int F = T / 64;
+  f32x16_t acc[F][F];
+  uint4 qa[F], qb[F];            // codes of the current 64-wide chunk: the lane's 32-element block
+  uint32_t sa[2][F], sb[2][F];   // the stage's 8 E8M0 bytes of each lane row: byte 2 (c & 1) + h of
+                                 // dword c >> 1 is block 2c + h
+  int swa[F], swb[F];
+};
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ i32x8_t fp4_operand(const uint4& q) {
+  return i32x8_t{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+}
+
+// The F x F scaled MFMAs of one 64-wide chunk: lane (r, h) supplies the 32 E2M1 codes of block
+// 2c + h of its A row and W row and their E8M0 bytes, byte OPSEL + h of the scale dwords (the
+// dwords are shifted right by sh = 8h here, at their use, so that OPSEL is the same for every
+// lane).  The hardware scales each product by 2^(sa - 127) * 2^(sb - 127) and accumulates in fp32.
+template <int F, int OPSEL>
+__device__ __forceinline__ void mx_chunk_mma(f32x16_t (&acc)[F][F], const uint4 (&qa)[F], const uint4 (&qb)[F],
+                                             const uint32_t (&sa)[F], const uint32_t (&sb)[F], uint32_t sh) {
+  int xa[F], xb[F];
+#pragma unroll
+  for (int i = 0; i < F; ++i) {
+    xa[i] = (int)(sa[i] >> sh);
+    xb[i] = (int)(sb[i] >> sh);
+  }
+#pragma unroll
+  for (int i = 0; i < F; ++i)
+#pragma unroll
+    for (int j = 0; j < F; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4_operand(qa[i]), fp4_operand(qb[j]), acc[i][j],
+                                                                  4, 4, OPSEL, xa[i], OPSEL, xb[j]);
+}
+
+// One 256-deep stage kt of an MXFP4 tile, as 4 chunks of 64-deep scaled MFMAs.  While a chunk's
+// MFMAs run, the next chunk's codes are read from LDS; before the last chunk the stage kt+1
+// copies are waited for and published with the stage's only barrier, the copies of stage kt+2
+// are issued into stage kt's buffer when LOAD (every read of it is done), and the next stage's
+// first codes and scale bytes are read.  In the last stage that look-ahead reads a stale
+// buffer whose values are never used.
+template <int T, bool LOAD>
+__device__ __forceinline__ void mx_stage(const GemmArgs& g, uint8_t* lds, int m0, int n0, int kt, MxRegs<T>& R) {
+  using C = TileCfg<T>;
+  constexpr int F = C::F;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = (wave >> 1) * (T / 2), wn = (wave & 1) * (T / 2);
+  const int r = lane & 31, h = lane >> 5;
+  uint8_t* buf = lds + (kt & 1) * C::kStageBytes;
+  const uint8_t* nbuf = lds + ((kt + 1) & 1) * C::kStageBytes;
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    __builtin_amdgcn_sched_barrier(0);
+    const bool last = c + 1 == kChunks;
+    if (last) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0): stage kt+1 copied by this wave
+      __syncthreads();                           // ... and by every wave
+      if (LOAD) load_stage_lds<T, true>(g, m0, n0, kt + 2, buf);
+    }
+    const uint8_t* src = last ? nbuf : buf;
+    const int slot = last ? h : 2 * (c + 1) + h;
+    const uint8_t* ca = src + (wm + r) * kRowBytes;
+    const uint8_t* cb = src + C::kCodeTile + (wn + r) * kRowBytes;
+    uint4 na[F], nb[F];
+#pragma unroll
+    for (int i = 0; i < F; ++i) {
+      na[i] = *reinterpret_cast<const uint4*>(ca + 32 * i * kRowBytes + ((slot ^ R.swa[i]) << 4));
+      nb[i] = *reinterpret_cast<const uint4*>(cb + 32 * i * kRowBytes + ((slot ^ R.swb[i]) << 4));
+    }
+    uint32_t nsa[2][F], nsb[2][F];
+    if (last) {
+      const uint8_t* sa_t = nbuf + 2 * C::kCodeTile + (wm + r) * 8;
+      const uint8_t* sb_t = nbuf + 2 * C::kCodeTile + C::kScaleTile + (wn + r) * 8;
+#pragma unroll
+      for (int i = 0; i < F; ++i) {
+        const uint2 xa = *reinterpret_cast<const uint2*>(sa_t + 32 * i * 8);
+        const uint2 xb = *reinterpret_cast<const uint2*>(sb_t + 32 * i * 8);
+        nsa[0][i] = xa.x;
+        nsa[1][i] = xa.y;
+        nsb[0][i] = xb.x;
+        nsb[1][i] = xb.y;
+      }
+    }
+    const uint32_t sh = 8u * (uint32_t)h;
+    if ((c & 1) == 0)
+      mx_chunk_mma<F, 0>(R.acc, R.qa, R.qb, R.sa[c >> 1], R.sb[c >> 1], sh);
+    else
+      mx_chunk_mma<F, 2>(R.acc, R.qa, R.qb, R.sa[c >> 1], R.sb[c >> 1], sh);
+    // Issue order: the look-ahead LDS reads first, one between consecutive MFMAs, so that they
+    // complete long before the next chunk needs them.
+    constexpr int kMma = F * F;
+    const int reads = last ? 4 * F : 2 * F;
+#pragma unroll
+    for (int k = 0; k < 4 * F; ++k) {
+      if (k < reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (k < kMma) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    if (kMma > 4 * F) __builtin_amdgcn_sched_group_barrier(0x008, kMma - 4 * F, 0);
+#pragma unroll
+    for (int i = 0; i < F; ++i) {
+      R.qa[i] = na[i];
+      R.qb[i] = nb[i];
+    }
+    if (last) {
+#pragma unroll
+      for (int i = 0; i < F; ++i) {
+        R.sa[0][i] = nsa[0][i];
+        R.sa[1][i] = nsa[1][i];
+        R.sb[0][i] = nsb[0][i];
+        R.sb[1][i] = nsb[1][i];
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // One T x T output tile (T = 256 or 128) on 4 waves in a 2 x 2 grid, each wave T/2 x T/2 as
 // (T/64) x (T/64) MFMA 32x32x16 f16 tiles, over the whole K range in 256-deep stages
 // double-buffered in LDS.
-template <int T, int EPI>
+template <int T, int EPI, bool MX = false>
 __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, int m0, int n0) {
   using C = TileCfg<T>;
   constexpr int F = C::F;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = (wave >> 1) * (T / 2), wn = (wave & 1) * (T / 2);
   const int r = lane & 31, h = lane >> 5;
-  PrefillRegs<T> R;
-  R.sel = scale_halves_sel(h);
+  std::conditional_t<MX, MxRegs<T>, PrefillRegs<T>> R;
+  if constexpr (!MX) R.sel = scale_halves_sel(h);
 #pragma unroll
   for (int i = 0; i < F; ++i) {
     R.swa[i] = slot_swizzle(wm + 32 * i + r);
@@ -359,8 +502,8 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
   // Prologue: stages 0 and 1 in flight, the scale tables filled, stage 0 published, its
   // first step's fragments made.
   const int nk = g.K / BK;
-  load_stage_lds<T>(g, m0, n0, 0, lds);
-  if (nk > 1) load_stage_lds<T>(g, m0, n0, 1, lds + C::kStageBytes);
+  load_stage_lds<T, MX>(g, m0, n0, 0, lds);
+  if (nk > 1) load_stage_lds<T, MX>(g, m0, n0, 1, lds + C::kStageBytes);
   {
     float* row_scale = reinterpret_cast<float*>(lds + kScaleTableOffset);
     for (int t = threadIdx.x; t < 2 * T; t += kPrefillThreads)
@@ -369,7 +512,23 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
   __syncthreads();
-  {
+  if constexpr (MX) {
+    const uint8_t* ca = lds + (wm + r) * kRowBytes;
+    const uint8_t* cb = lds + C::kCodeTile + (wn + r) * kRowBytes;
+    const uint8_t* sa_t = lds + 2 * C::kCodeTile + (wm + r) * 8;
+    const uint8_t* sb_t = lds + 2 * C::kCodeTile + C::kScaleTile + (wn + r) * 8;
+#pragma unroll
+    for (int i = 0; i < F; ++i) {
+      R.qa[i] = *reinterpret_cast<const uint4*>(ca + 32 * i * kRowBytes + ((h ^ R.swa[i]) << 4));
+      R.qb[i] = *reinterpret_cast<const uint4*>(cb + 32 * i * kRowBytes + ((h ^ R.swb[i]) << 4));
+      const uint2 xa = *reinterpret_cast<const uint2*>(sa_t + 32 * i * 8);
+      const uint2 xb = *reinterpret_cast<const uint2*>(sb_t + 32 * i * 8);
+      R.sa[0][i] = xa.x;
+      R.sa[1][i] = xa.y;
+      R.sb[0][i] = xb.x;
+      R.sb[1][i] = xb.y;
+    }
+  } else {
     const uint8_t* ca = lds + (wm + r) * kRowBytes;
     const uint8_t* cb = lds + C::kCodeTile + (wn + r) * kRowBytes;
     const uint8_t* sa_t = lds + 2 * C::kCodeTile + (wm + r) * kScaleRow;
@@ -389,8 +548,13 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
     dequant_step<F>(R.qa, R.qb, R.pa, R.pb, 0, R.fa, R.fb);
   }
   int kt = 0;
-  for (; kt + 2 < nk; ++kt) prefill_stage<T, true>(g, lds, m0, n0, kt, R);
-  for (; kt < nk; ++kt) prefill_stage<T, false>(g, lds, m0, n0, kt, R);
+  if constexpr (MX) {
+    for (; kt + 2 < nk; ++kt) mx_stage<T, true>(g, lds, m0, n0, kt, R);
+    for (; kt < nk; ++kt) mx_stage<T, false>(g, lds, m0, n0, kt, R);
+  } else {
+    for (; kt + 2 < nk; ++kt) prefill_stage<T, true>(g, lds, m0, n0, kt, R);
+    for (; kt < nk; ++kt) prefill_stage<T, false>(g, lds, m0, n0, kt, R);
+  }
   auto& acc = R.acc;
 
   // Epilogue: y = (acc * s_gA[m]) * s_gW[seg(n)], with the scales from the tables.
@@ -568,6 +732,20 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(GemmAr
     int tm, tn;
     tile_coords(blockIdx.x - tiles_big, (g.M + 127) / 128, (g.N - n_split + 127) / 128, tm, tn);
     prefill_tile<128, EPI>(g, lds, tm * 128, n_split + tn * 128);
+  }
+}
+
+// The same tiling with MXFP4 operands (scaled FP4 MFMAs), fp32 or bf16 output.
+__global__ __launch_bounds__(kPrefillThreads, 1) void gemm_mx_kernel(GemmArgs g, int n_split, int tiles_big) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  if ((int)blockIdx.x < tiles_big) {
+    int tm, tn;
+    tile_coords(blockIdx.x, (g.M + 255) / 256, (n_split + 255) / 256, tm, tn);
+    prefill_tile<256, kEpiStore, true>(g, lds, tm * 256, tn * 256);
+  } else {
+    int tm, tn;
+    tile_coords(blockIdx.x - tiles_big, (g.M + 127) / 128, (g.N - n_split + 127) / 128, tm, tn);
+    prefill_tile<128, kEpiStore, true>(g, lds, tm * 128, n_split + tn * 128);
   }
 }
 
@@ -933,15 +1111,11 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return 0;   // no path needs device scratch
 }
 
-int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
-                const float* a_global, int a_global_per_row, const uint8_t* w_codes, const uint8_t* w_scales,
-                const float* w_globals, const SegmentTable& seg, void* y, int y_dtype, int64_t ldy, void* workspace,
-                hipStream_t stream, const QuantOut* qout, const GateOut* gates) {
-  (void)workspace;
-  if (M == 0 || N == 0) return NVFP4_OK;
-  const bool plain = K % 128 != 0 || (M > 16 && (K % BK != 0 || K >= (1 << 24)));
-  if (qout && (plain || N % 16 != 0)) return NVFP4_ERR_UNSUPPORTED;
-  if (qout && gates) return NVFP4_ERR_INVALID_ARG;
+namespace {
+
+GemmArgs gemm_args(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+                   const float* a_global, int a_global_per_row, const uint8_t* w_codes, const uint8_t* w_scales,
+                   const float* w_globals, const SegmentTable& seg, void* y, int y_dtype, int64_t ldy) {
   GemmArgs g;
   g.M = (int32_t)M;
   g.N = (int32_t)N;
@@ -958,6 +1132,72 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
   g.ldy = ldy;
   g.y_vec = reinterpret_cast<uintptr_t>(y) % 16 == 0 && (ldy * (g.y_bf16 ? 2 : 4)) % 16 == 0;
   g.seg = seg;
+  g.q_out = 0;
+  g.q_global = nullptr;
+  g.q_codes = nullptr;
+  g.q_scales = nullptr;
+  g.gate_n0 = (int32_t)N;
+  g.gate_h = 0;
+  g.gate_a_log = nullptr;
+  g.gate_dt_bias = nullptr;
+  g.gate_g = nullptr;
+  g.gate_beta = nullptr;
+  return g;
+}
+
+// Once per device: raise the tile kernels' dynamic LDS limit (their 146 KB exceed the default)
+// and read the CU count.
+int tile_kernels_ready(int& cus) {
+  static bool ready[64] = {};
+  static int cu_count[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return NVFP4_ERR_HIP;
+  if (!ready[dev]) {
+    const void* kernels[] = {reinterpret_cast<const void*>(gemm_prefill_kernel<kEpiStore>),
+                             reinterpret_cast<const void*>(gemm_prefill_kernel<kEpiNvfp4>),
+                             reinterpret_cast<const void*>(gemm_prefill_kernel<kEpiGates>),
+                             reinterpret_cast<const void*>(gemm_mx_kernel)};
+    for (const void* k : kernels)
+      if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kPrefillLds) != hipSuccess)
+        return NVFP4_ERR_HIP;
+    if (hipDeviceGetAttribute(&cu_count[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return NVFP4_ERR_HIP;
+    ready[dev] = true;
+  }
+  cus = cu_count[dev];
+  return NVFP4_OK;
+}
+
+// One 256 x 256 tile per CU at a time.  If the last round of tiles would fill at most half of
+// the CUs, enough whole tile columns move to 128 x 128 tiles to absorb it: workgroups
+// [0, big) take 256 x 256 tiles of columns [0, n_split), the other `small` 128 x 128 tiles.
+void tile_grid(int64_t M, int64_t N, int cus, int64_t& n_split, int64_t& big, int64_t& small) {
+  const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256;
+  const int64_t rem = (tm * tn) % cus;
+  int64_t peel = 0;
+  n_split = N;
+  if (rem > 0 && rem <= cus / 2) {
+    peel = (rem + tm - 1) / tm;
+    if (peel >= tn) peel = 0;
+    n_split = (tn - peel) * 256;
+  }
+  big = tm * ((n_split + 255) / 256);
+  small = peel ? ((M + 127) / 128) * ((N - n_split + 127) / 128) : 0;
+}
+
+}  // namespace
+
+int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+                const float* a_global, int a_global_per_row, const uint8_t* w_codes, const uint8_t* w_scales,
+                const float* w_globals, const SegmentTable& seg, void* y, int y_dtype, int64_t ldy, void* workspace,
+                hipStream_t stream, const QuantOut* qout, const GateOut* gates) {
+  (void)workspace;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  const bool plain = K % 128 != 0 || (M > 16 && (K % BK != 0 || K >= (1 << 24)));
+  if (qout && (plain || N % 16 != 0)) return NVFP4_ERR_UNSUPPORTED;
+  if (qout && gates) return NVFP4_ERR_INVALID_ARG;
+  GemmArgs g = gemm_args(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales, w_globals, seg,
+                         y, y_dtype, ldy);
   g.q_out = qout != nullptr;
   g.q_global = qout ? qout->global : nullptr;
   g.q_codes = qout ? qout->codes : nullptr;
@@ -996,35 +1236,11 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
     else
       gemm_decode_kernel<false><<<grid, kDecodeThreads, 0, stream>>>(g);
   } else {
-    // The 146 KB of dynamic LDS exceed the default limit; raise it once per device.
-    static bool attr_set[64] = {};
-    static int cus[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return NVFP4_ERR_HIP;
-    if (!attr_set[dev]) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_prefill_kernel<kEpiStore>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kPrefillLds) != hipSuccess ||
-          hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_prefill_kernel<kEpiNvfp4>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kPrefillLds) != hipSuccess ||
-          hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_prefill_kernel<kEpiGates>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kPrefillLds) != hipSuccess)
-        return NVFP4_ERR_HIP;
-      if (hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return NVFP4_ERR_HIP;
-      attr_set[dev] = true;
-    }
-    // One 256 x 256 tile per CU at a time.  If the last round of tiles would fill at most
-    // half of the CUs, move enough whole tile columns to 128 x 128 tiles to absorb it.
-    const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256;
-    const int64_t rem = (tm * tn) % cus[dev];
-    int64_t n_split = N, peel = 0;
-    if (rem > 0 && rem <= cus[dev] / 2) {
-      peel = (rem + tm - 1) / tm;
-      if (peel >= tn) peel = 0;
-      n_split = (tn - peel) * 256;
-    }
-    const int64_t big = tm * ((n_split + 255) / 256);
-    const int64_t small = peel ? ((M + 127) / 128) * ((N - n_split + 127) / 128) : 0;
+    int cus = 0;
+    const int st = tile_kernels_ready(cus);
+    if (st != NVFP4_OK) return st;
+    int64_t n_split, big, small;
+    tile_grid(M, N, cus, n_split, big, small);
     const unsigned grid = (unsigned)(big + small);
     if (g.q_out)
       gemm_prefill_kernel<kEpiNvfp4><<<grid, kPrefillThreads, kPrefillLds, stream>>>(g, (int)n_split, (int)big);
@@ -1033,6 +1249,23 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
     else
       gemm_prefill_kernel<kEpiStore><<<grid, kPrefillThreads, kPrefillLds, stream>>>(g, (int)n_split, (int)big);
   }
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+int launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+                   const float* a_global, int a_global_per_row, const uint8_t* w_codes, const uint8_t* w_scales,
+                   const float* w_globals, const SegmentTable& seg, void* y, int y_dtype, int64_t ldy,
+                   hipStream_t stream) {
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (K % BK != 0 || K >= (1 << 24)) return NVFP4_ERR_UNSUPPORTED;
+  const GemmArgs g = gemm_args(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales,
+                               w_globals, seg, y, y_dtype, ldy);
+  int cus = 0;
+  const int st = tile_kernels_ready(cus);
+  if (st != NVFP4_OK) return st;
+  int64_t n_split, big, small;
+  tile_grid(M, N, cus, n_split, big, small);
+  gemm_mx_kernel<<<(unsigned)(big + small), kPrefillThreads, kPrefillLds, stream>>>(g, (int)n_split, (int)big);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 

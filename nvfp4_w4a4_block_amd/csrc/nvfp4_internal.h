@@ -78,6 +78,17 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
                 const QuantOut* qout = nullptr, const GateOut* gates = nullptr);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+// MXFP4 operands (E2M1 codes [rows, K/2] as NVFP4, E8M0 scale bytes [rows, K/32]), the same
+// tiling with scaled FP4 MFMAs; K % 256 == 0 and K < 2^24 (NVFP4_ERR_UNSUPPORTED otherwise).
+int launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+                   const float* a_global, int a_global_per_row, const uint8_t* w_codes, const uint8_t* w_scales,
+                   const float* w_globals, const SegmentTable& seg, void* y, int y_dtype, int64_t ldy,
+                   hipStream_t stream);
+
+// Lossy NVFP4 -> MXFP4 re-encoding (mxfp4.hip); cols % 32 == 0, contiguous rows.
+int launch_mx_reencode(int64_t rows, int64_t cols, const uint8_t* codes, const uint8_t* scales, uint8_t* mx_codes,
+                       uint8_t* mx_scales, hipStream_t stream);
+
 // FP8 KV-cache codec launchers (kv_fp8.hip).
 int launch_kv_quantize(const void* x, int x_dtype, int64_t n, const float* scale, uint8_t* q, hipStream_t stream);
 int launch_kv_dequantize(const uint8_t* q, int64_t n, const float* scale, void* y, int y_dtype, hipStream_t stream);

@@ -146,7 +146,7 @@ def test_m0_is_only_set_for_lds_copies(tmp_path):
         if not re.search(r"\bm0\b", l):
             continue
         assert re.fullmatch(r"s_mov_b32 m0, s\d+", l), l
-        assert code[i + 1].startswith("global_load_lds_dwordx4"), (l, code[i + 1])
+        assert code[i + 1].startswith("global_load_lds_dword"), (l, code[i + 1])
         writes += 1
     assert writes > 0
     # global_load_lds reads M0 implicitly: each one must follow its own M0 write.
@@ -195,3 +195,23 @@ def test_gdn_gates_argument_errors(nv):
     assert call(gg=A16 + 2) == 1 and call(beta=A16 + 1) == 1 and call(al=A16 + 2) == 1
     assert call(y=None) == 1
     assert call(M=0) == 0                          # empty product: a no-op
+
+
+def test_mxfp4_argument_errors(nv):
+    r = nv.lib.nvfp4_to_mxfp4
+    assert r(4, 48, A16, A16, A16, A16, None) == 1            # cols not a multiple of 32
+    assert r(-1, 64, A16, A16, A16, A16, None) == 1
+    assert r(4, 64, A16 + 8, A16, A16, A16, None) == 1        # codes must be 16-byte aligned
+    assert r(4, 64, A16, A16 + 1, A16, A16, None) == 1        # scales 2-byte aligned
+    assert r(4, 64, A16, A16, None, A16, None) == 1
+    assert r(0, 64, None, None, None, None, None) == 0
+    g = nv.lib.nvfp4_mxfp4_gemm
+    w = (ctypes.c_int64 * 1)(64)
+
+    def call(M=32, K=512, y=A16, dt=1):
+        return g(M, K, A16, A16, A16, 0, 1, ctypes.cast(w, ctypes.c_void_p), A16, A16, A16, y, dt, 64, None)
+
+    assert call(K=384) == 2                        # K not a multiple of 256
+    assert call(K=40) == 1                         # K not a multiple of 16
+    assert call(y=None) == 1 and call(dt=7) == 1
+    assert call(M=0) == 0
