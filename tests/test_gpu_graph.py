@@ -1,0 +1,96 @@
+"""The library under HIP graph capture: every entry point is stream-ordered, allocates nothing
+and never synchronises, so a captured step must replay to exactly the eager result.  Each
+graph is replayed several times with new inputs written eagerly between the replays, and every
+replay is compared bitwise with an eager run on the same inputs."""
+import pytest
+import torch
+
+import workloads
+from tests.gpu_helpers import DEV, nv, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _fill(t: torch.Tensor, seed: int, rows: int, cols: int) -> None:
+    t.copy_(to_gpu(workloads.activation(seed, 0, rows, cols, outlier_frac=0.01, outlier_gain=50.0)))
+
+
+def _replay_and_compare(g: torch.cuda.CUDAGraph, x: torch.Tensor, rows: int, cols: int, outputs, eager) -> None:
+    for i in range(4):
+        _fill(x, 300 + i, rows, cols)           # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = eager()
+        torch.cuda.synchronize()
+        for got, ref in zip(outputs, want):
+            assert torch.equal(got, ref), f"replay {i}"
+
+
+def test_graph_quantize_then_gemm():
+    M, N, K = 512, 1024, 1024
+    w = nv().quantize(to_gpu(workloads.weight(200, 1, N, K)))
+    x = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+    _fill(x, 299, M, K)
+    a = nv().quantize(x)                          # eager first: per-device set-up happens here
+    y = nv().gemm(a, w, torch.bfloat16)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        nv().quantize(x, out=a)
+        nv().gemm(a, w, torch.bfloat16, out=y)
+
+    def eager():
+        ae = nv().quantize(x)
+        return ae.codes, ae.scales, ae.global_scale, nv().gemm(ae, w, torch.bfloat16)
+
+    _replay_and_compare(g, x, M, K, (a.codes, a.scales, a.global_scale, y), eager)
+
+
+def test_graph_decode_per_row():
+    M, N, K = 4, 512, 2048
+    w = nv().quantize(to_gpu(workloads.weight(201, 1, N, K)))
+    x = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+    _fill(x, 299, M, K)
+    a = nv().quantize(x, "per_row")
+    y = nv().gemm(a, w, torch.float32)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        nv().quantize(x, "per_row", out=a)
+        nv().gemm(a, w, torch.float32, out=y)
+
+    def eager():
+        ae = nv().quantize(x, "per_row")
+        return ae.codes, ae.global_scale, nv().gemm(ae, w, torch.float32)
+
+    _replay_and_compare(g, x, M, K, (a.codes, a.global_scale, y), eager)
+
+
+def test_graph_fp8_kv_and_mxfp4():
+    M, N, K = 256, 512, 512
+    scale = torch.tensor([0.05], dtype=torch.float32, device=DEV)
+    w = nv().to_mxfp4(nv().quantize(to_gpu(workloads.weight(202, 1, N, K))))
+    x = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+    _fill(x, 299, M, K)
+    q = nv().fp8_kv_quantize(x, scale)
+    back = nv().fp8_kv_dequantize(q, scale, torch.bfloat16)
+    a = nv().quantize(x)
+    am = nv().to_mxfp4(a)
+    y = nv().mxfp4_gemm(am, w.codes, w.scales, (N,), w.global_scale, torch.float32)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        nv().fp8_kv_quantize(x, scale, out=q)
+        nv().fp8_kv_dequantize(q, scale, torch.bfloat16, out=back)
+        nv().quantize(x, out=a)
+        nv().to_mxfp4(a, out=am)
+        nv().mxfp4_gemm(am, w.codes, w.scales, (N,), w.global_scale, torch.float32, out=y)
+
+    def eager():
+        qe = nv().fp8_kv_quantize(x, scale)
+        ae = nv().to_mxfp4(nv().quantize(x))
+        return (qe, nv().fp8_kv_dequantize(qe, scale, torch.bfloat16), ae.codes, ae.scales,
+                nv().mxfp4_gemm(ae, w.codes, w.scales, (N,), w.global_scale, torch.float32))
+
+    _replay_and_compare(g, x, M, K, (q, back, am.codes, am.scales, y), eager)
