@@ -146,6 +146,20 @@ def _bytes_quantize(rows: int, cols: int, in_bytes: int = 2) -> float:
     return rows * cols * (in_bytes + 0.5 + 1.0 / 16)
 
 
+def bf16_library_gemm(steps: int, warmup: int, settle_s: float) -> dict:
+    """Context: PyTorch's bf16 GEMM (the ROCm BLAS library) on random bf16 operands at the
+    prefill shape, Y = X . W^T, timed like the NVFP4 GEMM.  Not part of the path."""
+    p = workloads.PREFILL
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(0)
+    x = torch.randn(p.M, p.K, device=dev, dtype=torch.bfloat16, generator=g)
+    wt = torch.randn(p.N, p.K, device=dev, dtype=torch.bfloat16, generator=g).t()
+    y = torch.empty(p.M, p.N, device=dev, dtype=torch.bfloat16)
+    ms = _mean_ms(lambda i: torch.matmul(x, wt, out=y), steps, warmup, settle_s)
+    return {"what": "torch.matmul bf16 x bf16 -> bf16 at the same shape (ROCm BLAS library)",
+            "ms": round(ms, 4), "tflops": round(p.flops / (ms * 1e-3) / 1e12, 2)}
+
+
 def bench_prefill(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: int = 8):
     p = workloads.PREFILL
     dev = torch.device("cuda:0")
@@ -550,7 +564,8 @@ def main() -> int:
                          "algorithmic_bytes": res["qbytes"]},
         },
         "context": {"pages": "17.5 GiB NVFP4 checkpoint and +14-19% prefill vs the other recipes compared; "
-                             "hardware not stated"},
+                             "hardware not stated",
+                    "bf16_library_gemm": bf16_library_gemm(min(args.steps, 20), args.warmup, args.settle_s)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_prefill(p)
