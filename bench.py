@@ -401,6 +401,55 @@ def bench_gdn_gates(nv, steps: int, warmup: int, settle_s: float = 0.0):
 MFMA_FP4_PEAK_TFLOPS = 10100.0   # MI355X dense FP4 / FP6
 
 
+def bench_sweep(nv, steps: int, warmup: int, settle_s: float = 0.0):
+    """Every linear GEMM of the synthetic 64-layer hybrid (48 GDN + 16 attention layers, hidden
+    5120, MLP 17408) at M = 16384 prefill tokens: per launch, the per-tensor NVFP4 quantize of
+    its activation and the fused NVFP4 GEMM to bf16.  Each of the 256 launches has its own
+    weights (seeded N(0, 0.02) drawn on the GPU, quantized per module: ~12.8 GB of NVFP4), so no
+    launch finds another's weights in a cache.  Activations: one seeded bf16 tensor per K."""
+    sw = workloads.SWEEP
+    dev = torch.device("cuda:0")
+    launches = workloads.sweep_launches(sw)
+    gen = torch.Generator(device=dev).manual_seed(sw.seed)
+    weights = []
+    for li, L in enumerate(launches):
+        if li % 32 == 0:
+            print(f"[sweep] quantizing weights of launch {li}/{len(launches)}", file=sys.stderr, flush=True)
+        qs = []
+        for n in L.widths:
+            w = torch.randn(n, L.K, device=dev, dtype=torch.bfloat16, generator=gen).mul_(sw.w_sigma)
+            qs.append(nv.quantize(w))
+            del w
+        weights.append((torch.cat([q.codes for q in qs]), torch.cat([q.scales for q in qs]),
+                        torch.cat([q.global_scale for q in qs])))
+    xs = {K: torch.from_numpy(sw.x(0, K)).to(dev).to(torch.bfloat16) for K in sorted({L.K for L in launches})}
+    aq = {K: nv.quantize(x) for K, x in xs.items()}
+    ys = {N: torch.empty((sw.M, N), dtype=torch.bfloat16, device=dev) for N in sorted({L.N for L in launches})}
+    flops = sum(2.0 * sw.M * L.N * L.K for L in launches)
+
+    def step(i):
+        for L, (c, s_, g) in zip(launches, weights):
+            a = nv.quantize(xs[L.K], out=aq[L.K])
+            nv.gemm_fused_segments(a, c, s_, L.widths, g, torch.bfloat16, out=ys[L.N])
+
+    ms = _mean_ms(step, max(1, steps), warmup, settle_s)
+    kinds = {}
+    for kind in ("gdn_in", "gdn_out", "attn_qkv", "attn_o", "mlp_gate_up", "mlp_down"):
+        i = next(j for j, L in enumerate(launches) if L.kind == kind)
+        L, (c, s_, g) = launches[i], weights[i]
+        a = aq[L.K]
+        kms = _mean_ms(lambda _: nv.gemm_fused_segments(a, c, s_, L.widths, g, torch.bfloat16, out=ys[L.N]),
+                       10, 2, 0.0)
+        f = 2.0 * sw.M * L.N * L.K
+        kinds[kind] = {"N": L.N, "K": L.K, "segments": len(L.widths), "count": sum(1 for x in launches if x.kind == kind),
+                       "gemm_ms": round(kms, 4), "tflops": round(f / (kms * 1e-3) / 1e12, 1)}
+    nvfp4_bytes = sum(int(c.numel() + s_.numel() + 4 * g.numel()) for c, s_, g in weights)
+    return {"launches": len(launches), "tflop": round(flops / 1e12, 1), "ms_per_sweep": round(ms, 3),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1), "frac_mfma_f16": round(flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+            "weights_nvfp4_gb": round(nvfp4_bytes / 1e9, 2), "per_kind": kinds,
+            "note": "each launch: per-tensor quantize of its activation + fused NVFP4 GEMM to bf16"}
+
+
 def bench_mxfp4(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: int = 8):
     """The lossy MXFP4 variant at the prefill shape: per step, the NVFP4 quantize of X, its
     re-encoding to MXFP4 and the scaled-FP4 MFMA GEMM (W re-encoded offline), beside the NVFP4
@@ -480,7 +529,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--settle-s", type=float, default=1.0,
                     help="seconds of untimed steps before the warmup steps, for steady clocks")
-    ap.add_argument("--workload", choices=["prefill", "decode", "fused", "nvfp4_out", "kv_fp8", "gdn_gates", "mxfp4"],
+    ap.add_argument("--workload", choices=["prefill", "decode", "fused", "nvfp4_out", "kv_fp8", "gdn_gates", "mxfp4",
+                                           "sweep"],
                     default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=TRAFFIC_JSON,
@@ -506,6 +556,10 @@ def main() -> int:
         return 0
     if args.workload == "kv_fp8":
         print(json.dumps({"workload": "kv_fp8", "results": bench_kv_fp8(nv, args.steps, args.warmup, args.settle_s)}))
+        return 0
+    if args.workload == "sweep":
+        print(json.dumps({"workload": "sweep", "results": bench_sweep(nv, min(args.steps, 5), min(args.warmup, 2),
+                                                                      args.settle_s)}))
         return 0
     if args.workload == "mxfp4":
         print(json.dumps({"workload": "mxfp4", "results": bench_mxfp4(nv, args.steps, args.warmup, args.settle_s)}))
