@@ -24,6 +24,11 @@
 //    reduce them in LDS in a fixed order (deterministic) before the scales are applied.
 //  * A plain kernel (one thread per output, fp32 FMA) serves shapes the fast kernels do not
 //    take (K not a multiple of 128; for M > 16, K not a multiple of 256 or K >= 2^24).
+//  * Epilogue modes, chosen at compile time so that each kernel keeps its registers: Y in fp32
+//    or bf16; Y quantized to NVFP4 in the same launch under a given output global scale (for
+//    the next linear layer); Y plus the Gated DeltaNet gates of the last two fused segments.
+//  * MXFP4 operands (a lossy variant; E2M1 codes with one E8M0 scale per 32 elements): the same
+//    tiles and copies, with gfx950's scaled FP4 MFMA instead of dequantization.
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
 
