@@ -215,3 +215,38 @@ def test_mxfp4_argument_errors(nv):
     assert call(K=40) == 1                         # K not a multiple of 16
     assert call(y=None) == 1 and call(dt=7) == 1
     assert call(M=0) == 0
+
+
+def test_header_is_c99_and_links_from_c(nv, tmp_path):
+    """The header is plain C: a C99 program that takes the address of every declared entry point
+    compiles with -pedantic -Werror, links against the library, and runs its host-only paths
+    (version, status strings, argument errors detected before any launch)."""
+    fns = _declared_functions()
+    src = tmp_path / "abi_check.c"
+    src.write_text("""#include <stdio.h>
+#include "nvfp4.h"
+typedef void (*fn_t)(void);
+static const fn_t entry_points[] = {
+""" + ",\n".join(f"  (fn_t){f}" for f in fns) + """
+};
+int main(void) {
+  unsigned i;
+  for (i = 0; i < sizeof entry_points / sizeof entry_points[0]; ++i)
+    if (!entry_points[i]) return 1;
+  if (nvfp4_version() <= 0) return 2;
+  if (!nvfp4_status_string(NVFP4_ERR_INVALID_ARG)) return 3;
+  /* K not a multiple of 16: rejected on the host, before anything touches a GPU */
+  if (nvfp4_gemm(16, 16, 24, 0, 0, 0, 0, 0, 0, 0, 0, NVFP4_BF16, 16, 0, 0, 0) != NVFP4_ERR_INVALID_ARG) return 4;
+  printf("ok %u\\n", (unsigned)(sizeof entry_points / sizeof entry_points[0]));
+  return 0;
+}
+""")
+    lib_dir = os.path.dirname(nv.library_path())
+    exe = tmp_path / "abi_check"
+    rocm_lib = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
+    r = subprocess.run(["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        str(src), "-o", str(exe), "-L", lib_dir, "-lnvfp4", f"-Wl,-rpath,{lib_dir}",
+                        f"-Wl,-rpath-link,{rocm_lib}"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == f"ok {len(fns)}", (r.returncode, r.stdout, r.stderr[-2000:])
