@@ -135,3 +135,35 @@ def test_deterministic():
     a, b = nv().quantize(x), nv().quantize(x)
     assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales)
     assert torch.equal(a.global_scale, b.global_scale)
+
+
+@pytest.mark.parametrize("sg", [1.0, 2.0 ** -10, 3.7, 2.0 ** 20])
+@pytest.mark.parametrize("arrangement", ["sorted", "shuffled"])
+def test_every_finite_bf16_value(sg, arrangement):
+    # All 65280 finite bf16 bit patterns (both signs, subnormals and zeros included), in blocks of
+    # 16 neighbouring magnitudes or randomly mixed, encoded under a given global scale.
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32)
+    vals = vals[np.isfinite(vals)]
+    if arrangement == "sorted":
+        vals = vals[np.argsort(np.abs(vals), kind="stable")]
+    else:
+        vals = vals[np.random.default_rng(7).permutation(vals.size)]
+    x = vals.reshape(-1, 256)                # 255 rows x 256 columns, exact in bf16
+    assert x.shape[0] * 256 == vals.size
+    _check(x, "given", bf16=True, given=sg, what=f"all bf16 {arrangement} sg={sg}")
+
+
+@pytest.mark.parametrize("sg", [1.0, 2.0 ** -40, 2.0 ** 40])
+def test_random_fp32_blocks_across_the_range(sg):
+    # fp32 inputs with full random mantissas; each 16-block spans 4 octaves around its own
+    # exponent in [-100, 100], so the quotient takes the fast and the fallback path alike.
+    g = np.random.default_rng(11)
+    nblk = 1 << 17
+    e_blk = g.integers(-100, 101, nblk)
+    e = np.repeat(e_blk, 16) - g.integers(0, 5, nblk * 16)
+    m = 1.0 + g.random(nblk * 16)
+    sgn = np.where(g.random(nblk * 16) < 0.5, -1.0, 1.0)
+    x = (sgn * np.ldexp(m, e)).astype(np.float32).reshape(-1, 1024)
+    assert np.isfinite(x).all()
+    _check(x, "given", bf16=False, given=sg, what=f"random fp32 sg={sg}")
