@@ -8,7 +8,7 @@ several X copies are rotated so that no step reads its X from the 256 MB last-le
 
 Workloads (--workload):
   prefill  X[4096x5120] bf16 (0.1% channels x50), W[17408x5120]        (default)
-  decode   X[M x 17408], W[5120x17408], M in {1,4,16}, per-token scales
+  decode   X[M x 17408] W[5120x17408] and X[M x 5120] W[17408x5120], M in {1,4,16}, per-token scales
   fused    X[8192x5120], six GDN input projections with their own global scales
 
 Prints one JSON line.  `value` is GEMM flops of the whole step divided by the step time.
@@ -231,14 +231,23 @@ def cpu_baseline_prefill(p, sample_rows: int = 4096):
 
 
 def bench_decode(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: int = 8):
-    d = workloads.DECODE
+    """Per-token quantize + decode GEMM for M in {1, 4, 16} on two weight shapes: the MLP down
+    projection W[5120 x 17408] (K-split kernel) and the up projection W[17408 x 5120] (balanced
+    kernel), each with 8 distinct weight copies rotating so W never comes from the cache."""
+    out = {}
+    for label, d in (("down", workloads.DECODE), ("up", workloads.DECODE_UP)):
+        out[label] = _bench_decode_shape(nv, d, steps, warmup, settle_s, rotate)
+    return out
+
+
+def _bench_decode_shape(nv, d, steps: int, warmup: int, settle_s: float, rotate: int):
     dev = torch.device("cuda:0")
     w0 = torch.from_numpy(d.w()).to(dev).to(torch.bfloat16)
     ws = [nv.quantize(w0)]
-    for _ in range(rotate - 1):        # distinct copies: 8 x 56 MB defeats the 256 MB cache
+    for _ in range(rotate - 1):        # distinct copies: 8 x 50 MB defeats the 256 MB cache
         q = ws[0]
         ws.append(nv.NVFP4Tensor(q.codes.clone(), q.scales.clone(), q.global_scale.clone()))
-    out = {}
+    out = {"N": d.N, "K": d.K}
     for M in d.Ms:
         x = torch.from_numpy(d.x(M)).to(dev).to(torch.bfloat16)
         a = nv.quantize(x, "per_row")

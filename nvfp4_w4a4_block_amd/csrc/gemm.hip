@@ -1079,6 +1079,235 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(GemmArg
   decode_epilogue<GATES>(g, red, reinterpret_cast<float*>(lds), wave, lane, n0);
 }
 
+// ------------------------------------------------------------------ decode, balanced rows
+
+// M <= 16 tokens, K a multiple of 256, one launch in which every CU streams the same bytes:
+// workgroup b owns W rows [b R, b R + R) and all of K, R (at most 16 G) chosen by the host so
+// that the grid is a whole number of rounds over the CUs (68 rows per workgroup, one round,
+// for N = 17408 on 256 CUs).
+//
+// A 256-wide K stage holds the codes of the 16 G W rows and the 16 token rows as 1 KB chunks
+// of 8 rows x 128 B (whole lines; 16-byte piece p of row i in slot p ^ i), copied straight
+// from global memory into a ring of kDepth stages shared by the workgroup.  Wavefronts 0-3
+// issue the copies, the chunks of a stage shared out among them (a wavefront with fewer
+// chunks than the others copies chunk 0 again into a scratch slot, so each issues the same
+// number per stage; copying only the chunks that hold real rows measured slower).  The loop
+// runs in steps of kSteps stages: at the top of a step every copying wavefront waits for its
+// copies of the step's stages, the step's only barrier publishes them to all and frees the
+// slots of the previous step, which are refilled at once kDepth - kSteps stages ahead.  kSteps and kDepth grow as the stage shrinks (fewer row
+// groups), so every step and the bytes in flight stay large.  The scale bytes of all rows
+// over all of K are copied once, up front, in the same chunk layout (8 rows x 8 stages of
+// 16 B per chunk).
+//
+// Eight wavefronts, two per SIMD so that one's dequantization hides the other's waits:
+// wavefront w multiplies K elements [32 w, 32 w + 32) of every stage for all G row groups, one
+// 16x16x32 MFMA per group (lane group q supplies K elements 32 w + 8 q .. + 8, inside one
+// block, so one scale byte) with one dequantized token fragment shared by the groups.  The
+// eight partial tiles of a group are summed in a fixed order at the end.  Rows past the
+// workgroup's last row load that row and token rows past M load row M - 1; their outputs are
+// not stored.
+template <int G> struct DwCfg {
+  static constexpr int kChunks = 2 * G + 2;             // 1 KB chunks per stage: W rows, then tokens
+  static constexpr int kPerWave = (kChunks + 3) / 4;    // copies per copying wavefront per stage
+  static constexpr int kStageBytes = kChunks * 1024;
+  static constexpr int kSteps = G >= 3 ? 2 : 4;         // stages per barrier
+  static constexpr int kDepth = 4 * kSteps;             // stages in the ring
+  static constexpr int kScratch = kDepth * kStageBytes; // 1 KB target of padding copies
+  static constexpr int kScales = kScratch + 1024;       // scale chunks: block b, chunk c at (b kChunks + c) KB
+};
+constexpr int kDwMaxG = 5;
+constexpr int kDwThreads = 512;
+
+// LDS bytes of the balanced decode kernel for G row groups and K (0 if K does not fit).
+template <int G>
+int dw_lds_bytes_g(int64_t K) {
+  using C = DwCfg<G>;
+  const int64_t blocks = (K / 256 + 7) / 8;
+  const int64_t bytes = C::kScales + blocks * C::kChunks * 1024;
+  return bytes <= 160 * 1024 ? (int)bytes : 0;
+}
+inline int dw_lds_bytes(int G, int64_t K) {
+  switch (G) {
+    case 1: return dw_lds_bytes_g<1>(K);
+    case 2: return dw_lds_bytes_g<2>(K);
+    case 3: return dw_lds_bytes_g<3>(K);
+    case 4: return dw_lds_bytes_g<4>(K);
+    default: return dw_lds_bytes_g<5>(K);
+  }
+}
+
+// Copy chunk c (rows 8c .. 8c+7 of the stage's row list) of 256-wide stage t: lane l copies
+// 16-byte piece (l & 7) ^ (l >> 3) of row l >> 3 into slot l & 7 of that row.
+template <int G>
+__device__ __forceinline__ void dw_copy_codes(const GemmArgs& g, const uint8_t* wcb, const uint32_t (&row_off)[DwCfg<G>::kPerWave],
+                                              int wave, int lane, int t, uint8_t* lds) {
+  using C = DwCfg<G>;
+  const uint32_t piece = (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16) + (uint32_t)t * 128;
+  uint8_t* stage = lds + (t % C::kDepth) * C::kStageBytes;
+#pragma unroll
+  for (int i = 0; i < C::kPerWave; ++i) {
+    const int c = wave + 4 * i;
+    if (c < C::kChunks)
+      copy16_to_lds(c < 2 * G ? wcb : g.a_codes, row_off[i] + piece, stage + c * 1024);
+    else
+      copy16_to_lds(wcb, row_off[i] + piece, lds + C::kScratch);
+  }
+}
+
+// s_waitcnt for at most n stages of copies (n <= kDepth - 2 kSteps) still in flight.
+template <int G>
+__device__ __forceinline__ void dw_wait_stages(int n) {
+  using C = DwCfg<G>;
+  static_assert(C::kDepth - 2 * C::kSteps <= 8 && 8 * C::kPerWave <= 63, "wait cases");
+  switch (n) {
+    case 8: __builtin_amdgcn_s_waitcnt(vmcnt_imm(8 * C::kPerWave)); break;
+    case 7: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7 * C::kPerWave)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6 * C::kPerWave)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * C::kPerWave)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * C::kPerWave)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * C::kPerWave)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * C::kPerWave)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(1 * C::kPerWave)); break;
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+  }
+}
+
+template <int G, bool GATES>
+__global__ __launch_bounds__(kDwThreads) void gemm_decode_rows_kernel(GemmArgs g, int rows_per_wg) {
+  using C = DwCfg<G>;
+  constexpr int S = C::kSteps, D = C::kDepth;
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int rr = lane & 15, q = lane >> 4;
+  const int r0 = blockIdx.x * rows_per_wg;
+  const int rw = min(rows_per_wg, g.N - r0);             // rows of this workgroup (>= 1)
+  const uint32_t kb = (uint32_t)g.K / 2, ks = (uint32_t)g.K / 16;
+  const int nst = g.K / 256;
+  const uint8_t* wcb = g.w_codes + (size_t)r0 * kb;
+  const uint8_t* wsb = g.w_scales + (size_t)r0 * ks;
+
+  // Row of the stage's row list that lane l copies in chunk c: W row min(8c + l/8, rw - 1) of
+  // the workgroup, or token row min(8(c - 2G) + l/8, M - 1); chunks past the list copy row 0.
+  auto list_row = [&](int c, uint32_t pitch) -> uint32_t {
+    const int i = lane >> 3;
+    if (c < 2 * G) return (uint32_t)min(8 * c + i, rw - 1) * pitch;
+    if (c < C::kChunks) return (uint32_t)min(8 * (c - 2 * G) + i, g.M - 1) * pitch;
+    return 0u;
+  };
+  const bool copier = wave < 4;
+  uint32_t row_off[C::kPerWave];
+#pragma unroll
+  for (int i = 0; i < C::kPerWave; ++i) row_off[i] = list_row((wave & 3) + 4 * i, kb);
+
+  // Scale bytes, all stages: block b (stages 8b .. 8b+7), chunk c = rows 8c .. 8c+7, each
+  // row's 8 pieces of 16 B (one per stage) in the code chunks' slot order; pieces past the
+  // last stage repeat it.
+  {
+    const int nblk = (nst + 7) / 8;
+    const int p = (lane & 7) ^ (lane >> 3);
+    for (int e = wave; e < nblk * C::kChunks; e += 8) {
+      const int b = e / C::kChunks, c = e - b * C::kChunks;
+      const uint32_t off = list_row(c, ks) + (uint32_t)min(8 * b + p, nst - 1) * 16;
+      copy16_to_lds(c < 2 * G ? wsb : g.a_scales, off, lds + C::kScales + e * 1024);
+    }
+  }
+  if (copier) {
+    for (int t = 0; t < D - S && t < nst; ++t) dw_copy_codes<G>(g, wcb, row_off, wave, lane, t, lds);
+  } else {
+    // The loop's waits count stage copies, which these wavefronts do not issue: their scale
+    // copies must be complete before the first barrier.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+
+  // Where this lane reads: row rr & 7 of chunk 2j + rr/8 (W group j) or 2G + rr/8 (tokens),
+  // 4 bytes at byte 16 w + 4 q of the row's 128 (piece w), and scale byte 2w + q/2 of the
+  // stage's 16 (dword w/2).
+  const int ir = rr & 7, ch = rr >> 3;
+  const int code_off = ir * 128 + ((wave ^ ir) << 4) + 4 * q;
+  const int sc_off = 4 * (wave >> 1);
+  const int byte_sh = 8 * (2 * (wave & 1) + (q >> 1));
+  f32x4_t acc[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) acc[j] = f32x4_t{};
+
+  for (int t0 = 0; t0 < nst; t0 += S) {
+    // Stages t0 .. t0+S-1 must be complete; copies issued after them (up to stage
+    // t0 + D - S - 1, at most D - 2S stages) may still be in flight.
+    dw_wait_stages<G>(min(t0 + D - S - 1, nst - 1) - min(t0 + S - 1, nst - 1));
+    asm volatile("" ::: "memory");
+    __syncthreads();            // this step's stages copied by every wavefront; the last step's read by all
+    if (copier) {
+#pragma unroll
+      for (int u = 0; u < S; ++u)
+        if (t0 + D - S + u < nst) dw_copy_codes<G>(g, wcb, row_off, wave, lane, t0 + D - S + u, lds);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      const int t = t0 + u;
+      if (t < nst) {
+        const uint8_t* stage = lds + (t % D) * C::kStageBytes;
+        const uint8_t* sc = lds + C::kScales + (t >> 3) * C::kChunks * 1024 + ir * 128 + (((t & 7) ^ ir) << 4) + sc_off;
+        const uint32_t a = *reinterpret_cast<const uint32_t*>(stage + (2 * G + ch) * 1024 + code_off);
+        const uint32_t as = *reinterpret_cast<const uint32_t*>(sc + (2 * G + ch) * 1024);
+        const half8_t fa = dequant8_f16(a, scale_pair_f16((as >> byte_sh) & 0xFFu));
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(stage + (2 * j + ch) * 1024 + code_off);
+          const uint32_t ws = *reinterpret_cast<const uint32_t*>(sc + (2 * j + ch) * 1024);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, dequant8_f16(w, scale_pair_f16((ws >> byte_sh) & 0xFFu)),
+                                                          acc[j], 0, 0, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // Sum the eight wavefronts' tiles of each group in a fixed order, then scale and store.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  asm volatile("" ::: "memory");
+  __syncthreads();              // every wavefront is done with the ring
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(lds);
+#pragma unroll
+  for (int j = 0; j < G; ++j) red[(wave * G + j) * 64 + lane] = acc[j];
+  __syncthreads();
+  float* qy = reinterpret_cast<float*>(lds + 8 * G * 1024);   // 16 tokens x 16 G columns (NVFP4 out)
+  for (int j = wave; j < G; j += 8) {
+    // D[m][n] of a 16x16 tile sits in lane n + 16 (m / 4), register m % 4.
+    f32x4_t sum = red[j * 64 + lane];
+    for (int w = 1; w < 8; ++w) sum += red[(w * G + j) * 64 + lane];
+    const int nl = 16 * j + rr, n = r0 + nl;
+    const bool nv = nl < rw;
+    const float sw = nv ? g.w_globals[segment_of(n, g.seg)] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * q + i;
+      const bool ok = m < g.M && nv;
+      const float v = ok ? (sum[i] * g.a_global[g.a_per_row ? m : 0]) * sw : 0.0f;
+      if (g.q_out)
+        qy[m * (16 * G) + nl] = v;
+      else if (ok)
+        store_out(g, m, n, v);
+      if constexpr (GATES) {
+        if (ok && n >= g.gate_n0) store_gate(g, m, n, v);
+      }
+    }
+  }
+  if (g.q_out) {
+    __syncthreads();
+    const int t = (int)threadIdx.x;
+    if (t < 16 * G) {
+      const int m = t / G, j = t - m * G;
+      if (m < g.M && 16 * j < rw) {
+        float v[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = qy[m * (16 * G) + 16 * j + e];
+        store_block_nvfp4(g, m, r0 + 16 * j, v);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ plain kernel
 
 __device__ __forceinline__ float e2m1_value(uint32_t c) {
@@ -1173,6 +1402,65 @@ int tile_kernels_ready(int& cus) {
   return NVFP4_OK;
 }
 
+// Rows per workgroup of the balanced decode kernel: the fewest rounds over the CUs with at
+// most 16 kDwMaxG rows per workgroup, the rows then spread evenly over the workgroups of those
+// rounds (a multiple of 16 for NVFP4 output, whose 16-column blocks must not straddle
+// workgroups).  Returns the kernel's LDS bytes, 0 when K is too long for its LDS.
+int decode_rows_plan(int64_t N, int64_t K, int cus, bool blocks16, int& rows, int& groups) {
+  const int64_t cap = 16 * kDwMaxG;
+  const int64_t rounds = (N + cus * cap - 1) / (cus * cap);
+  int64_t r = (N + cus * rounds - 1) / (cus * rounds);
+  if (blocks16) r = (r + 15) / 16 * 16;
+  rows = (int)r;
+  groups = (int)((r + 15) / 16);
+  return dw_lds_bytes(groups, K);
+}
+
+template <int G>
+int set_decode_rows_lds() {
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_decode_rows_kernel<G, false>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess ||
+      hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_decode_rows_kernel<G, true>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+    return NVFP4_ERR_HIP;
+  return NVFP4_OK;
+}
+
+// Device set-up of the decode kernels (once per device): LDS limits and the CU count.
+int decode_kernels_ready(int& cus) {
+  static bool ready[64] = {};
+  static int cu_count[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return NVFP4_ERR_HIP;
+  if (!ready[dev]) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_decode_lds_kernel<false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kDlLds) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_decode_lds_kernel<true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kDlLds) != hipSuccess)
+      return NVFP4_ERR_HIP;
+    int st = set_decode_rows_lds<1>();
+    if (st == NVFP4_OK) st = set_decode_rows_lds<2>();
+    if (st == NVFP4_OK) st = set_decode_rows_lds<3>();
+    if (st == NVFP4_OK) st = set_decode_rows_lds<4>();
+    if (st == NVFP4_OK) st = set_decode_rows_lds<5>();
+    if (st != NVFP4_OK) return st;
+    if (hipDeviceGetAttribute(&cu_count[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return NVFP4_ERR_HIP;
+    ready[dev] = true;
+  }
+  cus = cu_count[dev];
+  return NVFP4_OK;
+}
+
+template <int G>
+void launch_decode_rows(const GemmArgs& g, bool gated, int rows, int lds_bytes, hipStream_t stream) {
+  const unsigned grid = (unsigned)((g.N + rows - 1) / rows);
+  if (gated)
+    gemm_decode_rows_kernel<G, true><<<grid, kDwThreads, lds_bytes, stream>>>(g, rows);
+  else
+    gemm_decode_rows_kernel<G, false><<<grid, kDwThreads, lds_bytes, stream>>>(g, rows);
+}
+
 // One 256 x 256 tile per CU at a time.  If the last round of tiles would fill at most half of
 // the CUs, enough whole tile columns move to 128 x 128 tiles to absorb it: workgroups
 // [0, big) take 256 x 256 tiles of columns [0, n_split), the other `small` 128 x 128 tiles.
@@ -1218,22 +1506,28 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
     const int64_t total = M * N;
     gemm_plain_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(g);
   } else if (M <= 16 && K % 256 == 0) {
-    static bool dl_attr[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return NVFP4_ERR_HIP;
-    if (!dl_attr[dev]) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_decode_lds_kernel<false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kDlLds) != hipSuccess ||
-          hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_decode_lds_kernel<true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kDlLds) != hipSuccess)
-        return NVFP4_ERR_HIP;
-      dl_attr[dev] = true;
+    int cus = 0;
+    const int st = decode_kernels_ready(cus);
+    if (st != NVFP4_OK) return st;
+    // Up to one round of 32-row workgroups the K-split kernel is the faster; past it, the
+    // balanced kernel avoids the partial last round.
+    int rows = 0, groups = 0;
+    const int lds_bytes = N > (int64_t)kDecodeRows * cus ? decode_rows_plan(N, K, cus, g.q_out != 0, rows, groups) : 0;
+    if (lds_bytes == 0) {
+      const unsigned grid = (unsigned)((N + kDecodeRows - 1) / kDecodeRows);
+      if (gated)
+        gemm_decode_lds_kernel<true><<<grid, kDecodeThreads, kDlLds, stream>>>(g);
+      else
+        gemm_decode_lds_kernel<false><<<grid, kDecodeThreads, kDlLds, stream>>>(g);
+    } else {
+      switch (groups) {
+        case 1: launch_decode_rows<1>(g, gated, rows, lds_bytes, stream); break;
+        case 2: launch_decode_rows<2>(g, gated, rows, lds_bytes, stream); break;
+        case 3: launch_decode_rows<3>(g, gated, rows, lds_bytes, stream); break;
+        case 4: launch_decode_rows<4>(g, gated, rows, lds_bytes, stream); break;
+        default: launch_decode_rows<5>(g, gated, rows, lds_bytes, stream); break;
+      }
     }
-    const unsigned grid = (unsigned)((N + kDecodeRows - 1) / kDecodeRows);
-    if (gated)
-      gemm_decode_lds_kernel<true><<<grid, kDecodeThreads, kDlLds, stream>>>(g);
-    else
-      gemm_decode_lds_kernel<false><<<grid, kDecodeThreads, kDlLds, stream>>>(g);
   } else if (M <= 16) {
     const unsigned grid = (unsigned)((N + kDecodeRows - 1) / kDecodeRows);
     if (gated)

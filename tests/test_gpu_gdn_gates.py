@@ -81,6 +81,14 @@ def test_decode_gates(M, K):
     _run(M, K, (64, 48, 48), seed=60 + M, a_mode="per_row")
 
 
+@pytest.mark.parametrize("M", [1, 16])
+def test_decode_gates_full_fused_gdn_width(M):
+    # The fused GDN projection's width (12384 columns) at decode: 49 rows per workgroup, four
+    # row groups, the gate columns spread over the last workgroups.
+    f = workloads.FUSED
+    _run(M, 1024, f.widths, seed=80 + M, a_mode="per_row")
+
+
 def test_plain_kernel_gates():
     # K not a multiple of 128: the plain kernel.
     _run(20, 144, (32, 24, 24), seed=70)

@@ -55,6 +55,29 @@ def test_decode(M, a_mode):
     assert_gemm_close(y, Y, T, f"decode M={M}")
 
 
+@pytest.fixture(scope="module")
+def decode_up_weight():
+    """The MLP up projection's weight at decode (17408 x 5120), quantized on the GPU and by the
+    oracle once for the module."""
+    wg = to_gpu(workloads.DECODE_UP.w())
+    q = nv().quantize(wg)
+    ow = ref.quantize(wg.float().cpu().numpy())
+    assert_quant_equal(q, ow, what="W")
+    return q, ow
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_decode_up_projection(M, decode_up_weight):
+    # The balanced decode kernel at its full shape: 68 W rows per workgroup, one round.
+    q, ow = decode_up_weight
+    xg = to_gpu(workloads.DECODE_UP.x(M))
+    a = nv().quantize(xg, "per_row")
+    oa = ref.quantize(xg.float().cpu().numpy(), ref.PER_ROW)
+    assert_quant_equal(a, oa, what="A")
+    Y, T = ref.gemm(oa, ow)
+    assert_gemm_close(nv().gemm(a, q, torch.bfloat16), Y, T, f"decode up M={M}")
+
+
 def _fused_weights(f, K=None, rows=None):
     segs_gpu, segs_ora = [], []
     for i in range(len(f.widths)):
@@ -160,6 +183,48 @@ def test_decode_ragged(M, N, K, a_mode):
     for dt in (torch.float32, torch.bfloat16):
         y = nv().gemm(a, q, dt)
         assert_gemm_close(y, Y, T, f"decode {M}x{N}x{K} {a_mode} {dt}")
+
+
+# Balanced decode kernel (M <= 16, K a multiple of 256, N past one round of 32-row workgroups,
+# 8192 on 256 CUs): rows per workgroup chosen so that the grid is a whole number of rounds over
+# the CUs.  Shapes hit 3 to 5 row groups per workgroup, partial last groups and chunks, one or
+# two token chunks, two rounds, fewer stages than the copy ring holds, scale blocks cut short,
+# and the LDS limit (K = 10240 still fits five row groups, 10496 goes to the other kernel);
+# below the cut, the K-split kernel.
+@pytest.mark.parametrize("M,N,K", [(1, 8455, 256), (5, 8455, 512), (16, 12384, 1792), (9, 17408, 2304),
+                                   (16, 20481, 768), (8, 16700, 10240), (1, 16700, 10496), (3, 5120, 8448),
+                                   (2, 5120, 17408), (16, 300, 1280)])
+def test_decode_balanced_rows(M, N, K):
+    # Seeded NVFP4 operands built directly (random codes, block scales over 2^-5 .. 2^1, a
+    # global scale per token row), the same bytes for the GPU and the oracle.
+    g = np.random.default_rng(M * N + K)
+
+    def operand(R, per_row):
+        codes = g.integers(0, 256, (R, K // 2), dtype=np.uint8)
+        scales = g.integers(0x10, 0x40, (R, K // 16), dtype=np.uint8)
+        gs = g.uniform(0.5, 2.0, R if per_row else 1).astype(np.float32)
+        return ref.NVFP4(codes, scales, gs, R, K)
+
+    oa, ow = operand(M, True), operand(N, False)
+    Y, T = ref.gemm(oa, ow)
+    y = nv().gemm(to_device(oa), to_device(ow), torch.float32)
+    assert_gemm_close(y, Y, T, f"decode {M}x{N}x{K}")
+
+
+def test_decode_balanced_rows_segments():
+    M, K, widths = 4, 2048, (4000, 48, 3000)
+    xg = to_gpu(workloads.activation(36, 0, M, K))
+    a = nv().quantize(xg, "per_row")
+    oa = ref.quantize(xg.float().cpu().numpy(), ref.PER_ROW)
+    gq, oq = [], []
+    for i, n in enumerate(widths):
+        wg = to_gpu(workloads.weight(36, 10 + i, n, K, sigma=0.02 * (i + 1)))
+        gq.append(nv().quantize(wg))
+        oq.append(ref.quantize(wg.float().cpu().numpy()))
+    y = nv().gemm_fused_segments(a, torch.cat([q.codes for q in gq]), torch.cat([q.scales for q in gq]), widths,
+                                 torch.cat([q.global_scale for q in gq]), torch.bfloat16)
+    Y, T = ref.fused_segments(oa, oq)
+    assert_gemm_close(y, Y, T, "decode fused, balanced rows")
 
 
 def test_decode_fused_segments():

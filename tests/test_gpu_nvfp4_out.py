@@ -77,7 +77,7 @@ def test_prefill_full_shape_sampled_rows():
 
 
 @pytest.mark.parametrize("M,K,widths", [(1, 2048, (96,)), (7, 384, (48, 48)), (16, 4096, (1024,)),
-                                        (16, 640, (32, 16))])
+                                        (16, 640, (32, 16)), (16, 1024, (12288,)), (3, 512, (4096, 1024, 3072))])
 @pytest.mark.parametrize("a_mode", ["per_tensor", "per_row"])
 def test_decode_path(M, K, widths, a_mode):
     _check(M, K, widths, a_mode=a_mode)

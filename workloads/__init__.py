@@ -33,6 +33,7 @@ __all__ = [
     "TINY",
     "PREFILL",
     "DECODE",
+    "DECODE_UP",
     "FUSED",
     "SWEEP",
     "sweep_launches",
@@ -146,7 +147,8 @@ class Prefill:
 
 @dataclass(frozen=True)
 class Decode:
-    """Decode down-projection: X[M x 17408] bf16 with M in {1,4,16}; W[5120x17408]."""
+    """Decode down-projection: X[M x 17408] bf16 with M in {1,4,16}; W[5120x17408].  The same
+    class with N and K swapped is the MLP up projection at decode."""
     name: str = "decode"
     seed: int = 2
     Ms: tuple[int, ...] = (1, 4, 16)
@@ -257,5 +259,6 @@ def sweep_launches(sw: Sweep | None = None) -> list[Launch]:
 TINY = Tiny()
 PREFILL = Prefill()
 DECODE = Decode()
+DECODE_UP = Decode(name="decode_up", seed=4, N=17408, K=5120)
 FUSED = Fused()
 SWEEP = Sweep()
