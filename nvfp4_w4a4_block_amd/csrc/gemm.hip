@@ -840,14 +840,15 @@ __device__ __forceinline__ void decode_chunk_mma(const DecodeChunk& d, f32x4_t& 
 }
 
 // Epilogue of the decode kernels: the 4 wavefronts' 16x16 tiles (red[(wave * 2 + group) * 64 +
-// lane]) are summed in a fixed order, scaled (y = (sum * s_gA[m]) * s_gW[seg(n)]) and stored; for
+// lane]) are summed in a fixed order, scaled (y = (sum * s_gA[m]) * s_gW[seg(n)]) and stored for
+// the workgroup's rows n < n_end; for
 // NVFP4 output the scaled values of the 16 x 32 tile go through qy (16 x 32 floats of LDS) and
 // each of the first 32 threads encodes one 16-column block.  GATES: gate columns also get
 // their gates from the same fp32 value.
 constexpr int kDecodeRowsE = 32;
 template <bool GATES>
 __device__ __forceinline__ void decode_epilogue(const GemmArgs& g, const f32x4_t* red, float* qy, int wave, int lane,
-                                                int n0) {
+                                                int n0, int n_end) {
   const int rr = lane & 15, grp = lane >> 4;
   __syncthreads();
   if (wave < 2) {
@@ -855,17 +856,17 @@ __device__ __forceinline__ void decode_epilogue(const GemmArgs& g, const f32x4_t
     f32x4_t sum = f32x4_t{};
     for (int w = 0; w < 4; ++w) sum += red[(w * 2 + wave) * 64 + lane];
     const int n = n0 + 16 * wave + rr;
-    const float sw = n < g.N ? g.w_globals[segment_of(n, g.seg)] : 0.0f;
+    const float sw = n < n_end ? g.w_globals[segment_of(n, g.seg)] : 0.0f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int m = 4 * grp + q;
-      const float v = m < g.M && n < g.N ? (sum[q] * g.a_global[g.a_per_row ? m : 0]) * sw : 0.0f;
+      const float v = m < g.M && n < n_end ? (sum[q] * g.a_global[g.a_per_row ? m : 0]) * sw : 0.0f;
       if (g.q_out)
         qy[m * kDecodeRowsE + 16 * wave + rr] = v;
-      else if (m < g.M && n < g.N)
+      else if (m < g.M && n < n_end)
         store_out(g, m, n, v);
       if constexpr (GATES) {
-        if (m < g.M && n < g.N && n >= g.gate_n0) store_gate(g, m, n, v);
+        if (m < g.M && n < n_end && n >= g.gate_n0) store_gate(g, m, n, v);
       }
     }
   }
@@ -874,7 +875,7 @@ __device__ __forceinline__ void decode_epilogue(const GemmArgs& g, const f32x4_t
     const int t = (int)threadIdx.x;
     if (t < 32) {
       const int m = t >> 1, n = n0 + 16 * (t & 1);
-      if (m < g.M && n < g.N) {
+      if (m < g.M && n < n_end) {
         float v[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) v[e] = qy[m * kDecodeRowsE + 16 * (t & 1) + e];
@@ -968,7 +969,7 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(GemmArgs g)
   }
   red[(wave * 2 + 0) * 64 + lane] = acc0;
   red[(wave * 2 + 1) * 64 + lane] = acc1;
-  decode_epilogue<GATES>(g, red, qy, wave, lane, n0);
+  decode_epilogue<GATES>(g, red, qy, wave, lane, n0, g.N);
 }
 
 // M <= 16 tokens, K a multiple of 256: the same work as gemm_decode_kernel, but every load
@@ -1000,11 +1001,12 @@ __device__ __forceinline__ void dl_copy_chunk(const uint8_t* base, uint32_t row_
 }
 
 template <bool GATES>
-__global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(GemmArgs g) {
+__global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(GemmArgs g, int rows_per_wg) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int rr = lane & 15, grp = lane >> 4, i8 = lane >> 3;
-  const int n0 = blockIdx.x * kDecodeRows;
+  const int n0 = blockIdx.x * rows_per_wg;              // rows [n0, n_end), at most 32
+  const int n_end = min(n0 + rows_per_wg, g.N);
   const uint32_t kb = (uint32_t)g.K / 2, ks = (uint32_t)g.K / 16;
   const int nst = g.K / 256;
   const int s0 = wave * nst / kDecodeWaves, cnt = (wave + 1) * nst / kDecodeWaves - s0;
@@ -1014,7 +1016,7 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(GemmArg
   uint32_t row_codes[kDlChunks], row_scales[kDlChunks];
 #pragma unroll
   for (int c = 0; c < kDlChunks; ++c) {
-    const int r = c < 4 ? min(8 * c + i8, g.N - 1 - n0) : min(8 * (c - 4) + i8, g.M - 1);
+    const int r = c < 4 ? min(8 * c + i8, n_end - 1 - n0) : min(8 * (c - 4) + i8, g.M - 1);
     row_codes[c] = (uint32_t)r * kb;
     row_scales[c] = (uint32_t)r * ks;
   }
@@ -1076,7 +1078,7 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(GemmArg
   f32x4_t* red = reinterpret_cast<f32x4_t*>(lds + kDlRedOffset);
   red[(wave * 2 + 0) * 64 + lane] = acc0;
   red[(wave * 2 + 1) * 64 + lane] = acc1;
-  decode_epilogue<GATES>(g, red, reinterpret_cast<float*>(lds), wave, lane, n0);
+  decode_epilogue<GATES>(g, red, reinterpret_cast<float*>(lds), wave, lane, n0, n_end);
 }
 
 // ------------------------------------------------------------------ decode, balanced rows
@@ -1514,11 +1516,15 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
     int rows = 0, groups = 0;
     const int lds_bytes = N > (int64_t)kDecodeRows * cus ? decode_rows_plan(N, K, cus, g.q_out != 0, rows, groups) : 0;
     if (lds_bytes == 0) {
-      const unsigned grid = (unsigned)((N + kDecodeRows - 1) / kDecodeRows);
+      // Rows per workgroup: about N / CUs, so that every CU takes a share (16 to 32; 32 for
+      // NVFP4 output, whose 16-column blocks must not straddle workgroups).
+      const int64_t share = (N + cus - 1) / cus;
+      const int r = g.q_out ? kDecodeRows : (int)std::min<int64_t>(kDecodeRows, std::max<int64_t>(16, share));
+      const unsigned grid = (unsigned)((N + r - 1) / r);
       if (gated)
-        gemm_decode_lds_kernel<true><<<grid, kDecodeThreads, kDlLds, stream>>>(g);
+        gemm_decode_lds_kernel<true><<<grid, kDecodeThreads, kDlLds, stream>>>(g, r);
       else
-        gemm_decode_lds_kernel<false><<<grid, kDecodeThreads, kDlLds, stream>>>(g);
+        gemm_decode_lds_kernel<false><<<grid, kDecodeThreads, kDlLds, stream>>>(g, r);
     } else {
       switch (groups) {
         case 1: launch_decode_rows<1>(g, gated, rows, lds_bytes, stream); break;

@@ -171,9 +171,11 @@ def test_ragged_shapes(M, N, K, a_mode):
 
 # Decode path (M <= 16, K a multiple of 128): odd chunk counts (a last 128-wide chunk after
 # the 256-wide stages; K = 128 has no stage at all), per-wave stage splits of unequal length,
-# N not a multiple of the 32-row workgroup, N = 1.
+# N not a multiple of the workgroup's rows (17 and 32 rows per workgroup for N = 4100 and
+# 7990 on 256 CUs, a last workgroup of 3 and 22 rows), N = 1.
 @pytest.mark.parametrize("M,N,K", [(3, 100, 384), (16, 33, 128), (7, 1, 640), (1, 4097, 1152),
-                                   (16, 64, 2048), (2, 96, 2304), (16, 200, 4224)])
+                                   (16, 64, 2048), (2, 96, 2304), (16, 200, 4224), (4, 4100, 512),
+                                   (11, 7990, 1024)])
 @pytest.mark.parametrize("a_mode", ["per_tensor", "per_row"])
 def test_decode_ragged(M, N, K, a_mode):
     x = workloads.activation(33, M, M, K, outlier_frac=0.02)
