@@ -22,6 +22,7 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWideThreads = 1024;       // per-row workgroups when there are fewer rows than CUs
 constexpr int kMaxPartials = 1024;        // pass-1 workgroups (4 partials per pass-2 thread)
 
 // 16 B of input as fp32 values.
@@ -62,16 +63,17 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
-// Workgroup max of one value per thread; the result is valid in every thread.
+// Workgroup max of one value per thread (NT threads); the result is valid in every thread.
+template <int NT = kThreads>
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
-  __shared__ uint32_t red[kThreads / 64];
+  __shared__ uint32_t red[NT / 64];
   v = wave_max_u32(v);
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[wave] = v;
   __syncthreads();
   uint32_t r = red[0];
 #pragma unroll
-  for (int i = 1; i < kThreads / 64; ++i) r = max(r, red[i]);
+  for (int i = 1; i < NT / 64; ++i) r = max(r, red[i]);
   __syncthreads();
   return r;
 }
@@ -134,10 +136,12 @@ __global__ __launch_bounds__(kThreads) void row_scale_kernel(const T* __restrict
   }
 }
 
-// Per-row mode in one pass: one workgroup per row (strided over rows) keeps the row's blocks
-// in registers (up to MAXB per thread), reduces the row max, writes s_g[r] and encodes.
-template <typename T, int MAXB>
-__global__ __launch_bounds__(kThreads) void row_quant_kernel(const T* __restrict__ x, int64_t rows, uint32_t bpr,
+// Per-row mode in one pass: one workgroup of NT threads per row (strided over rows) keeps the
+// row's blocks in registers (up to MAXB per thread), reduces the row max, writes s_g[r] and
+// encodes.  Few rows (decode) take 1024-thread workgroups, so each thread has one or two
+// blocks to load and encode; many rows take 256-thread workgroups, several per CU.
+template <typename T, int MAXB, int NT = kThreads>
+__global__ __launch_bounds__(NT) void row_quant_kernel(const T* __restrict__ x, int64_t rows, uint32_t bpr,
                                                               int64_t ldx, uint8_t* __restrict__ codes,
                                                               uint8_t* __restrict__ scales,
                                                               float* __restrict__ sg_out) {
@@ -148,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void row_quant_kernel(const T* __restrict
     uint32_t m = 0;
 #pragma unroll
     for (int j = 0; j < MAXB; ++j) {
-      const uint32_t b = threadIdx.x + j * kThreads;
+      const uint32_t b = threadIdx.x + j * NT;
       if (b < bpr) {
         const uint4* p = reinterpret_cast<const uint4*>(row + (int64_t)b * 16);
 #pragma unroll
@@ -158,12 +162,12 @@ __global__ __launch_bounds__(kThreads) void row_quant_kernel(const T* __restrict
         }
       }
     }
-    m = block_max_u32(m);
+    m = block_max_u32<NT>(m);
     const float sg = __uint_as_float(m) / kGlobalDivisor;
     if (threadIdx.x == 0) sg_out[r] = sg;
 #pragma unroll
     for (int j = 0; j < MAXB; ++j) {
-      const uint32_t b = threadIdx.x + j * kThreads;
+      const uint32_t b = threadIdx.x + j * NT;
       if (b < bpr) {
         float v[16];
 #pragma unroll
@@ -325,6 +329,15 @@ int launch_typed(const T* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* c
     case kPerRow: {
       const int g = (int)(rows < 8 * cus ? rows : 8 * cus);
       constexpr int kMaxB = sizeof(T) == 2 ? 8 : 4;     // blocks per thread held in registers
+      if (rows < cus && bpr <= (uint32_t)(2 * kWideThreads)) {
+        if (bpr <= (uint32_t)kWideThreads)
+          row_quant_kernel<T, 1, kWideThreads><<<g, kWideThreads, 0, stream>>>(x, rows, bpr, ldx, codes, scales,
+                                                                                  global_scale);
+        else
+          row_quant_kernel<T, 2, kWideThreads><<<g, kWideThreads, 0, stream>>>(x, rows, bpr, ldx, codes, scales,
+                                                                                  global_scale);
+        break;
+      }
       if (bpr <= (uint32_t)(kMaxB * kThreads)) {
         if (bpr <= (uint32_t)(2 * kThreads))
           row_quant_kernel<T, 2><<<g, kThreads, 0, stream>>>(x, rows, bpr, ldx, codes, scales, global_scale);
