@@ -67,6 +67,28 @@ def test_graph_decode_per_row():
     _replay_and_compare(g, x, M, K, (a.codes, a.global_scale, y), eager)
 
 
+def test_graph_decode_balanced_rows():
+    # N past one round of 32-row workgroups (8192 on 256 CUs): the balanced decode kernel,
+    # with its shared LDS ring and per-step barriers, under capture.
+    M, N, K = 8, 9000, 1024
+    w = nv().quantize(to_gpu(workloads.weight(203, 1, N, K)))
+    x = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+    _fill(x, 299, M, K)
+    a = nv().quantize(x, "per_row")
+    y = nv().gemm(a, w, torch.bfloat16)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        nv().quantize(x, "per_row", out=a)
+        nv().gemm(a, w, torch.bfloat16, out=y)
+
+    def eager():
+        ae = nv().quantize(x, "per_row")
+        return ae.codes, ae.global_scale, nv().gemm(ae, w, torch.bfloat16)
+
+    _replay_and_compare(g, x, M, K, (a.codes, a.global_scale, y), eager)
+
+
 def test_graph_fp8_kv_and_mxfp4():
     M, N, K = 256, 512, 512
     scale = torch.tensor([0.05], dtype=torch.float32, device=DEV)
