@@ -972,14 +972,15 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(GemmArgs g)
   decode_epilogue<GATES>(g, red, qy, wave, lane, n0, g.N);
 }
 
-// M <= 16 tokens, K a multiple of 256: the same work as gemm_decode_kernel, but every load
-// is a whole 128-byte line copied straight into LDS (8 rows x 128 B per wavefront
-// instruction), which moves the same bytes with a third of the memory requests of the
-// register loads (16 rows x 64 B, and 16-byte scale pieces).  Each wavefront owns a private
-// LDS region: a ring of kDlDepth stages (codes of the 32 W rows and 16 token rows of one
-// 256-wide K stage) and two blocks of scale bytes (8 stages each); it waits for its own
-// copies with explicit counts, so no barrier is needed until the final reduction.  Inside a
-// 1 KB chunk of 8 rows, 16-byte piece p of row i sits in slot p ^ i.
+// M <= 16 tokens, K a multiple of 256: the work of gemm_decode_kernel for a workgroup of
+// rows_per_wg <= 32 W rows (rows past the workgroup's last row load that row, their outputs
+// are not stored), but every load is a whole 128-byte line copied straight into LDS (8 rows x
+// 128 B per wavefront instruction), which moves the same bytes with a third of the memory
+// requests of the register loads (16 rows x 64 B, and 16-byte scale pieces).  Each wavefront
+// owns a private LDS region: a ring of kDlDepth stages (codes of the 32-row W list and 16
+// token rows of one 256-wide K stage) and two blocks of scale bytes (8 stages each); it waits
+// for its own copies with explicit counts, so no barrier is needed until the final
+// reduction.  Inside a 1 KB chunk of 8 rows, 16-byte piece p of row i sits in slot p ^ i.
 constexpr int kDlDepth = 4;                         // 256-wide stages in flight per wavefront
 constexpr int kDlChunks = 6;                        // 1 KB chunks: W rows 0-31, then token rows 0-15
 constexpr int kDlStageBytes = kDlChunks * 1024;     // codes of one stage
