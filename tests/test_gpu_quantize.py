@@ -42,6 +42,17 @@ def test_decode_per_token_activations(M):
     _check(x, "per_tensor", what=f"decode x M={M} per_tensor")
 
 
+# Per-row mode routes by the blocks per row (bpr) when rows are fewer than the CUs: 1024-thread
+# workgroups holding one block per thread (bpr <= 1024) or two (<= 2048); past that the
+# 256-thread kernel (bf16 up to 2048 blocks per row, fp32 up to 1024) or the row-scale +
+# encode pair.  Each side of every boundary, both input types.
+@pytest.mark.parametrize("bpr", [1024, 1025, 2048, 2049, 4100])
+@pytest.mark.parametrize("bf16", [True, False])
+def test_per_row_block_count_routes(bpr, bf16):
+    x = workloads.activation(37, bpr, 3, 16 * bpr, outlier_frac=0.01, outlier_gain=30.0)
+    _check(x, "per_row", bf16=bf16, what=f"per_row 3 x {16 * bpr} {'bf16' if bf16 else 'fp32'}")
+
+
 def test_decode_weights_full():
     _check(workloads.DECODE.w(), what="decode w 5120x17408")
 
