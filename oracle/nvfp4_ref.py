@@ -81,6 +81,17 @@ instructions take; its definition here follows that published specification):
       the NVFP4 code.  A block of zeros gets scale byte 0 and magnitude 0.
   R17 The MXFP4 GEMM is the same contraction as R8's with the MXFP4 values
       E2M1 * 2^(byte - 127) * s_g.
+
+Gated MLP input projection (the quantized feed-forward linears of the 27B hybrid model: paper
+abstract, "all 496 linear layers"; "Why Gated DeltaNet Survives 4-Bit Quantization"
+(kipquest), "The deep dive": W4A4 on every linear, feed-forward layers included).  The pages
+do not name the MLP's activation:
+  R18 The MLP is gated with SiLU (SwiGLU, the Qwen family's feed-forward block): the gate and
+      up projections are two segments of one fused module, each with its own global scale,
+      and the hidden activation is h = silu(y_gate) * y_up, silu(y) = y * sigmoid(y), taken
+      from the GEMM's float32 outputs (global scales applied) before any output rounding.
+      When h feeds the next linear (the down projection) it is encoded as NVFP4 under a
+      given global scale, each 16-element block exactly as ``quantize`` in GIVEN mode.
 """
 from __future__ import annotations
 
@@ -364,6 +375,25 @@ def fused_gdn_gates(a: NVFP4, segments: list[NVFP4], a_log, dt_bias, a_rows=None
     N = Y.shape[1]
     g, beta = gdn_gates(Y[:, N - 2 * H:N - H], Y[:, N - H:], a_log, dt_bias)
     return Y, T, g, beta
+
+
+# ------------------------------------------------------------------------------ SwiGLU MLP input
+
+def silu(y) -> np.ndarray:
+    """y * sigmoid(y) in float64 (R18), with the overflow-free sigmoid above."""
+    y = np.asarray(y, dtype=F64)
+    return y * sigmoid(y)
+
+
+def swiglu_mlp(a: NVFP4, gate: NVFP4, up: NVFP4, a_rows=None):
+    """The gated MLP input projection (R18): Y_g = A^ . G^T and Y_u = A^ . U^T, each weight
+    dequantized under its own global scale, and H = silu(Y_g) * Y_u, all float64.  Returns
+    (H, Y_g, T_g, Y_u, T_u), the T being ``gemm``'s tolerance scales of the two products."""
+    if gate.rows != up.rows:
+        raise ValueError("the gate and up projections must have the same width")
+    yg, tg = gemm(a, gate, a_rows)
+    yu, tu = gemm(a, up, a_rows)
+    return silu(yg) * yu, yg, tg, yu, tu
 
 
 # ------------------------------------------------------------------------------ MXFP4 (lossy)
