@@ -237,6 +237,53 @@ int nvfp4_mxfp4_gemm(int64_t M, int64_t K,
                      void* y, int y_dtype, int64_t ldy, void* stream);
 
 /*
+ * Interleave the gate and up projections of a gated (SwiGLU) MLP into the weight layout
+ * nvfp4_gemm_swiglu takes: rows 32p .. 32p+15 of w are gate rows 16p .. 16p+15 and rows
+ * 32p+16 .. 32p+31 the up rows 16p .. 16p+15 (codes and scale bytes alike), so that each
+ * 32-row group holds both projections of 16 hidden units.  A one-time weight preparation (a
+ * pure row permutation, stream-ordered device-to-device copies); the two projections keep
+ * their own global scales, passed to nvfp4_gemm_swiglu as {gate, up}.
+ *   F > 0 and a multiple of 16 (hidden width); K > 0 and a multiple of 16.
+ *   gate_codes, up_codes    [F, K/2];  gate_scales, up_scales [F, K/16]   (device, contiguous).
+ *   w_codes  out [2F, K/2];  w_scales out [2F, K/16]  (device, contiguous; must not overlap
+ *   the inputs).
+ */
+int nvfp4_interleave_gate_up(int64_t F, int64_t K,
+                             const uint8_t* gate_codes, const uint8_t* gate_scales,
+                             const uint8_t* up_codes, const uint8_t* up_scales,
+                             uint8_t* w_codes, uint8_t* w_scales, void* stream);
+
+/*
+ * The gated MLP input projection in one launch: the fused gate+up GEMM of the quantized
+ * feed-forward block (paper abstract: NVFP4 W4A4 on all linear layers; "Why Gated DeltaNet
+ * Survives 4-Bit Quantization", "The deep dive") with its SwiGLU activation and, optionally,
+ * the NVFP4 encoding of the result for the down projection.  The pages do not name the MLP's
+ * activation; this is the gated SiLU (SwiGLU) block of the Qwen family:
+ *   y_gate[m, j], y_up[m, j] = the fp32 GEMM outputs (acc * a_global[m or 0]) * w_globals[0
+ *   or 1] of hidden unit j, as nvfp4_gemm_fused_segments computes them for the segments
+ *   [gate, up];
+ *   h[m, j] = silu(y_gate) * y_up,  silu(y) = y * sigmoid(y) = y / (1 + e^-y)  (fp32).
+ * h is stored as fp32 or bf16 (round to nearest even) when h is given, and as NVFP4 when
+ * h_codes is given: each 16-element block of a row encoded exactly as nvfp4_quantize in
+ * NVFP4_SCALE_GIVEN mode encodes it under h_global[0] (a calibrated, static scale).  At least
+ * one of the two outputs is required.
+ *   F > 0, a multiple of 16 (hidden width); K a multiple of 128, and for M > 16 a multiple of
+ *   256 below 2^24 (other shapes: NVFP4_ERR_UNSUPPORTED); M * F < 2^31.
+ *   w_codes [2F, K/2], w_scales [2F, K/16]: the interleaved layout of nvfp4_interleave_gate_up.
+ *   w_globals device [2] = {gate, up}.
+ *   h       out [M, F] of h_dtype, row pitch ldh >= F elements, or NULL.
+ *   h_global device [1], finite and > 0; h_codes out [M, F/2], h_scales out [M, F/16], both
+ *   16-byte aligned; all three NULL when no NVFP4 output is wanted.
+ *   Other arguments as in nvfp4_gemm.
+ */
+int nvfp4_gemm_swiglu(int64_t M, int64_t F, int64_t K,
+                      const uint8_t* a_codes, const uint8_t* a_scales,
+                      const float* a_global, int a_global_per_row,
+                      const uint8_t* w_codes, const uint8_t* w_scales, const float* w_globals,
+                      void* h, int h_dtype, int64_t ldh,
+                      const float* h_global, uint8_t* h_codes, uint8_t* h_scales, void* stream);
+
+/*
  * FP8 key-value cache codec with a calibrated per-tensor scale (the pages' second serving
  * finding: calibrated FP8 KV-cache scales are performance-free -- paper abstract;
  * "Quantizing All Layers Reveals Recurrent Memory Is Robust", "The Calibrated Cache That

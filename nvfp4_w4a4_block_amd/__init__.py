@@ -21,6 +21,11 @@ Entry points (same names as the C ABI):
   to_mxfp4(a) / mxfp4_gemm(a_mx, w_codes, w_scales, widths, w_globals, out_dtype)
                                          -> lossy MXFP4 re-encoding and the GEMM on gfx950's
                                             scaled FP4 MFMA
+  interleave_gate_up(gate, up)           -> (w_codes, w_scales): gate and up projections of a
+                                            gated MLP in 16-row interleaved groups
+  gemm_swiglu(a, w_codes, w_scales, w_globals, h_dtype, h_global)
+                                         -> (h, h as NVFP4): the fused gate+up GEMM with its
+                                            SwiGLU activation, h = silu(gate) * up
 """
 from __future__ import annotations
 
@@ -33,7 +38,7 @@ import torch
 
 __all__ = [
     "NVFP4Tensor", "NVFP4Error", "quantize", "gemm", "gemm_fused_segments", "gemm_nvfp4_out", "gemm_fused_gdn_gates", "MXFP4Tensor", "to_mxfp4", "mxfp4_gemm",
-    "fp8_kv_quantize", "fp8_kv_dequantize",
+    "fp8_kv_quantize", "fp8_kv_dequantize", "interleave_gate_up", "gemm_swiglu",
     "library_path", "lib",
     "PER_TENSOR", "PER_ROW", "GIVEN", "MAX_SEGMENTS", "EXPORTED_SYMBOLS",
 ]
@@ -49,7 +54,7 @@ EXPORTED_SYMBOLS = (
     "nvfp4_quantize", "nvfp4_quantize_workspace_size", "nvfp4_gemm", "nvfp4_gemm_fused_segments",
     "nvfp4_gemm_nvfp4_out", "nvfp4_gemm_fused_gdn_gates", "nvfp4_to_mxfp4", "nvfp4_mxfp4_gemm",
     "nvfp4_gemm_workspace_size", "nvfp4_fp8_kv_quantize", "nvfp4_fp8_kv_dequantize",
-    "nvfp4_status_string", "nvfp4_version",
+    "nvfp4_interleave_gate_up", "nvfp4_gemm_swiglu", "nvfp4_status_string", "nvfp4_version",
 )
 
 
@@ -83,6 +88,10 @@ def _load() -> ctypes.CDLL:
     L.nvfp4_fp8_kv_quantize.restype = i32
     L.nvfp4_fp8_kv_dequantize.argtypes = [p, i64, p, p, i32, p]
     L.nvfp4_fp8_kv_dequantize.restype = i32
+    L.nvfp4_interleave_gate_up.argtypes = [i64, i64, p, p, p, p, p, p, p]
+    L.nvfp4_interleave_gate_up.restype = i32
+    L.nvfp4_gemm_swiglu.argtypes = [i64, i64, i64, p, p, p, i32, p, p, p, p, i32, i64, p, p, p, p]
+    L.nvfp4_gemm_swiglu.restype = i32
     L.nvfp4_gemm_workspace_size.argtypes = [i64, i64, i64]
     L.nvfp4_gemm_workspace_size.restype = sz
     L.nvfp4_status_string.argtypes = [i32]
@@ -334,6 +343,56 @@ def mxfp4_gemm(a: MXFP4Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, se
                               _ptr(y), _y_dtype(out_dtype), y.stride(0) if M > 0 else N, _stream(dev))
     _check(st, "nvfp4_mxfp4_gemm")
     return y
+
+
+def interleave_gate_up(gate: NVFP4Tensor, up: NVFP4Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """The weight layout gemm_swiglu takes: rows 32p .. 32p+15 are gate rows 16p .. 16p+15,
+    rows 32p+16 .. 32p+31 the up rows 16p .. 16p+15.  Returns (codes [2F, K/2], scales
+    [2F, K/16]); the global scales stay the projections' own (pass them as {gate, up})."""
+    F, K = gate.rows, gate.cols
+    _require(up.rows == F and up.cols == K, "gate and up must have the same shape")
+    for t in (gate.codes, gate.scales, up.codes, up.scales):
+        _require(t.is_cuda and t.is_contiguous(), "contiguous GPU NVFP4 tensors")
+    dev = gate.codes.device
+    w_codes = torch.empty((2 * F, K // 2), dtype=torch.uint8, device=dev)
+    w_scales = torch.empty((2 * F, K // 16), dtype=torch.uint8, device=dev)
+    st = lib.nvfp4_interleave_gate_up(F, K, _ptr(gate.codes), _ptr(gate.scales), _ptr(up.codes), _ptr(up.scales),
+                                      _ptr(w_codes), _ptr(w_scales), _stream(dev))
+    _check(st, "nvfp4_interleave_gate_up")
+    return w_codes, w_scales
+
+
+def gemm_swiglu(a: NVFP4Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, w_globals: torch.Tensor,
+                h_dtype: torch.dtype | None = torch.bfloat16, h_global: torch.Tensor | None = None,
+                out: torch.Tensor | None = None,
+                q_out: NVFP4Tensor | None = None) -> tuple[torch.Tensor | None, NVFP4Tensor | None]:
+    """Gated MLP input projection in one launch: h = silu(A . Wg^T) * (A . Wu^T) with the
+    weights in interleave_gate_up's layout and w_globals = fp32 GPU tensor [2] = {gate, up}.
+    h is returned as h_dtype [M, F] unless h_dtype is None, and as NVFP4 under the given
+    h_global (fp32 GPU tensor of one element) when h_global is set.  Returns (h, h_nvfp4)."""
+    M, K = a.rows, a.cols
+    _require(w_codes.dim() == 2 and w_codes.shape[0] % 32 == 0, "w_codes: [2F, K/2], F a multiple of 16")
+    F = w_codes.shape[0] // 2
+    _require(w_codes.shape == (2 * F, K // 2) and w_scales.shape == (2 * F, K // 16), "bad interleaved weight shapes")
+    _require(w_globals.dtype == torch.float32 and w_globals.is_cuda and w_globals.numel() == 2, "w_globals: fp32 [2]")
+    _require(h_dtype is not None or h_global is not None, "ask for h, its NVFP4 encoding, or both")
+    dev = a.codes.device
+    h = _out_tensor(M, F, h_dtype, dev, out) if h_dtype is not None else None
+    q = None
+    if h_global is not None:
+        _require(h_global.dtype == torch.float32 and h_global.is_cuda and h_global.numel() == 1, "h_global: fp32 [1]")
+        q = q_out if q_out is not None else NVFP4Tensor(
+            torch.empty((M, F // 2), dtype=torch.uint8, device=dev),
+            torch.empty((M, F // 16), dtype=torch.uint8, device=dev), h_global)
+        q.global_scale = h_global
+    per_row = int(a.global_scale.numel() == M and M != 1)
+    st = lib.nvfp4_gemm_swiglu(M, F, K, _ptr(a.codes), _ptr(a.scales), _ptr(a.global_scale), per_row,
+                               _ptr(w_codes), _ptr(w_scales), _ptr(w_globals), _ptr(h),
+                               _y_dtype(h_dtype) if h is not None else _BF16,
+                               h.stride(0) if h is not None and M > 0 else F, _ptr(h_global),
+                               _ptr(q.codes) if q else None, _ptr(q.scales) if q else None, _stream(dev))
+    _check(st, "nvfp4_gemm_swiglu")
+    return h, q
 
 
 def fp8_kv_quantize(x: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:

@@ -203,6 +203,61 @@ int nvfp4_mxfp4_gemm(int64_t M, int64_t K, const uint8_t* a_codes, const uint8_t
                         y_dtype, ldy, static_cast<hipStream_t>(stream));
 }
 
+int nvfp4_interleave_gate_up(int64_t F, int64_t K, const uint8_t* gate_codes, const uint8_t* gate_scales,
+                             const uint8_t* up_codes, const uint8_t* up_scales, uint8_t* w_codes, uint8_t* w_scales,
+                             void* stream) {
+  if (F <= 0 || F % 16 != 0 || K <= 0 || K % 16 != 0) return NVFP4_ERR_INVALID_ARG;
+  if (F > INT32_MAX || K > INT32_MAX) return NVFP4_ERR_UNSUPPORTED;
+  if (!gate_codes || !gate_scales || !up_codes || !up_scales || !w_codes || !w_scales) return NVFP4_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t groups = (size_t)(F / 16);
+  const size_t code_block = (size_t)16 * (size_t)(K / 2), scale_block = (size_t)16 * (size_t)(K / 16);
+  // One 2-D copy per operand and projection: 16-row blocks of the source, every other block
+  // of the destination.
+  const struct { uint8_t* dst; const uint8_t* src; size_t width; } copies[4] = {
+      {w_codes, gate_codes, code_block},
+      {w_codes + code_block, up_codes, code_block},
+      {w_scales, gate_scales, scale_block},
+      {w_scales + scale_block, up_scales, scale_block}};
+  for (const auto& c : copies)
+    if (hipMemcpy2DAsync(c.dst, 2 * c.width, c.src, c.width, c.width, groups, hipMemcpyDeviceToDevice, s) !=
+        hipSuccess)
+      return NVFP4_ERR_HIP;
+  return NVFP4_OK;
+}
+
+int nvfp4_gemm_swiglu(int64_t M, int64_t F, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+                      const float* a_global, int a_global_per_row, const uint8_t* w_codes, const uint8_t* w_scales,
+                      const float* w_globals, void* h, int h_dtype, int64_t ldh, const float* h_global,
+                      uint8_t* h_codes, uint8_t* h_scales, void* stream) {
+  if (F <= 0 || F % 16 != 0) return NVFP4_ERR_INVALID_ARG;
+  if (F > INT32_MAX / 2) return NVFP4_ERR_UNSUPPORTED;
+  const int64_t N = 2 * F;
+  const bool quant = h_codes || h_scales || h_global;
+  if (!h && !quant) return NVFP4_ERR_INVALID_ARG;
+  // h is checked below; check_gemm_common's output checks get a stand-in.
+  int st = check_gemm_common(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales, a_codes,
+                             NVFP4_BF16, N);
+  if (st != NVFP4_OK || M == 0) return st;
+  if (!w_globals || !aligned(w_globals, 4)) return NVFP4_ERR_INVALID_ARG;
+  if (h) {
+    if (h_dtype != NVFP4_F32 && h_dtype != NVFP4_BF16) return NVFP4_ERR_INVALID_ARG;
+    if (ldh < F || !aligned(h, h_dtype == NVFP4_F32 ? 4 : 2)) return NVFP4_ERR_INVALID_ARG;
+  }
+  if (quant && (!h_codes || !h_scales || !h_global || !aligned(h_codes, 16) || !aligned(h_scales, 16) ||
+                !aligned(h_global, 4)))
+    return NVFP4_ERR_INVALID_ARG;
+  if ((uint64_t)M * (uint64_t)F >= (1ull << 31)) return NVFP4_ERR_UNSUPPORTED;
+  SegmentTable seg{};
+  seg.count = 1;
+  seg.bound[0] = 0;
+  seg.bound[1] = (int32_t)N;
+  QuantOut q{h_global, h_codes, h_scales};
+  return launch_gemm(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales, w_globals, seg, h,
+                     h ? h_dtype : NVFP4_BF16, h ? ldh : F, nullptr, static_cast<hipStream_t>(stream),
+                     quant ? &q : nullptr, nullptr, true);
+}
+
 int nvfp4_fp8_kv_quantize(const void* x, int x_dtype, int64_t n, const float* scale, uint8_t* q, void* stream) {
   if (n < 0 || (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16)) return NVFP4_ERR_INVALID_ARG;
   if (n == 0) return NVFP4_OK;

@@ -60,12 +60,14 @@ struct GemmArgs {
   const float* gate_dt_bias;
   float* gate_g;
   float* gate_beta;
+  int32_t swiglu;     // SwiGLU pairs: see store_swiglu_block (w_globals = {gate, up})
 };
 
 // Epilogue modes of the MFMA kernels.
 constexpr int kEpiStore = 0;   // Y in fp32 or bf16
 constexpr int kEpiNvfp4 = 1;   // Y as NVFP4 under a given global scale
 constexpr int kEpiGates = 2;   // Y, and the GDN gates of the last two segments
+constexpr int kEpiSwiglu = 3;  // h = silu(gate) * up of interleaved 32-column pairs
 
 // One 16-column block of output row m (columns n .. n+15, all valid) as NVFP4: the same
 // encoder as the quantizer, under the given global scale.
@@ -80,6 +82,12 @@ __device__ __forceinline__ int segment_of(int n, const SegmentTable& seg) {
   int s = 0;
   for (int i = 1; i < seg.count; ++i) s += n >= seg.bound[i];
   return s;
+}
+
+// Global scale of the weight row behind output column n: its segment's, or with SwiGLU pairs
+// the gate's (columns 32p .. 32p+15) or the up projection's (32p+16 .. 32p+31).
+__device__ __forceinline__ float w_global_at(const GemmArgs& g, int n) {
+  return g.swiglu ? g.w_globals[(n >> 4) & 1] : g.w_globals[segment_of(n, g.seg)];
 }
 
 __device__ __forceinline__ void store_out(const GemmArgs& g, int m, int n, float v) {
@@ -112,6 +120,61 @@ __device__ __forceinline__ void store_gate(const GemmArgs& g, int m, int n, floa
   } else {
     const int j = c - g.gate_h;
     g.gate_g[(int64_t)m * g.gate_h + j] = gate_log_decay(y, expf(g.gate_a_log[j]), g.gate_dt_bias[j]);
+  }
+}
+
+// SiLU of an fp32 GEMM output, y * sigmoid(y) (the gated MLP's activation); for y below about
+// -88 e^-y overflows and the result is -0, where the exact value is under 3e-37.
+__device__ __forceinline__ float silu(float y) { return y * gate_write_strength(y); }
+
+// SwiGLU of one interleaved column pair of output row m: fused columns n .. n+15 (n a multiple
+// of 32) are gate outputs and n+16 .. n+31 the up outputs of the same 16 hidden units
+// n/2 .. n/2+15, so h = silu(gate) * up is one 16-element block of the hidden row (width N/2).
+// gv and uv hold the 16 fp32 outputs (global scales applied) each, 16-byte aligned.  h is stored
+// as fp32 or bf16 when y is given (row pitch ldy) and as one NVFP4 block under q_global[0]
+// when q_out (codes [M, N/4], scale bytes [M, N/32]).
+__device__ __forceinline__ void store_swiglu_block(const GemmArgs& g, int m, int n, const float* gv,
+                                                   const float* uv) {
+  float h[16];
+#pragma unroll
+  for (int e = 0; e < 16; e += 4) {
+    const float4 a = *reinterpret_cast<const float4*>(gv + e);
+    const float4 b = *reinterpret_cast<const float4*>(uv + e);
+    h[e] = silu(a.x) * b.x;
+    h[e + 1] = silu(a.y) * b.y;
+    h[e + 2] = silu(a.z) * b.z;
+    h[e + 3] = silu(a.w) * b.w;
+  }
+  const int j = n >> 1;                       // first hidden column of the block
+  if (g.y) {
+    if (g.y_bf16) {
+      uint16_t* y = static_cast<uint16_t*>(g.y) + (int64_t)m * g.ldy + j;
+      if (g.y_vec) {
+        uint4* y4 = reinterpret_cast<uint4*>(y);
+        y4[0] = make_uint4(bf16_pair(h[0], h[1]), bf16_pair(h[2], h[3]), bf16_pair(h[4], h[5]), bf16_pair(h[6], h[7]));
+        y4[1] = make_uint4(bf16_pair(h[8], h[9]), bf16_pair(h[10], h[11]), bf16_pair(h[12], h[13]),
+                           bf16_pair(h[14], h[15]));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) y[e] = f32_to_bf16_rne(h[e]);
+      }
+    } else {
+      float* y = static_cast<float*>(g.y) + (int64_t)m * g.ldy + j;
+      if (g.y_vec) {
+#pragma unroll
+        for (int e = 0; e < 16; e += 4) *reinterpret_cast<float4*>(y + e) = make_float4(h[e], h[e + 1], h[e + 2], h[e + 3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) y[e] = h[e];
+      }
+    }
+  }
+  if (g.q_out) {
+    uint32_t sb, lo, hi;
+    encode_block(h, g.q_global[0], sb, lo, hi);
+    const int64_t width = g.N >> 1;
+    *reinterpret_cast<uint2*>(g.q_codes + (int64_t)m * (width / 2) + j / 2) = make_uint2(lo, hi);
+    g.q_scales[(int64_t)m * (width / 16) + j / 16] = (uint8_t)sb;
   }
 }
 
@@ -511,9 +574,11 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
   if (nk > 1) load_stage_lds<T, MX>(g, m0, n0, 1, lds + C::kStageBytes);
   {
     float* row_scale = reinterpret_cast<float*>(lds + kScaleTableOffset);
-    for (int t = threadIdx.x; t < 2 * T; t += kPrefillThreads)
+    for (int t = threadIdx.x; t < 2 * T; t += kPrefillThreads) {
+      const int n = min(n0 + t - T, g.N - 1);
       row_scale[t] = t < T ? g.a_global[g.a_per_row ? min(m0 + t, g.M - 1) : 0]
-                           : g.w_globals[segment_of(min(n0 + t - T, g.N - 1), g.seg)];
+                           : g.w_globals[EPI == kEpiSwiglu ? (n >> 4) & 1 : segment_of(n, g.seg)];
+    }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
   __syncthreads();
@@ -568,11 +633,12 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
   float sw[F];
 #pragma unroll
   for (int j = 0; j < F; ++j) sw[j] = col_scale[wn + 32 * j + r];
-  if constexpr (EPI == kEpiNvfp4 || EPI == kEpiGates) {
+  if constexpr (EPI == kEpiNvfp4 || EPI == kEpiGates || EPI == kEpiSwiglu) {
     // The scaled fp32 results go through LDS in passes of 128 tile rows (row pitch T + 8
     // floats, so the two row groups one write touches use disjoint banks).  NVFP4 output: each
-    // thread then encodes whole 16-column blocks of a row.  Gates: the tile's gate columns are
-    // read back, one value per thread and step; tiles without gate columns skip this.
+    // thread then encodes whole 16-column blocks of a row.  SwiGLU: each thread takes whole
+    // 32-column gate/up pairs of a row.  Gates: the tile's gate columns are read back, one
+    // value per thread and step; tiles without gate columns skip this.
     constexpr int kQPitch = T + 8;
     constexpr int kQPasses = T / 128;
     constexpr int kBlocksPerRow = T / 16;
@@ -582,7 +648,7 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
       c0 = max(n0, g.gate_n0);
       c1 = min(n0 + T, g.N);
     }
-    if (EPI == kEpiNvfp4 || c0 < c1) {
+    if (EPI != kEpiGates || c0 < c1) {
       __syncthreads();
 #pragma unroll
       for (int p = 0; p < kQPasses; ++p) {
@@ -616,6 +682,14 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
               store_block_nvfp4(g, m, n, v);
             }
           }
+        } else if constexpr (EPI == kEpiSwiglu) {
+          constexpr int kPairsPerRow = T / 32;
+          for (int b = threadIdx.x; b < 128 * kPairsPerRow; b += kPrefillThreads) {
+            const int lr = b / kPairsPerRow, pj = b % kPairsPerRow;
+            const int m = m0 + 128 * p + lr, n = n0 + 32 * pj;
+            const float* v = out + lr * kQPitch + 32 * pj;
+            if (m < g.M && n < g.N) store_swiglu_block(g, m, n, v, v + 16);
+          }
         } else {
           // One gate segment at a time, so that a wavefront evaluates one function; a lane
           // keeps its column's head parameters in registers across the rows.
@@ -639,7 +713,7 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs& g, uint8_t* lds, in
         if (p + 1 < kQPasses) __syncthreads();
       }
     }
-    if constexpr (EPI == kEpiNvfp4) return;
+    if constexpr (EPI == kEpiNvfp4 || EPI == kEpiSwiglu) return;
   }
   if (!g.y_bf16) {
     // fp32: each store instruction covers 128 contiguous bytes of two rows; store directly.
@@ -843,8 +917,9 @@ __device__ __forceinline__ void decode_chunk_mma(const DecodeChunk& d, f32x4_t& 
 // lane]) are summed in a fixed order, scaled (y = (sum * s_gA[m]) * s_gW[seg(n)]) and stored for
 // the workgroup's rows n < n_end; for
 // NVFP4 output the scaled values of the 16 x 32 tile go through qy (16 x 32 floats of LDS) and
-// each of the first 32 threads encodes one 16-column block.  GATES: gate columns also get
-// their gates from the same fp32 value.
+// each of the first 32 threads encodes one 16-column block; with SwiGLU pairs (the workgroup's
+// 32 rows are one gate/up pair) each of the first 16 threads takes one token's pair.  GATES:
+// gate columns also get their gates from the same fp32 value.
 constexpr int kDecodeRowsE = 32;
 template <bool GATES>
 __device__ __forceinline__ void decode_epilogue(const GemmArgs& g, const f32x4_t* red, float* qy, int wave, int lane,
@@ -856,12 +931,12 @@ __device__ __forceinline__ void decode_epilogue(const GemmArgs& g, const f32x4_t
     f32x4_t sum = f32x4_t{};
     for (int w = 0; w < 4; ++w) sum += red[(w * 2 + wave) * 64 + lane];
     const int n = n0 + 16 * wave + rr;
-    const float sw = n < n_end ? g.w_globals[segment_of(n, g.seg)] : 0.0f;
+    const float sw = n < n_end ? w_global_at(g, n) : 0.0f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int m = 4 * grp + q;
       const float v = m < g.M && n < n_end ? (sum[q] * g.a_global[g.a_per_row ? m : 0]) * sw : 0.0f;
-      if (g.q_out)
+      if (g.q_out || g.swiglu)
         qy[m * kDecodeRowsE + 16 * wave + rr] = v;
       else if (m < g.M && n < n_end)
         store_out(g, m, n, v);
@@ -870,7 +945,11 @@ __device__ __forceinline__ void decode_epilogue(const GemmArgs& g, const f32x4_t
       }
     }
   }
-  if (g.q_out) {
+  if (g.swiglu) {
+    __syncthreads();
+    const int m = (int)threadIdx.x;
+    if (m < 16 && m < g.M && n0 < n_end) store_swiglu_block(g, m, n0, qy + m * kDecodeRowsE, qy + m * kDecodeRowsE + 16);
+  } else if (g.q_out) {
     __syncthreads();
     const int t = (int)threadIdx.x;
     if (t < 32) {
@@ -900,7 +979,7 @@ constexpr int kDecodeDepth = 4;             // 256-wide stages in flight per lan
 template <bool GATES>
 __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(GemmArgs g) {
   __shared__ f32x4_t red[kDecodeWaves * 2 * 64];
-  __shared__ float qy[16 * kDecodeRows];
+  __shared__ __align__(16) float qy[16 * kDecodeRows];
   // wave is uniform: made explicit so that the stage loop's exits are scalar branches.
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int rr = lane & 15, grp = lane >> 4;
@@ -1281,13 +1360,13 @@ __global__ __launch_bounds__(kDwThreads) void gemm_decode_rows_kernel(GemmArgs g
     for (int w = 1; w < 8; ++w) sum += red[(w * G + j) * 64 + lane];
     const int nl = 16 * j + rr, n = r0 + nl;
     const bool nv = nl < rw;
-    const float sw = nv ? g.w_globals[segment_of(n, g.seg)] : 0.0f;
+    const float sw = nv ? w_global_at(g, n) : 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 4 * q + i;
       const bool ok = m < g.M && nv;
       const float v = ok ? (sum[i] * g.a_global[g.a_per_row ? m : 0]) * sw : 0.0f;
-      if (g.q_out)
+      if (g.q_out || g.swiglu)
         qy[m * (16 * G) + nl] = v;
       else if (ok)
         store_out(g, m, n, v);
@@ -1296,7 +1375,20 @@ __global__ __launch_bounds__(kDwThreads) void gemm_decode_rows_kernel(GemmArgs g
       }
     }
   }
-  if (g.q_out) {
+  if (g.swiglu) {
+    // Rows per workgroup are a multiple of 32 here, so G is even: G / 2 gate/up pairs (the
+    // host never picks an odd G for SwiGLU pairs).
+    __syncthreads();
+    if constexpr (G % 2 == 0) {
+      constexpr int P = G / 2;
+      const int t = (int)threadIdx.x;
+      if (t < 16 * P) {
+        const int m = t / P, j = t - m * P;
+        const float* v = qy + m * (16 * G) + 32 * j;
+        if (m < g.M && 32 * j < rw) store_swiglu_block(g, m, r0 + 32 * j, v, v + 16);
+      }
+    }
+  } else if (g.q_out) {
     __syncthreads();
     const int t = (int)threadIdx.x;
     if (t < 16 * G) {
@@ -1334,7 +1426,7 @@ __global__ __launch_bounds__(256) void gemm_plain_kernel(GemmArgs g) {
       acc = __builtin_fmaf(e2m1_value(ca >> 4) * sa, e2m1_value(cw >> 4) * sw, acc);
     }
   }
-  const float v = (acc * g.a_global[g.a_per_row ? m : 0]) * g.w_globals[segment_of(n, g.seg)];
+  const float v = (acc * g.a_global[g.a_per_row ? m : 0]) * w_global_at(g, n);
   store_out(g, m, n, v);
   if (g.gate_h > 0 && n >= g.gate_n0) store_gate(g, m, n, v);
 }
@@ -1379,6 +1471,7 @@ GemmArgs gemm_args(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, cons
   g.gate_dt_bias = nullptr;
   g.gate_g = nullptr;
   g.gate_beta = nullptr;
+  g.swiglu = 0;
   return g;
 }
 
@@ -1393,6 +1486,7 @@ int tile_kernels_ready(int& cus) {
     const void* kernels[] = {reinterpret_cast<const void*>(gemm_prefill_kernel<kEpiStore>),
                              reinterpret_cast<const void*>(gemm_prefill_kernel<kEpiNvfp4>),
                              reinterpret_cast<const void*>(gemm_prefill_kernel<kEpiGates>),
+                             reinterpret_cast<const void*>(gemm_prefill_kernel<kEpiSwiglu>),
                              reinterpret_cast<const void*>(gemm_mx_kernel)};
     for (const void* k : kernels)
       if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kPrefillLds) != hipSuccess)
@@ -1406,14 +1500,16 @@ int tile_kernels_ready(int& cus) {
 }
 
 // Rows per workgroup of the balanced decode kernel: the fewest rounds over the CUs with at
-// most 16 kDwMaxG rows per workgroup, the rows then spread evenly over the workgroups of those
-// rounds (a multiple of 16 for NVFP4 output, whose 16-column blocks must not straddle
-// workgroups).  Returns the kernel's LDS bytes, 0 when K is too long for its LDS.
-int decode_rows_plan(int64_t N, int64_t K, int cus, bool blocks16, int& rows, int& groups) {
-  const int64_t cap = 16 * kDwMaxG;
+// most cap rows per workgroup (the largest multiple of unit up to 16 kDwMaxG), the rows then
+// spread evenly over the workgroups of those rounds and rounded up to a multiple of unit (16
+// for NVFP4 output, whose 16-column blocks must not straddle workgroups; 32 for SwiGLU pairs;
+// else 1); that stays within cap, as N <= rounds * CUs * cap.  Returns the kernel's LDS bytes,
+// 0 when K is too long for its LDS.
+int decode_rows_plan(int64_t N, int64_t K, int cus, int unit, int& rows, int& groups) {
+  const int64_t cap = 16 * kDwMaxG / unit * unit;
   const int64_t rounds = (N + cus * cap - 1) / (cus * cap);
   int64_t r = (N + cus * rounds - 1) / (cus * rounds);
-  if (blocks16) r = (r + 15) / 16 * 16;
+  r = (r + unit - 1) / unit * unit;
   rows = (int)r;
   groups = (int)((r + 15) / 16);
   return dw_lds_bytes(groups, K);
@@ -1486,12 +1582,13 @@ void tile_grid(int64_t M, int64_t N, int cus, int64_t& n_split, int64_t& big, in
 int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
                 const float* a_global, int a_global_per_row, const uint8_t* w_codes, const uint8_t* w_scales,
                 const float* w_globals, const SegmentTable& seg, void* y, int y_dtype, int64_t ldy, void* workspace,
-                hipStream_t stream, const QuantOut* qout, const GateOut* gates) {
+                hipStream_t stream, const QuantOut* qout, const GateOut* gates, bool swiglu) {
   (void)workspace;
   if (M == 0 || N == 0) return NVFP4_OK;
   const bool plain = K % 128 != 0 || (M > 16 && (K % BK != 0 || K >= (1 << 24)));
-  if (qout && (plain || N % 16 != 0)) return NVFP4_ERR_UNSUPPORTED;
-  if (qout && gates) return NVFP4_ERR_INVALID_ARG;
+  if ((qout || swiglu) && (plain || N % 16 != 0)) return NVFP4_ERR_UNSUPPORTED;
+  if ((qout || swiglu) && gates) return NVFP4_ERR_INVALID_ARG;
+  if (swiglu && N % 32 != 0) return NVFP4_ERR_INVALID_ARG;
   GemmArgs g = gemm_args(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales, w_globals, seg,
                          y, y_dtype, ldy);
   g.q_out = qout != nullptr;
@@ -1504,6 +1601,7 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
   g.gate_dt_bias = gates ? gates->dt_bias : nullptr;
   g.gate_g = gates ? gates->g : nullptr;
   g.gate_beta = gates ? gates->beta : nullptr;
+  g.swiglu = swiglu;
   const bool gated = gates != nullptr;
   if (plain) {
     const int64_t total = M * N;
@@ -1515,18 +1613,21 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
     // Up to one round of 32-row workgroups the K-split kernel is the faster; past it, the
     // balanced kernel avoids the partial last round.
     int rows = 0, groups = 0;
-    const int lds_bytes = N > (int64_t)kDecodeRows * cus ? decode_rows_plan(N, K, cus, g.q_out != 0, rows, groups) : 0;
+    const int unit = swiglu ? 32 : g.q_out ? 16 : 1;
+    const int lds_bytes = N > (int64_t)kDecodeRows * cus ? decode_rows_plan(N, K, cus, unit, rows, groups) : 0;
     if (lds_bytes == 0) {
       // Rows per workgroup: about N / CUs, so that every CU takes a share (16 to 32; 32 for
-      // NVFP4 output, whose 16-column blocks must not straddle workgroups).
+      // NVFP4 output, whose 16-column blocks must not straddle workgroups, and for SwiGLU
+      // pairs, one pair per workgroup).
       const int64_t share = (N + cus - 1) / cus;
-      const int r = g.q_out ? kDecodeRows : (int)std::min<int64_t>(kDecodeRows, std::max<int64_t>(16, share));
+      const int r = unit > 1 ? kDecodeRows : (int)std::min<int64_t>(kDecodeRows, std::max<int64_t>(16, share));
       const unsigned grid = (unsigned)((N + r - 1) / r);
       if (gated)
         gemm_decode_lds_kernel<true><<<grid, kDecodeThreads, kDlLds, stream>>>(g, r);
       else
         gemm_decode_lds_kernel<false><<<grid, kDecodeThreads, kDlLds, stream>>>(g, r);
     } else {
+      if (swiglu && groups % 2 != 0) return NVFP4_ERR_UNSUPPORTED;   // not reached: rows % 32 == 0
       switch (groups) {
         case 1: launch_decode_rows<1>(g, gated, rows, lds_bytes, stream); break;
         case 2: launch_decode_rows<2>(g, gated, rows, lds_bytes, stream); break;
@@ -1548,7 +1649,9 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
     int64_t n_split, big, small;
     tile_grid(M, N, cus, n_split, big, small);
     const unsigned grid = (unsigned)(big + small);
-    if (g.q_out)
+    if (swiglu)
+      gemm_prefill_kernel<kEpiSwiglu><<<grid, kPrefillThreads, kPrefillLds, stream>>>(g, (int)n_split, (int)big);
+    else if (g.q_out)
       gemm_prefill_kernel<kEpiNvfp4><<<grid, kPrefillThreads, kPrefillLds, stream>>>(g, (int)n_split, (int)big);
     else if (gated)
       gemm_prefill_kernel<kEpiGates><<<grid, kPrefillThreads, kPrefillLds, stream>>>(g, (int)n_split, (int)big);

@@ -71,11 +71,14 @@ struct GateOut {
 // With qout set, y is unused and the result is written as NVFP4 instead; then N % 16 == 0 and
 // the shape must be one the MFMA kernels take (NVFP4_ERR_UNSUPPORTED otherwise).  With gates
 // set, y is written as usual and the gates as well; qout and gates are not combined.
+// With swiglu, W's rows are gate/up pairs interleaved in groups of 16 (N % 32 == 0, w_globals =
+// {gate, up}, seg unused) and the output is h = silu(gate) * up, [M, N/2]: in y (fp32 or bf16,
+// pitch ldy) unless y is null, and as NVFP4 ([M, N/4] codes, [M, N/32] scales) when qout is set.
 int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
                 const float* a_global, int a_global_per_row, const uint8_t* w_codes,
                 const uint8_t* w_scales, const float* w_globals, const SegmentTable& seg,
                 void* y, int y_dtype, int64_t ldy, void* workspace, hipStream_t stream,
-                const QuantOut* qout = nullptr, const GateOut* gates = nullptr);
+                const QuantOut* qout = nullptr, const GateOut* gates = nullptr, bool swiglu = false);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 // MXFP4 operands (E2M1 codes [rows, K/2] as NVFP4, E8M0 scale bytes [rows, K/32]), the same

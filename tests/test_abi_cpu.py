@@ -197,6 +197,28 @@ def test_gdn_gates_argument_errors(nv):
     assert call(M=0) == 0                          # empty product: a no-op
 
 
+def test_swiglu_argument_errors(nv):
+    f = nv.lib.nvfp4_gemm_swiglu
+
+    def call(M=32, F=64, K=256, h=A16, dt=1, ldh=64, hg=A16, hc=A16, hs=A16, wg=A16):
+        return f(M, F, K, A16, A16, A16, 0, A16, A16, wg, h, dt, ldh, hg, hc, hs, None)
+
+    assert call(F=40) == 1 and call(F=0) == 1      # F not a positive multiple of 16
+    assert call(h=None, hg=None, hc=None, hs=None) == 1     # no output asked for
+    assert call(hg=None) == 1 and call(hc=None) == 1 and call(hs=None) == 1   # partial NVFP4 output
+    assert call(hc=A16 + 8) == 1 and call(hs=A16 + 4) == 1 and call(hg=A16 + 2) == 1
+    assert call(ldh=48) == 1 and call(dt=7) == 1 and call(h=A16 + 1) == 1
+    assert call(wg=None) == 1
+    assert call(K=272) == 2                        # K not a multiple of 128: no kernel takes it
+    assert call(K=384) == 2                        # M > 16 needs K % 256 == 0
+    assert call(M=0) == 0                          # empty product: a no-op
+    g = nv.lib.nvfp4_interleave_gate_up
+    assert g(40, 256, A16, A16, A16, A16, A16, A16, None) == 1      # F not a multiple of 16
+    assert g(64, 40, A16, A16, A16, A16, A16, A16, None) == 1       # K not a multiple of 16
+    assert g(64, 256, A16, A16, None, A16, A16, A16, None) == 1
+    assert g(64, 256, A16, A16, A16, A16, A16, None, None) == 1
+
+
 def test_mxfp4_argument_errors(nv):
     r = nv.lib.nvfp4_to_mxfp4
     assert r(4, 48, A16, A16, A16, A16, None) == 1            # cols not a multiple of 32
