@@ -1197,7 +1197,8 @@ template <int G> struct DwCfg {
   static constexpr int kScratch = kDepth * kStageBytes; // 1 KB target of padding copies
   static constexpr int kScales = kScratch + 1024;       // scale chunks: block b, chunk c at (b kChunks + c) KB
 };
-constexpr int kDwMaxG = 5;
+constexpr int kDwMaxG = 5;     // row groups per workgroup; SwiGLU pairs may take kDwPairG
+constexpr int kDwPairG = 6;
 constexpr int kDwThreads = 512;
 
 // LDS bytes of the balanced decode kernel for G row groups and K (0 if K does not fit).
@@ -1214,7 +1215,8 @@ inline int dw_lds_bytes(int G, int64_t K) {
     case 2: return dw_lds_bytes_g<2>(K);
     case 3: return dw_lds_bytes_g<3>(K);
     case 4: return dw_lds_bytes_g<4>(K);
-    default: return dw_lds_bytes_g<5>(K);
+    case 5: return dw_lds_bytes_g<5>(K);
+    default: return dw_lds_bytes_g<kDwPairG>(K);
   }
 }
 
@@ -1503,10 +1505,12 @@ int tile_kernels_ready(int& cus) {
 // most cap rows per workgroup (the largest multiple of unit up to 16 kDwMaxG), the rows then
 // spread evenly over the workgroups of those rounds and rounded up to a multiple of unit (16
 // for NVFP4 output, whose 16-column blocks must not straddle workgroups; 32 for SwiGLU pairs;
-// else 1); that stays within cap, as N <= rounds * CUs * cap.  Returns the kernel's LDS bytes,
-// 0 when K is too long for its LDS.
+// else 1); that stays within cap, as N <= rounds * CUs * cap.  SwiGLU pairs may take three per
+// workgroup (96 rows) where K leaves room in LDS: with two, the rounding to whole pairs adds a
+// short last round, and a workgroup's time is mostly its K loop's latency, not its rows.
+// Returns the kernel's LDS bytes, 0 when K is too long for its LDS.
 int decode_rows_plan(int64_t N, int64_t K, int cus, int unit, int& rows, int& groups) {
-  const int64_t cap = 16 * kDwMaxG / unit * unit;
+  const int64_t cap = unit == 32 && dw_lds_bytes(kDwPairG, K) ? 16 * kDwPairG : 16 * kDwMaxG / unit * unit;
   const int64_t rounds = (N + cus * cap - 1) / (cus * cap);
   int64_t r = (N + cus * rounds - 1) / (cus * rounds);
   r = (r + unit - 1) / unit * unit;
@@ -1542,6 +1546,7 @@ int decode_kernels_ready(int& cus) {
     if (st == NVFP4_OK) st = set_decode_rows_lds<3>();
     if (st == NVFP4_OK) st = set_decode_rows_lds<4>();
     if (st == NVFP4_OK) st = set_decode_rows_lds<5>();
+    if (st == NVFP4_OK) st = set_decode_rows_lds<kDwPairG>();
     if (st != NVFP4_OK) return st;
     if (hipDeviceGetAttribute(&cu_count[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return NVFP4_ERR_HIP;
@@ -1633,7 +1638,8 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
         case 2: launch_decode_rows<2>(g, gated, rows, lds_bytes, stream); break;
         case 3: launch_decode_rows<3>(g, gated, rows, lds_bytes, stream); break;
         case 4: launch_decode_rows<4>(g, gated, rows, lds_bytes, stream); break;
-        default: launch_decode_rows<5>(g, gated, rows, lds_bytes, stream); break;
+        case 5: launch_decode_rows<5>(g, gated, rows, lds_bytes, stream); break;
+        default: launch_decode_rows<kDwPairG>(g, gated, rows, lds_bytes, stream); break;
       }
     }
   } else if (M <= 16) {
