@@ -123,9 +123,15 @@ __device__ __forceinline__ void store_gate(const GemmArgs& g, int m, int n, floa
   }
 }
 
-// SiLU of an fp32 GEMM output, y * sigmoid(y) (the gated MLP's activation); for y below about
-// -88 e^-y overflows and the result is -0, where the exact value is under 3e-37.
-__device__ __forceinline__ float silu(float y) { return y * gate_write_strength(y); }
+// SiLU of an fp32 GEMM output, y * sigmoid(y) = y / (1 + e^-y) (the gated MLP's activation),
+// with the hardware base-2 exponential and reciprocal, each within one ulp: the result's
+// relative error is at most about (|y| + 3) 2^-23, the |y| part from rounding the exponential's
+// argument -y log2(e) to fp32.  For y below about -88 the exponential overflows and the result
+// is -0, where the exact value is under 3e-37.
+__device__ __forceinline__ float silu(float y) {
+  const float e = __builtin_amdgcn_exp2f(-y * 1.44269504088896341f);   // log2(e)
+  return y * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // SwiGLU of one interleaved column pair of output row m: fused columns n .. n+15 (n a multiple
 // of 32) are gate outputs and n+16 .. n+31 the up outputs of the same 16 hidden units
