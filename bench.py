@@ -10,6 +10,8 @@ Workloads (--workload):
   prefill  X[4096x5120] bf16 (0.1% channels x50), W[17408x5120]        (default)
   decode   X[M x 17408] W[5120x17408] and X[M x 5120] W[17408x5120], M in {1,4,16}, per-token scales
   fused    X[8192x5120], six GDN input projections with their own global scales
+  swiglu   gated MLP input projection (gate and up 17408x5120, SwiGLU epilogue): M = 4096 and
+           M in {1, 16}, beside the plain fused gate+up GEMM with bf16 output
 
 Prints one JSON line.  `value` is GEMM flops of the whole step divided by the step time.
 `roofline` describes the dominant kernel (the GEMM) from HIP events on the launch stream;
@@ -531,6 +533,51 @@ def bench_kv_fp8(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: int
     return out
 
 
+def bench_swiglu(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: int = 4):
+    """The gated MLP input projection in one launch (fused gate+up GEMM, SwiGLU epilogue), h as
+    bf16 and as NVFP4 for the down projection (under a calibrated global scale), beside the
+    plain fused gate+up GEMM with bf16 output of the same operands (what an MLP without the
+    epilogue launches before a separate activation pass): prefill M = 4096 (per-tensor
+    activation scale) and decode M in {1, 16} (per-token scales; 4 weight copies rotating so W
+    never comes from the 256 MB cache)."""
+    m = workloads.MLP
+    dev = torch.device("cuda:0")
+    gate = nv.quantize(torch.from_numpy(m.gate()).to(dev).to(torch.bfloat16))
+    up = nv.quantize(torch.from_numpy(m.up()).to(dev).to(torch.bfloat16))
+    wg = torch.cat([gate.global_scale, up.global_scale])
+    wc, ws = nv.interleave_gate_up(gate, up)
+    fc, fs = torch.cat([gate.codes, up.codes]), torch.cat([gate.scales, up.scales])
+    del gate, up
+    copies = [(wc, ws, fc, fs)] + [tuple(t.clone() for t in (wc, ws, fc, fs)) for _ in range(rotate - 1)]
+    F, K = m.F, m.K
+    out = {"F": F, "K": K}
+    for M in (m.M,) + m.Ms:
+        a = nv.quantize(torch.from_numpy(m.x(M)).to(dev).to(torch.bfloat16), "per_tensor" if M == m.M else "per_row")
+        rot = 1 if M == m.M else rotate
+        hb = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+        nv.gemm_swiglu(a, wc, ws, wg, torch.bfloat16, out=hb)
+        hg = (hb.float().abs().max() / 2688.0).reshape(1)     # calibration (offline)
+        _, q = nv.gemm_swiglu(a, wc, ws, wg, None, hg)
+        y = torch.empty((M, 2 * F), dtype=torch.bfloat16, device=dev)
+        c = lambda i: copies[i % rot]
+        t_fused = _mean_ms(lambda i: nv.gemm_fused_segments(a, c(i)[2], c(i)[3], (F, F), wg, torch.bfloat16, out=y),
+                           steps, warmup, settle_s)
+        t_bf16 = _mean_ms(lambda i: nv.gemm_swiglu(a, c(i)[0], c(i)[1], wg, torch.bfloat16, out=hb),
+                          steps, warmup, settle_s)
+        t_q = _mean_ms(lambda i: nv.gemm_swiglu(a, c(i)[0], c(i)[1], wg, None, hg, q_out=q), steps, warmup, settle_s)
+        flops = 2.0 * M * 2 * F * K
+        wbytes = 2 * F * K * (0.5 + 1 / 16)
+        r = {"fused_gemm_bf16_us": t_fused * 1e3, "swiglu_bf16_us": t_bf16 * 1e3, "swiglu_nvfp4_us": t_q * 1e3}
+        if M == m.M:
+            r["swiglu_nvfp4_tflops"] = flops / (t_q * 1e-3) / 1e12
+            r["swiglu_nvfp4_frac_mfma_f16"] = r["swiglu_nvfp4_tflops"] / MFMA_F16_PEAK_TFLOPS
+        else:
+            r["swiglu_nvfp4_w_gbs"] = wbytes / (t_q * 1e-3) / 1e9
+            r["swiglu_nvfp4_frac_hbm"] = r["swiglu_nvfp4_w_gbs"] / HBM_PEAK_GBS
+        out["prefill" if M == m.M else f"decode M={M}"] = r
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -539,7 +586,7 @@ def main() -> int:
     ap.add_argument("--settle-s", type=float, default=1.0,
                     help="seconds of untimed steps before the warmup steps, for steady clocks")
     ap.add_argument("--workload", choices=["prefill", "decode", "fused", "nvfp4_out", "kv_fp8", "gdn_gates", "mxfp4",
-                                           "sweep"],
+                                           "sweep", "swiglu"],
                     default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=TRAFFIC_JSON,
@@ -580,6 +627,9 @@ def main() -> int:
     if args.workload == "nvfp4_out":
         print(json.dumps({"workload": "nvfp4_out", "results": bench_nvfp4_out(nv, args.steps, args.warmup,
                                                                               args.settle_s)}))
+        return 0
+    if args.workload == "swiglu":
+        print(json.dumps({"workload": "swiglu", "results": bench_swiglu(nv, args.steps, args.warmup, args.settle_s)}))
         return 0
     if args.workload == "fused":
         print(json.dumps({"workload": "fused", "results": bench_fused(nv, args.steps, args.warmup, args.settle_s)}))

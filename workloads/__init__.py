@@ -35,6 +35,7 @@ __all__ = [
     "DECODE",
     "DECODE_UP",
     "FUSED",
+    "MLP",
     "SWEEP",
     "sweep_launches",
     "Launch",
@@ -165,6 +166,32 @@ class Decode:
 
 
 @dataclass(frozen=True)
+class Mlp:
+    """Gated MLP input projection: X[M x 5120] bf16 (0.1% channels x50), gate and up weights
+    [17408 x 5120] each; prefill M = 4096, decode M in {1, 16}."""
+    name: str = "mlp"
+    seed: int = 5
+    M: int = 4096
+    Ms: tuple[int, ...] = (1, 16)
+    F: int = 17408
+    K: int = 5120
+    outlier_frac: float = 0.001
+    outlier_gain: float = 50.0
+    w_sigma: float = 0.02
+
+    def x(self, rows: int) -> np.ndarray:
+        # One activation tensor per token count (ids 100 + rows, clear of the weights' 1, 2).
+        return activation(self.seed, 100 + rows, rows, self.K, outlier_frac=self.outlier_frac,
+                          outlier_gain=self.outlier_gain)
+
+    def gate(self) -> np.ndarray:
+        return weight(self.seed, 1, self.F, self.K, sigma=self.w_sigma)
+
+    def up(self) -> np.ndarray:
+        return weight(self.seed, 2, self.F, self.K, sigma=self.w_sigma)
+
+
+@dataclass(frozen=True)
 class Fused:
     """Fused GDN input projections: six modules, each with its own sigma and global scale."""
     name: str = "fused"
@@ -261,4 +288,5 @@ PREFILL = Prefill()
 DECODE = Decode()
 DECODE_UP = Decode(name="decode_up", seed=4, N=17408, K=5120)
 FUSED = Fused()
+MLP = Mlp()
 SWEEP = Sweep()
