@@ -89,6 +89,37 @@ def test_graph_decode_balanced_rows():
     _replay_and_compare(g, x, M, K, (a.codes, a.global_scale, y), eager)
 
 
+@pytest.mark.parametrize("M,F,K,mode", [(8, 4608, 1024, "per_row"), (300, 1024, 512, "per_tensor")])
+def test_graph_mlp_swiglu_then_down(M, F, K, mode):
+    # The gated MLP under capture: quantize the tokens, the fused gate+up GEMM with its SwiGLU
+    # epilogue (h as bf16 and as NVFP4), then the down projection on the NVFP4 h.  Decode shape:
+    # the balanced kernel with 64-row workgroups; prefill shape: the tile kernel.
+    gate = nv().quantize(to_gpu(workloads.weight(204, 1, F, K)))
+    up = nv().quantize(to_gpu(workloads.weight(204, 2, F, K)))
+    down = nv().quantize(to_gpu(workloads.weight(204, 3, K, F)))
+    wc, ws = nv().interleave_gate_up(gate, up)
+    wg = torch.cat([gate.global_scale, up.global_scale])
+    hg = torch.tensor([0.01], dtype=torch.float32, device=DEV)
+    x = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+    _fill(x, 299, M, K)
+    a = nv().quantize(x, mode)
+    h, q = nv().gemm_swiglu(a, wc, ws, wg, torch.bfloat16, hg)
+    y = nv().gemm(q, down, torch.bfloat16)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        nv().quantize(x, mode, out=a)
+        nv().gemm_swiglu(a, wc, ws, wg, torch.bfloat16, hg, out=h, q_out=q)
+        nv().gemm(q, down, torch.bfloat16, out=y)
+
+    def eager():
+        ae = nv().quantize(x, mode)
+        he, qe = nv().gemm_swiglu(ae, wc, ws, wg, torch.bfloat16, hg)
+        return he, qe.codes, qe.scales, nv().gemm(qe, down, torch.bfloat16)
+
+    _replay_and_compare(g, x, M, K, (h, q.codes, q.scales, y), eager)
+
+
 def test_graph_fp8_kv_and_mxfp4():
     M, N, K = 256, 512, 512
     scale = torch.tensor([0.05], dtype=torch.float32, device=DEV)
