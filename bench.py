@@ -464,7 +464,7 @@ def bench_sweep(nv, steps: int, warmup: int, settle_s: float = 0.0):
 def bench_mxfp4(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: int = 8):
     """The lossy MXFP4 variant at the prefill shape: per step, the NVFP4 quantize of X, its
     re-encoding to MXFP4 and the scaled-FP4 MFMA GEMM (W re-encoded offline), beside the NVFP4
-    GEMM; and the variant's error against the NVFP4 GEMM's output."""
+    GEMM; the variant's error against the NVFP4 GEMM's output; and its decode GEMM."""
     p = workloads.PREFILL
     dev = torch.device("cuda:0")
     xs = [torch.from_numpy(p.x()).to(dev).to(torch.bfloat16)]
@@ -498,6 +498,34 @@ def bench_mxfp4(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: int 
     ynv = nv.gemm(a, w, torch.float32)
     out["rel_rms_error_vs_nvfp4"] = _rel_rms(ymx, ynv)
     out["reencode_bytes_per_element"] = 0.5 + 1 / 16 + 0.5 + 1 / 32
+    out["decode"] = _bench_mx_decode(nv, steps, warmup, settle_s)
+    return out
+
+
+def _bench_mx_decode(nv, steps: int, warmup: int, settle_s: float, rotate: int = 8):
+    """The MXFP4 decode GEMM (M in {1, 16}, per-token scales) beside the exact NVFP4 decode GEMM
+    on the MLP's down and up projections, 8 weight copies rotating past the 256 MB cache."""
+    dev = torch.device("cuda:0")
+    out = {}
+    for label, d in (("down", workloads.DECODE), ("up", workloads.DECODE_UP)):
+        w = nv.quantize(torch.from_numpy(d.w()).to(dev).to(torch.bfloat16))
+        wm = nv.to_mxfp4(w)
+        ws = [w] + [nv.NVFP4Tensor(w.codes.clone(), w.scales.clone(), w.global_scale) for _ in range(rotate - 1)]
+        wms = [wm] + [nv.MXFP4Tensor(wm.codes.clone(), wm.scales.clone(), wm.global_scale) for _ in range(rotate - 1)]
+        r = {"N": d.N, "K": d.K}
+        for M in (1, 16):
+            a = nv.quantize(torch.from_numpy(d.x(M)).to(dev).to(torch.bfloat16), "per_row")
+            am = nv.to_mxfp4(a)
+            y = torch.empty((M, d.N), dtype=torch.bfloat16, device=dev)
+            t_mx = _mean_ms(lambda i: nv.mxfp4_gemm(am, wms[i % rotate].codes, wms[i % rotate].scales, (d.N,),
+                                                    wm.global_scale, torch.bfloat16, out=y), steps, warmup, settle_s)
+            t_nv = _mean_ms(lambda i: nv.gemm(a, ws[i % rotate], torch.bfloat16, out=y), steps, warmup, settle_s)
+            mx_bytes = d.N * d.K * (0.5 + 1 / 32)
+            r[f"M={M}"] = {"mx_gemm_us": t_mx * 1e3, "nvfp4_gemm_us": t_nv * 1e3,
+                           "mx_w_gbs": mx_bytes / (t_mx * 1e-3) / 1e9,
+                           "mx_frac_hbm": mx_bytes / (t_mx * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        out[label] = r
+        del ws, wms, w, wm
     return out
 
 

@@ -834,6 +834,111 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_mx_kernel(GemmArgs g,
   }
 }
 
+// ------------------------------------------------------------------ MXFP4 decode kernel
+
+// M <= 16 tokens on MXFP4 operands: workgroup x owns W rows [32x, 32x + 32) (one 32-row scaled
+// MFMA group) and the whole K range; wavefront w takes the 256-wide K stages w, w + 4, ...,
+// keeping 4 stages of loads in flight per lane, and the 4 wavefronts' 32 x 32 tiles are summed
+// through LDS in a fixed order.  Lane (r, h) = (lane % 32, lane / 32) of a stage loads the 64
+// contiguous bytes of codes of MX blocks 4h .. 4h+3 of its A row and W row, and the 4 E8M0
+// bytes of those blocks (one dword each); chunk c of the stage multiplies block 4h + c.  The
+// same assignment of blocks to (chunk, lane half) holds for A and W, so every dot product is
+// unchanged.  Token rows past M load row M - 1 (their outputs are not stored).
+struct MxDecodeStage {
+  uint4 a[4], w[4];
+  uint32_t as, ws;
+};
+
+__device__ __forceinline__ void mx_decode_load(const uint8_t* ac, const uint8_t* asc, const uint8_t* wc,
+                                               const uint8_t* wsc, int st, MxDecodeStage& d) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) d.w[c] = *reinterpret_cast<const uint4*>(wc + st * 128 + 16 * c);
+  d.ws = *reinterpret_cast<const uint32_t*>(wsc + st * 8);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) d.a[c] = *reinterpret_cast<const uint4*>(ac + st * 128 + 16 * c);
+  d.as = *reinterpret_cast<const uint32_t*>(asc + st * 8);
+}
+
+// Scale byte c of the dwords goes in as byte 0 (the dwords are shifted at their use).
+__device__ __forceinline__ void mx_decode_mma(const MxDecodeStage& d, f32x16_t& acc) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4_operand(d.a[c]), fp4_operand(d.w[c]), acc, 4, 4, 0,
+                                                          (int)(d.as >> (8 * c)), 0, (int)(d.ws >> (8 * c)));
+}
+
+constexpr int kMxDecodeThreads = 256;
+constexpr int kMxDecodeWaves = kMxDecodeThreads / 64;
+constexpr int kMxDecodeRows = 32;
+
+__global__ __launch_bounds__(kMxDecodeThreads) void gemm_mx_decode_kernel(GemmArgs g) {
+  __shared__ f32x16_t red[kMxDecodeWaves * 64];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int r = lane & 31, h = lane >> 5;
+  const int n0 = blockIdx.x * kMxDecodeRows;
+  const int64_t kb = (int64_t)g.K / 2, kx = (int64_t)g.K / 32;
+  const int nst = g.K / 256;
+  const int cnt = wave < nst ? (nst - wave + kMxDecodeWaves - 1) / kMxDecodeWaves : 0;   // this wave's stages
+  const int wr = min(n0 + r, g.N - 1), ar = min(r, g.M - 1);
+  const uint8_t* ac = g.a_codes + ar * kb + 64 * h;
+  const uint8_t* asc = g.a_scales + ar * kx + 4 * h;
+  const uint8_t* wc = g.w_codes + wr * kb + 64 * h;
+  const uint8_t* wsc = g.w_scales + wr * kx + 4 * h;
+
+  // Stage i is multiplied while i+1 .. i+3 are loading; indices past the wave's last stage
+  // reload that stage (a cache hit), unused.
+  f32x16_t acc = f32x16_t{};
+  if (cnt > 0) {
+    const int last = wave + kMxDecodeWaves * (cnt - 1);
+    auto st = [&](int i) { return min(wave + kMxDecodeWaves * i, last); };
+    MxDecodeStage q0, q1, q2, q3;
+    mx_decode_load(ac, asc, wc, wsc, st(0), q0);
+    mx_decode_load(ac, asc, wc, wsc, st(1), q1);
+    mx_decode_load(ac, asc, wc, wsc, st(2), q2);
+    mx_decode_load(ac, asc, wc, wsc, st(3), q3);
+    int i = 0;
+    for (; i + 4 <= cnt; i += 4) {
+      mx_decode_mma(q0, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      mx_decode_load(ac, asc, wc, wsc, st(i + 4), q0);
+      __builtin_amdgcn_sched_barrier(0);
+      mx_decode_mma(q1, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      mx_decode_load(ac, asc, wc, wsc, st(i + 5), q1);
+      __builtin_amdgcn_sched_barrier(0);
+      mx_decode_mma(q2, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      mx_decode_load(ac, asc, wc, wsc, st(i + 6), q2);
+      __builtin_amdgcn_sched_barrier(0);
+      mx_decode_mma(q3, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      mx_decode_load(ac, asc, wc, wsc, st(i + 7), q3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int left = cnt - i;
+    if (left > 0) mx_decode_mma(q0, acc);
+    if (left > 1) mx_decode_mma(q1, acc);
+    if (left > 2) mx_decode_mma(q2, acc);
+  }
+  red[wave * 64 + lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    // D[m][n] of the 32 x 32 tile sits in lane n + 32 (m / 4 % 2), register 4 (m / 8) + m % 4;
+    // tokens m < 16 are registers 0 .. 7.
+    f32x16_t sum = red[lane];
+    for (int w = 1; w < kMxDecodeWaves; ++w) sum += red[w * 64 + lane];
+    const int n = n0 + r;
+    if (n < g.N) {
+      const float sw = w_global_at(g, n);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int m = 8 * (q >> 2) + 4 * h + (q & 3);
+        if (m < g.M) store_out(g, m, n, (sum[q] * g.a_global[g.a_per_row ? m : 0]) * sw);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ decode kernel
 
 // Operands of one 256-wide K stage for one lane of lane group g = lane / 16: the 32 B of codes
@@ -1681,6 +1786,10 @@ int launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, cons
   if (K % BK != 0 || K >= (1 << 24)) return NVFP4_ERR_UNSUPPORTED;
   const GemmArgs g = gemm_args(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales,
                                w_globals, seg, y, y_dtype, ldy);
+  if (M <= 16) {
+    gemm_mx_decode_kernel<<<(unsigned)((N + kMxDecodeRows - 1) / kMxDecodeRows), kMxDecodeThreads, 0, stream>>>(g);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+  }
   int cus = 0;
   const int st = tile_kernels_ready(cus);
   if (st != NVFP4_OK) return st;

@@ -1,8 +1,9 @@
 """GPU parity of the lossy NVFP4 -> MXFP4 variant against the oracle: nvfp4_to_mxfp4 bit-exact
 (codes and E8M0 bytes, in place too, zero blocks included), and nvfp4_mxfp4_gemm within
 1e-4 * sum_k |a_k w_k| (plus half a bf16 ulp for bf16 output) of the oracle's MXFP4 GEMM on
-the same operands: tile-aligned and ragged shapes, small M, fused segments, per-row
-activation scales, and the full prefill shape on sampled rows.  The error of the variant
+the same operands: tile-aligned and ragged shapes, small M (the decode kernel, up to the MLP's
+full up and down shapes), fused segments, per-row activation scales, and the full prefill shape
+on sampled rows.  The error of the variant
 against the exact NVFP4 product is measured and must stay within the range the re-encoding
 allows (it is lossy by design; the figure is reported, not a parity claim)."""
 import numpy as np
@@ -89,6 +90,47 @@ def test_mx_gemm_per_row_scales_and_segments():
                         torch.cat([s.global_scale for s in segs]), torch.float32)
     ys, ts = zip(*(ref.mx_gemm(oma, o) for o in osegs))
     assert_gemm_close(y, np.concatenate(ys, axis=1), np.concatenate(ts, axis=1), "mx fused per-row")
+
+
+def _random_mx(g, R, K, per_row=False):
+    """Seeded MXFP4 bytes: random codes, E8M0 scales over 2^-9 .. 2^8, global scale per row or
+    per tensor."""
+    codes = g.integers(0, 256, (R, K // 2), dtype=np.uint8)
+    scales = g.integers(118, 136, (R, K // 32), dtype=np.uint8)
+    gs = g.uniform(0.5, 2.0, R if per_row else 1).astype(np.float32)
+    return ref.MXFP4(codes, scales, gs, R, K)
+
+
+def _mx_device(o: ref.MXFP4):
+    return nv().MXFP4Tensor(torch.from_numpy(o.codes).to(DEV), torch.from_numpy(o.scales).to(DEV),
+                            torch.from_numpy(np.asarray(o.global_scale, np.float32)).to(DEV))
+
+
+# M <= 16: the MXFP4 decode kernel (32 W rows per workgroup, K split over 4 wavefronts).
+@pytest.mark.parametrize("M,N,K", [(1, 17408, 5120), (16, 17408, 5120), (16, 5120, 17408),  # MLP up / down
+                                   (8, 1000, 1280),     # 5 stages over 4 wavefronts; last workgroup 8 rows
+                                   (2, 64, 256),        # one stage: three wavefronts idle
+                                   (11, 4128, 2304)])
+def test_mx_decode(M, N, K):
+    g = np.random.default_rng(M * 7919 + N + K)
+    oa, ow = _random_mx(g, M, K, per_row=True), _random_mx(g, N, K)
+    w = _mx_device(ow)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        y = nv().mxfp4_gemm(_mx_device(oa), w.codes, w.scales, (N,), w.global_scale, out_dtype)
+        Y, T = ref.mx_gemm(oa, ow)
+        assert_gemm_close(y, Y, T, f"mx decode {M}x{N}x{K} {out_dtype}")
+
+
+def test_mx_decode_segments():
+    M, K, widths = 4, 768, (96, 48, 48, 40)
+    g = np.random.default_rng(17)
+    oa = _random_mx(g, M, K, per_row=True)
+    segs = [_random_mx(g, n, K) for n in widths]
+    ds = [_mx_device(o) for o in segs]
+    y = nv().mxfp4_gemm(_mx_device(oa), torch.cat([d.codes for d in ds]), torch.cat([d.scales for d in ds]), widths,
+                        torch.cat([d.global_scale for d in ds]), torch.float32)
+    ys, ts = zip(*(ref.mx_gemm(oa, o) for o in segs))
+    assert_gemm_close(y, np.concatenate(ys, axis=1), np.concatenate(ts, axis=1), "mx decode segments")
 
 
 def test_mx_gemm_full_prefill_shape_sampled_rows():
