@@ -1272,6 +1272,112 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(GemmArg
   decode_epilogue<GATES>(g, red, reinterpret_cast<float*>(lds), wave, lane, n0, n_end);
 }
 
+// M <= 16 tokens on MXFP4 operands with K a multiple of 512: the K-split scheme above (each
+// wavefront copies and multiplies its own contiguous range of 256-wide stages through a
+// private LDS ring: W rows 0-31 in chunks 0-3, token rows 0-15 in chunks 4-5), with the
+// scaled FP4 MFMA reading its operands from the ring.  MX scale bytes are 8 per row and
+// stage, so one 1 KB scale chunk holds 16 stages of 8 rows (16 B piece p of a row = stages
+// 2p and 2p+1); K % 512 == 0 and an even first stage per wavefront keep every piece whole and
+// 16-byte aligned.  Lane (r, h) multiplies MX block 4h + c of the stage in chunk c for W row r
+// and token row r mod 16 (lanes 16-31 read the same LDS rows as 0-15; their outputs are not
+// stored), with the stage's scale dword at byte 4h of its 8.
+__global__ __launch_bounds__(kDecodeThreads) void gemm_mx_decode_lds_kernel(GemmArgs g, int rows_per_wg) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int i8 = lane >> 3, r = lane & 31, h = lane >> 5;
+  const int n0 = blockIdx.x * rows_per_wg;              // rows [n0, n_end), at most 32
+  const int n_end = min(n0 + rows_per_wg, g.N);
+  const uint32_t kb = (uint32_t)g.K / 2, kx = (uint32_t)g.K / 32;
+  const int pairs = g.K / 512;
+  const int s0 = 2 * (wave * pairs / kDecodeWaves), cnt = 2 * ((wave + 1) * pairs / kDecodeWaves) - s0;
+  uint8_t* region = lds + wave * kDlWaveBytes;
+
+  uint32_t row_codes[kDlChunks], row_scales[kDlChunks];
+#pragma unroll
+  for (int c = 0; c < kDlChunks; ++c) {
+    const int rw = c < 4 ? min(8 * c + i8, n_end - 1 - n0) : min(8 * (c - 4) + i8, g.M - 1);
+    row_codes[c] = (uint32_t)rw * kb;
+    row_scales[c] = (uint32_t)rw * kx;
+  }
+  const uint8_t* wcb = g.w_codes + (size_t)n0 * kb;
+  const uint8_t* wxb = g.w_scales + (size_t)n0 * kx;
+  const uint32_t last_piece = kx - 16;
+  auto copy_codes = [&](int t) {      // stage t of this wavefront (clamped to its last)
+    const uint32_t col = (uint32_t)(s0 + min(t, cnt - 1)) * 128;
+    uint8_t* dst = region + (t % kDlDepth) * kDlStageBytes;
+#pragma unroll
+    for (int c = 0; c < kDlChunks; ++c)
+      dl_copy_chunk(c < 4 ? wcb : g.a_codes, row_codes[c], col, lane, dst + c * 1024);
+  };
+  auto copy_scales = [&](int b) {     // scale bytes of stages 16b .. 16b + 15 of this wavefront
+    const uint32_t col = (uint32_t)(s0 + 16 * b) * 8;
+    uint8_t* dst = region + kDlDepth * kDlStageBytes + (b & 1) * kDlScaleBytes;
+    const uint32_t p16 = (uint32_t)(((lane & 7) ^ i8) * 16);
+#pragma unroll
+    for (int c = 0; c < kDlChunks; ++c)   // pieces past the row's end (never read) clamped in bounds
+      copy16_to_lds(c < 4 ? wxb : g.a_scales, row_scales[c] + min(col + p16, last_piece), dst + c * 1024);
+  };
+
+  f32x16_t acc = f32x16_t{};
+  if (cnt > 0) {
+    copy_scales(0);
+#pragma unroll
+    for (int t = 0; t < kDlDepth; ++t) copy_codes(t);
+    const int iw = r & 7, wch = r >> 3, ach = 4 + ((r & 15) >> 3);
+    for (int t = 0; t < cnt; ++t) {
+      // Stage t's copies (and its scale block) are older than the copies of the next
+      // kDlDepth - 1 stages: at most that many may still be in flight.
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDlChunks * (kDlDepth - 1)));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      const uint8_t* cs = region + (t % kDlDepth) * kDlStageBytes;
+      const uint8_t* ss = region + kDlDepth * kDlStageBytes + ((t >> 4) & 1) * kDlScaleBytes;
+      const int sp = dl_slot(iw, (t & 15) >> 1) + 8 * (t & 1) + 4 * h;
+      const uint32_t ws = *reinterpret_cast<const uint32_t*>(ss + wch * 1024 + sp);
+      const uint32_t as = *reinterpret_cast<const uint32_t*>(ss + ach * 1024 + sp);
+      uint4 w[4], a[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        w[c] = *reinterpret_cast<const uint4*>(cs + wch * 1024 + dl_slot(iw, 4 * h + c));
+        a[c] = *reinterpret_cast<const uint4*>(cs + ach * 1024 + dl_slot(iw, 4 * h + c));
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4_operand(a[c]), fp4_operand(w[c]), acc, 4, 4, 0,
+                                                              (int)(as >> (8 * c)), 0, (int)(ws >> (8 * c)));
+      __builtin_amdgcn_sched_barrier(0);
+      // The slot just read is refilled with stage t + kDlDepth; a scale block is refilled
+      // once its 16 stages are done.  The MFMAs may be scheduled after the refill copies, so
+      // the stage's LDS reads are waited for here, before any copy can overwrite them.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0)
+      copy_codes(t + kDlDepth);
+      if (((t + kDlDepth) & 15) == 0) copy_scales((t + kDlDepth) >> 4);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  asm volatile("" ::: "memory");
+  __syncthreads();              // every wavefront is done with its ring: the sum reuses LDS
+  f32x16_t* red = reinterpret_cast<f32x16_t*>(lds);
+  red[wave * 64 + lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    // D[m][n] of the 32 x 32 tile sits in lane n + 32 (m / 4 % 2), register 4 (m / 8) + m % 4;
+    // tokens m < 16 are registers 0 .. 7.
+    f32x16_t sum = red[lane];
+    for (int w = 1; w < kDecodeWaves; ++w) sum += red[w * 64 + lane];
+    const int n = n0 + r;
+    if (n < n_end) {
+      const float sw = w_global_at(g, n);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int m = 8 * (q >> 2) + 4 * h + (q & 3);
+        if (m < g.M) store_out(g, m, n, (sum[q] * g.a_global[g.a_per_row ? m : 0]) * sw);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ decode, balanced rows
 
 // M <= 16 tokens, K a multiple of 256, one launch in which every CU streams the same bytes:
@@ -1650,6 +1756,8 @@ int decode_kernels_ready(int& cus) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_decode_lds_kernel<false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kDlLds) != hipSuccess ||
         hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_decode_lds_kernel<true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kDlLds) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_mx_decode_lds_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kDlLds) != hipSuccess)
       return NVFP4_ERR_HIP;
     int st = set_decode_rows_lds<1>();
@@ -1786,6 +1894,15 @@ int launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, cons
   if (K % BK != 0 || K >= (1 << 24)) return NVFP4_ERR_UNSUPPORTED;
   const GemmArgs g = gemm_args(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales,
                                w_globals, seg, y, y_dtype, ldy);
+  if (M <= 16 && K % 512 == 0) {
+    // Rows per workgroup about N / CUs (16 to 32), so that every CU takes a share.
+    int cus = 0;
+    const int st = decode_kernels_ready(cus);
+    if (st != NVFP4_OK) return st;
+    const int r = (int)std::min<int64_t>(32, std::max<int64_t>(16, (N + cus - 1) / cus));
+    gemm_mx_decode_lds_kernel<<<(unsigned)((N + r - 1) / r), kDecodeThreads, kDlLds, stream>>>(g, r);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+  }
   if (M <= 16) {
     gemm_mx_decode_kernel<<<(unsigned)((N + kMxDecodeRows - 1) / kMxDecodeRows), kMxDecodeThreads, 0, stream>>>(g);
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;

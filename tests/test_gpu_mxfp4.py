@@ -106,10 +106,13 @@ def _mx_device(o: ref.MXFP4):
                             torch.from_numpy(np.asarray(o.global_scale, np.float32)).to(DEV))
 
 
-# M <= 16: the MXFP4 decode kernel (32 W rows per workgroup, K split over 4 wavefronts).
+# M <= 16: the MXFP4 decode kernels.  K % 512 == 0: LDS rings (16 to 32 W rows per workgroup,
+# stage pairs split over 4 wavefronts, scale blocks of 16 stages); other K: from registers.
 @pytest.mark.parametrize("M,N,K", [(1, 17408, 5120), (16, 17408, 5120), (16, 5120, 17408),  # MLP up / down
-                                   (8, 1000, 1280),     # 5 stages over 4 wavefronts; last workgroup 8 rows
-                                   (2, 64, 256),        # one stage: three wavefronts idle
+                                   (7, 2000, 1536),     # 16-row workgroups, 3 stage pairs over 4 wavefronts
+                                   (3, 640, 32768),     # 32 stages per wavefront: two scale blocks each
+                                   (8, 1000, 1280),     # registers: 5 stages over 4 wavefronts
+                                   (2, 64, 256),        # registers: one stage, three wavefronts idle
                                    (11, 4128, 2304)])
 def test_mx_decode(M, N, K):
     g = np.random.default_rng(M * 7919 + N + K)
@@ -121,8 +124,9 @@ def test_mx_decode(M, N, K):
         assert_gemm_close(y, Y, T, f"mx decode {M}x{N}x{K} {out_dtype}")
 
 
-def test_mx_decode_segments():
-    M, K, widths = 4, 768, (96, 48, 48, 40)
+@pytest.mark.parametrize("K", [768, 1024])
+def test_mx_decode_segments(K):
+    M, widths = 4, (96, 48, 48, 40)
     g = np.random.default_rng(17)
     oa = _random_mx(g, M, K, per_row=True)
     segs = [_random_mx(g, n, K) for n in widths]
