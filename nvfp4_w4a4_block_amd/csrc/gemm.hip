@@ -1433,7 +1433,8 @@ inline int dw_lds_bytes(int G, int64_t K) {
     case 3: return dw_lds_bytes_g<3>(K);
     case 4: return dw_lds_bytes_g<4>(K);
     case 5: return dw_lds_bytes_g<5>(K);
-    default: return dw_lds_bytes_g<kDwPairG>(K);
+    case kDwPairG: return dw_lds_bytes_g<kDwPairG>(K);
+    default: return 0;
   }
 }
 
@@ -1858,7 +1859,8 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
         case 3: launch_decode_rows<3>(g, gated, rows, lds_bytes, stream); break;
         case 4: launch_decode_rows<4>(g, gated, rows, lds_bytes, stream); break;
         case 5: launch_decode_rows<5>(g, gated, rows, lds_bytes, stream); break;
-        default: launch_decode_rows<kDwPairG>(g, gated, rows, lds_bytes, stream); break;
+        case kDwPairG: launch_decode_rows<kDwPairG>(g, gated, rows, lds_bytes, stream); break;
+        default: return NVFP4_ERR_UNSUPPORTED;   // not reached: the plan caps the rows
       }
     }
   } else if (M <= 16) {
