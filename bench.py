@@ -455,10 +455,52 @@ def bench_sweep(nv, steps: int, warmup: int, settle_s: float = 0.0):
         kinds[kind] = {"N": L.N, "K": L.K, "segments": len(L.widths), "count": sum(1 for x in launches if x.kind == kind),
                        "gemm_ms": round(kms, 4), "tflops": round(f / (kms * 1e-3) / 1e12, 1)}
     nvfp4_bytes = sum(int(c.numel() + s_.numel() + 4 * g.numel()) for c, s_, g in weights)
+    chain = _sweep_mlp_chain(nv, sw, launches, weights, xs, aq, ys, flops, steps, warmup, settle_s)
     return {"launches": len(launches), "tflop": round(flops / 1e12, 1), "ms_per_sweep": round(ms, 3),
             "tflops": round(flops / (ms * 1e-3) / 1e12, 1), "frac_mfma_f16": round(flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
             "weights_nvfp4_gb": round(nvfp4_bytes / 1e9, 2), "per_kind": kinds,
-            "note": "each launch: per-tensor quantize of its activation + fused NVFP4 GEMM to bf16"}
+            "note": "each launch: per-tensor quantize of its activation + fused NVFP4 GEMM to bf16",
+            "mlp_chain": chain}
+
+
+def _sweep_mlp_chain(nv, sw, launches, weights, xs, aq, ys, flops, steps, warmup, settle_s):
+    """The same sweep with each MLP run as a model runs it: quantize x, the fused gate+up GEMM
+    with its SwiGLU epilogue writing h as NVFP4 (under one calibrated global scale), then the
+    down projection straight on that h -- no bf16 gate/up output and no separate quantize of
+    the down projection's input.  The other launches are unchanged."""
+    dev = torch.device("cuda:0")
+    inter = {}
+    for li, L in enumerate(launches):
+        if L.kind == "mlp_gate_up":
+            c, s_, g = weights[li]
+            f = L.widths[0]
+            gate = nv.NVFP4Tensor(c[:f], s_[:f], g[0:1])
+            up = nv.NVFP4Tensor(c[f:], s_[f:], g[1:2])
+            inter[li] = nv.interleave_gate_up(gate, up) + (g,)
+    first = min(inter)
+    wc, ws, wg = inter[first]
+    hb, _ = nv.gemm_swiglu(aq[sw.hidden], wc, ws, wg, torch.bfloat16)
+    hg = (hb.float().abs().max() / 2688.0).reshape(1)          # calibration (offline)
+    del hb
+    _, hq = nv.gemm_swiglu(aq[sw.hidden], wc, ws, wg, None, hg)
+    y_h = ys[sw.hidden]
+
+    def step(i):
+        for li, (L, (c, s_, g)) in enumerate(zip(launches, weights)):
+            if L.kind == "mlp_gate_up":
+                a = nv.quantize(xs[L.K], out=aq[L.K])
+                w_c, w_s, w_g = inter[li]
+                nv.gemm_swiglu(a, w_c, w_s, w_g, None, hg, q_out=hq)
+            elif L.kind == "mlp_down":
+                nv.gemm(hq, nv.NVFP4Tensor(c, s_, g), torch.bfloat16, out=y_h)
+            else:
+                a = nv.quantize(xs[L.K], out=aq[L.K])
+                nv.gemm_fused_segments(a, c, s_, L.widths, g, torch.bfloat16, out=ys[L.N])
+
+    ms = _mean_ms(step, max(1, steps), warmup, settle_s)
+    del inter
+    return {"ms_per_sweep": round(ms, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "note": "MLP: quantize x + SwiGLU GEMM to NVFP4 h + down GEMM on h; other launches as above"}
 
 
 def bench_mxfp4(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: int = 8):
