@@ -609,7 +609,8 @@ def bench_swiglu(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: int
     plain fused gate+up GEMM with bf16 output of the same operands (what an MLP without the
     epilogue launches before a separate activation pass): prefill M = 4096 (per-tensor
     activation scale) and decode M in {1, 16} (per-token scales; 4 weight copies rotating so W
-    never comes from the 256 MB cache)."""
+    never comes from the 256 MB cache); and the whole MLP layer as a chain: quantize x, the
+    SwiGLU GEMM to NVFP4 h, the down projection W[5120 x 17408] on h."""
     m = workloads.MLP
     dev = torch.device("cuda:0")
     gate = nv.quantize(torch.from_numpy(m.gate()).to(dev).to(torch.bfloat16))
@@ -618,11 +619,15 @@ def bench_swiglu(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: int
     wc, ws = nv.interleave_gate_up(gate, up)
     fc, fs = torch.cat([gate.codes, up.codes]), torch.cat([gate.scales, up.scales])
     del gate, up
-    copies = [(wc, ws, fc, fs)] + [tuple(t.clone() for t in (wc, ws, fc, fs)) for _ in range(rotate - 1)]
+    down = nv.quantize(torch.from_numpy(workloads.DECODE.w()).to(dev).to(torch.bfloat16))   # [5120 x 17408]
+    copies = [(wc, ws, fc, fs, down.codes, down.scales)] + [
+        tuple(t.clone() for t in (wc, ws, fc, fs, down.codes, down.scales)) for _ in range(rotate - 1)]
     F, K = m.F, m.K
     out = {"F": F, "K": K}
     for M in (m.M,) + m.Ms:
-        a = nv.quantize(torch.from_numpy(m.x(M)).to(dev).to(torch.bfloat16), "per_tensor" if M == m.M else "per_row")
+        mode = "per_tensor" if M == m.M else "per_row"
+        x = torch.from_numpy(m.x(M)).to(dev).to(torch.bfloat16)
+        a = nv.quantize(x, mode)
         rot = 1 if M == m.M else rotate
         hb = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
         nv.gemm_swiglu(a, wc, ws, wg, torch.bfloat16, out=hb)
@@ -637,7 +642,16 @@ def bench_swiglu(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: int
         t_q = _mean_ms(lambda i: nv.gemm_swiglu(a, c(i)[0], c(i)[1], wg, None, hg, q_out=q), steps, warmup, settle_s)
         flops = 2.0 * M * 2 * F * K
         wbytes = 2 * F * K * (0.5 + 1 / 16)
-        r = {"fused_gemm_bf16_us": t_fused * 1e3, "swiglu_bf16_us": t_bf16 * 1e3, "swiglu_nvfp4_us": t_q * 1e3}
+        yd = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+
+        def layer(i):           # the whole MLP: quantize x, SwiGLU GEMM to NVFP4 h, down GEMM on h
+            nv.quantize(x, mode, out=a)
+            nv.gemm_swiglu(a, c(i)[0], c(i)[1], wg, None, hg, q_out=q)
+            nv.gemm(q, nv.NVFP4Tensor(c(i)[4], c(i)[5], down.global_scale), torch.bfloat16, out=yd)
+
+        t_layer = _mean_ms(layer, steps, warmup, settle_s)
+        r = {"fused_gemm_bf16_us": t_fused * 1e3, "swiglu_bf16_us": t_bf16 * 1e3, "swiglu_nvfp4_us": t_q * 1e3,
+             "mlp_layer_us": t_layer * 1e3}
         if M == m.M:
             r["swiglu_nvfp4_tflops"] = flops / (t_q * 1e-3) / 1e12
             r["swiglu_nvfp4_frac_mfma_f16"] = r["swiglu_nvfp4_tflops"] / MFMA_F16_PEAK_TFLOPS
