@@ -224,8 +224,8 @@ int nvfp4_to_mxfp4(int64_t rows, int64_t cols, const uint8_t* codes, const uint8
  * stored as fp32 or bf16 (round to nearest even).  Operands as nvfp4_to_mxfp4 writes them;
  * the global scales are the NVFP4 tensors' own.  With the operands re-encoded from NVFP4 this
  * is a lossy variant of nvfp4_gemm_fused_segments.
- *   K a multiple of 256 below 2^24 (other K: NVFP4_ERR_UNSUPPORTED); any M >= 0 (tuned for
- *   M > 16).  a_scales [M, K/32], w_scales [N, K/32], 16-byte aligned.
+ *   K a multiple of 256 below 2^24 (other K: NVFP4_ERR_UNSUPPORTED); any M >= 0 (M <= 16 runs
+ *   a decode kernel that streams W).  a_scales [M, K/32], w_scales [N, K/32], 16-byte aligned.
  *   Other arguments as in nvfp4_gemm_fused_segments (one segment: a plain GEMM).
  */
 int nvfp4_mxfp4_gemm(int64_t M, int64_t K,
