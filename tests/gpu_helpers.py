@@ -107,3 +107,28 @@ def assert_gates_close(g: torch.Tensor, beta: torch.Tensor, Y: np.ndarray, T: np
         bad = np.argwhere(~(err <= bound))
         assert bad.size == 0, (f"{what} {name}: {len(bad)} out of tolerance, first {bad[:3].tolist()} "
                                f"got {got[tuple(bad[0])]} want {want[tuple(bad[0])]}")
+
+
+def swiglu_bound(H, yg, tg, yu, tu, h: torch.Tensor) -> np.ndarray:
+    """Allowed |h - H| for the SwiGLU epilogue: the GEMM bound 1e-4 * T of each product moved
+    through silu (slope at most 1.1 in magnitude) and the product, plus (|y_gate| + 4) 2^-23 of
+    H for the fp32 evaluation (hardware exponential and reciprocal within one ulp each, on an
+    argument rounded to fp32), plus 1e-30 (silu of y < -88 flushes to -0), plus half a bf16 ulp
+    for bf16 h."""
+    eg, eu = 1e-4 * tg, 1e-4 * tu
+    b = 1.1 * eg * (np.abs(yu) + eu) + np.abs(ref.silu(yg)) * eu + (np.abs(yg) + 4.0) * 2.0**-23 * np.abs(H) + 1e-30
+    if h.dtype == torch.bfloat16:
+        hh = h.float().cpu().numpy().astype(np.float64)
+        b = b + half_ulp_bf16(np.maximum(np.abs(hh), np.abs(H)))
+    return b
+
+
+def assert_swiglu_close(h: torch.Tensor, H, yg, tg, yu, tu, what: str = "") -> float:
+    hh = h.float().cpu().numpy().astype(np.float64)
+    err = np.abs(hh - H)
+    bound = swiglu_bound(H, yg, tg, yu, tu, h)
+    bad = np.argwhere(~(err <= bound))
+    worst = float(np.max(err / bound))
+    assert bad.size == 0, (f"{what}: {len(bad)} of {H.size} values out of tolerance, first {bad[:3].tolist()}, "
+                           f"max err/bound {worst:.3g}")
+    return worst

@@ -4,14 +4,15 @@ of each kind is run: the GDN input projection (six segments, own global scales),
 projection, the fused attention q/k/v and the attention output, the fused MLP gate+up and the
 MLP down projection.  Activations and weights are quantized on the GPU; sampled rows of both are
 checked bit-exact against the oracle (per-tensor scale from the whole tensor's amax), then 64
-sampled output rows of the (fused) GEMM against the oracle's GEMM on the same operands."""
+sampled output rows of the (fused) GEMM against the oracle's GEMM on the same operands.  The
+MLP gate+up launch is also run with its SwiGLU epilogue, as the sweep's MLP chain runs it."""
 import numpy as np
 import pytest
 import torch
 
 import workloads
 from oracle import nvfp4_ref as ref
-from tests.gpu_helpers import DEV, assert_gemm_close, assert_quant_equal, nv, to_gpu, to_host
+from tests.gpu_helpers import DEV, assert_gemm_close, assert_quant_equal, assert_swiglu_close, nv, to_gpu, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -48,3 +49,31 @@ def test_sweep_launch(kind):
     Y, T = ref.fused_segments(oa, osegs, rows)
     worst = assert_gemm_close(y[torch.from_numpy(rows).to(DEV)], Y, T, f"{kind} {sw.M}x{L.N}x{L.K}")
     print(f"{kind}: M={sw.M} N={L.N} K={L.K} segments={len(L.widths)} max err/T {worst:.3g}")
+
+
+def test_sweep_mlp_swiglu():
+    # The MLP gate+up launch as the sweep's MLP chain runs it: the SwiGLU epilogue on the
+    # interleaved weights, h as fp32 and as NVFP4 in one launch; 64 sampled rows of h against
+    # the oracle, and their NVFP4 encoding bit-exact against the oracle's GIVEN-mode quantize of
+    # the same launch's fp32 h.
+    sw = workloads.SWEEP
+    launches = workloads.sweep_launches(sw)
+    idx = next(i for i, l in enumerate(launches) if l.kind == "mlp_gate_up")
+    L = launches[idx]
+    F = L.widths[0]
+    rng = np.random.default_rng(2000 + idx)
+    rows = np.sort(rng.choice(sw.M, 64, replace=False))
+    a, oa = _quantized_sampled(sw.x(idx, L.K), rows, "mlp x")
+    (g, og), (u, ou) = [_quantized_sampled(sw.w(idx, s, F, L.K), np.sort(rng.choice(F, 32, replace=False)),
+                                           f"mlp w{s}") for s in range(2)]
+    wc, ws = nv().interleave_gate_up(g, u)
+    wg = torch.cat([g.global_scale, u.global_scale])
+    H, yg, tg, yu, tu = ref.swiglu_mlp(oa, og, ou, rows)
+    s_h = np.float32(np.max(np.abs(H)) / 2688.0)
+    h, q = nv().gemm_swiglu(a, wc, ws, wg, torch.float32, torch.tensor([s_h], dtype=torch.float32, device=DEV))
+    sel = torch.from_numpy(rows).to(DEV)
+    worst = assert_swiglu_close(h[sel], H, yg, tg, yu, tu, f"swiglu {sw.M}x{2 * F}x{L.K}")
+    want = ref.quantize(h[sel].cpu().numpy(), ref.GIVEN, float(s_h))
+    assert np.array_equal(q.scales[sel].cpu().numpy(), want.scales)
+    assert np.array_equal(q.codes[sel].cpu().numpy(), want.codes)
+    print(f"mlp swiglu: M={sw.M} F={F} K={L.K} max err/bound {worst:.3g}")

@@ -18,7 +18,7 @@ import torch
 
 import workloads
 from oracle import nvfp4_ref as ref
-from tests.gpu_helpers import DEV, half_ulp_bf16, nv, to_device
+from tests.gpu_helpers import DEV, assert_swiglu_close, nv, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -49,25 +49,8 @@ def _random_operands(seed, M, F, K):
     return oa, operand(F, [4.0 * unit]), operand(F, [2.0 * unit])
 
 
-def _bound(H, yg, tg, yu, tu, h):
-    eg, eu = 1e-4 * tg, 1e-4 * tu
-    # fp32 evaluation: the exponential's argument -y log2(e) rounded to fp32 moves e^-y by up to
-    # |y| 2^-24 relative; the exponential and reciprocal (1 ulp each), the addition and the two
-    # products add a few more ulps.
-    b = 1.1 * eg * (np.abs(yu) + eu) + np.abs(ref.silu(yg)) * eu + (np.abs(yg) + 4.0) * 2.0**-23 * np.abs(H) + 1e-30
-    if h.dtype == torch.bfloat16:
-        hh = h.float().cpu().numpy().astype(np.float64)
-        b = b + half_ulp_bf16(np.maximum(np.abs(hh), np.abs(H)))
-    return b
-
-
 def _assert_h_close(h, H, yg, tg, yu, tu, what):
-    hh = h.float().cpu().numpy().astype(np.float64)
-    err = np.abs(hh - H)
-    bound = _bound(H, yg, tg, yu, tu, h)
-    bad = np.argwhere(~(err <= bound))
-    assert bad.size == 0, (f"{what}: {len(bad)} of {H.size} values out of tolerance, first {bad[:3].tolist()}, "
-                           f"max err/bound {float(np.max(err / bound)):.3g}")
+    assert_swiglu_close(h, H, yg, tg, yu, tu, what)
 
 
 def _launch(oa, og, ou):
