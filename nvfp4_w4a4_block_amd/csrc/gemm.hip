@@ -1897,11 +1897,14 @@ int launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, cons
   const GemmArgs g = gemm_args(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales,
                                w_globals, seg, y, y_dtype, ldy);
   if (M <= 16 && K % 512 == 0) {
-    // Rows per workgroup about N / CUs (16 to 32), so that every CU takes a share.
+    // Rows per workgroup: the fewest rounds of 32-row workgroups over the CUs, the rows then
+    // spread evenly over the workgroups of those rounds (16 to 32 rows), so that no CU takes a
+    // whole extra workgroup in a short last round.
     int cus = 0;
     const int st = decode_kernels_ready(cus);
     if (st != NVFP4_OK) return st;
-    const int r = (int)std::min<int64_t>(32, std::max<int64_t>(16, (N + cus - 1) / cus));
+    const int64_t rounds = (N + 32 * cus - 1) / (32 * cus);
+    const int r = (int)std::min<int64_t>(32, std::max<int64_t>(16, (N + cus * rounds - 1) / (cus * rounds)));
     gemm_mx_decode_lds_kernel<<<(unsigned)((N + r - 1) / r), kDecodeThreads, kDlLds, stream>>>(g, r);
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
   }
