@@ -1623,6 +1623,176 @@ __global__ __launch_bounds__(kDwThreads) void gemm_decode_rows_kernel(GemmArgs g
   }
 }
 
+// ------------------------------------------------------------------ MXFP4 decode, balanced rows
+
+// M <= 16 tokens on MXFP4 operands, N > 32 x CUs, K % 512 == 0: the balanced-rows scheme of
+// gemm_decode_rows_kernel with G groups of 32 W rows (one scaled 32 x 32 x 64 MFMA group
+// each).  The 8 wavefronts share one ring of kDepth 256-wide stages (wavefronts 0-3 copy,
+// kSteps stages per barrier); every scale byte of the workgroup's rows is copied up front.
+// Wavefront w multiplies the 64-element piece w % 4 of every stage for the groups w / 4,
+// w / 4 + 2, ...: lane (r, h) takes MX block 2 (w % 4) + h of W row r of the group and of token
+// row r mod 16.  The 4 wavefronts of a group are summed through LDS in a fixed order.  MX scale
+// bytes are 8 per row and stage: a 1 KB scale chunk holds 16 stages of 8 rows (16 B piece q of a
+// row = stages 2q, 2q+1), so K % 512 == 0 keeps every piece whole.
+template <int G> struct MxDwCfg {
+  static constexpr int kChunks = 4 * G + 2;             // 1 KB chunks per stage: W rows, then tokens
+  static constexpr int kPerWave = (kChunks + 3) / 4;    // copies per copying wavefront per stage
+  static constexpr int kStageBytes = kChunks * 1024;
+  static constexpr int kSteps = 2;                      // stages per barrier
+  static constexpr int kDepth = 8;                      // stages in the ring
+  static constexpr int kScratch = kDepth * kStageBytes; // 1 KB target of padding copies
+  static constexpr int kScales = kScratch + 1024;       // scale chunks: block b, chunk c at (b kChunks + c) KB
+};
+// LDS bytes of the balanced MXFP4 decode kernel for G groups and K (0 if K does not fit).
+template <int G>
+int mx_dw_lds_bytes_g(int64_t K) {
+  using C = MxDwCfg<G>;
+  const int64_t blocks = (K / 256 + 15) / 16;
+  const int64_t bytes = C::kScales + blocks * C::kChunks * 1024;
+  return bytes <= 160 * 1024 ? (int)bytes : 0;
+}
+
+// s_waitcnt for at most n stages of P copies each still in flight (n <= 4).
+template <int P>
+__device__ __forceinline__ void mx_dw_wait_stages(int n) {
+  static_assert(4 * P <= 63, "wait cases");
+  switch (n) {
+    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * P)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * P)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * P)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(1 * P)); break;
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(kDwThreads) void gemm_mx_decode_rows_kernel(GemmArgs g, int rows_per_wg) {
+  using C = MxDwCfg<G>;
+  constexpr int S = C::kSteps, D = C::kDepth, NA = (G + 1) / 2;
+  static_assert(D - 2 * S <= 4, "wait cases");
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int r0 = blockIdx.x * rows_per_wg;
+  const int rw = min(rows_per_wg, g.N - r0);             // rows of this workgroup (>= 1)
+  const uint32_t kb = (uint32_t)g.K / 2, kx = (uint32_t)g.K / 32;
+  const int nst = g.K / 256;
+  const uint8_t* wcb = g.w_codes + (size_t)r0 * kb;
+  const uint8_t* wxb = g.w_scales + (size_t)r0 * kx;
+
+  // Row of the stage's row list that lane l copies in chunk c: W row min(8c + l/8, rw - 1) of
+  // the workgroup, or token row min(8(c - 4G) + l/8, M - 1); chunks past the list copy row 0.
+  auto list_row = [&](int c, uint32_t pitch) -> uint32_t {
+    const int i = lane >> 3;
+    if (c < 4 * G) return (uint32_t)min(8 * c + i, rw - 1) * pitch;
+    if (c < C::kChunks) return (uint32_t)min(8 * (c - 4 * G) + i, g.M - 1) * pitch;
+    return 0u;
+  };
+  const bool copier = wave < 4;
+  uint32_t row_off[C::kPerWave];
+#pragma unroll
+  for (int i = 0; i < C::kPerWave; ++i) row_off[i] = list_row((wave & 3) + 4 * i, kb);
+  // Lane l copies 16 B piece (l & 7) ^ (l >> 3) of row l >> 3 into slot l & 7 of that row.
+  const uint32_t piece16 = (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
+  auto copy_codes = [&](int t) {
+    uint8_t* stage = lds + (t % D) * C::kStageBytes;
+#pragma unroll
+    for (int i = 0; i < C::kPerWave; ++i) {
+      const int c = (wave & 3) + 4 * i;
+      if (c < C::kChunks)
+        copy16_to_lds(c < 4 * G ? wcb : g.a_codes, row_off[i] + piece16 + (uint32_t)t * 128, stage + c * 1024);
+      else
+        copy16_to_lds(wcb, row_off[i] + piece16 + (uint32_t)t * 128, lds + C::kScratch);
+    }
+  };
+
+  // Scale bytes, all stages: block b (stages 16b .. 16b+15), chunk c = rows 8c .. 8c+7, piece q
+  // of a row = stages 16b + 2q and 16b + 2q + 1; pieces past the last stage repeat the last pair.
+  {
+    const int nblk = (nst + 15) / 16;
+    const int q = (lane & 7) ^ (lane >> 3);
+    for (int e = wave; e < nblk * C::kChunks; e += 8) {
+      const int b = e / C::kChunks, c = e - b * C::kChunks;
+      const uint32_t off = list_row(c, kx) + (uint32_t)min(16 * b + 2 * q, nst - 2) * 8;
+      copy16_to_lds(c < 4 * G ? wxb : g.a_scales, off, lds + C::kScales + e * 1024);
+    }
+  }
+  if (copier) {
+    for (int t = 0; t < D - S && t < nst; ++t) copy_codes(t);
+  } else {
+    // The loop's waits count stage copies, which these wavefronts do not issue: their scale
+    // copies must be complete before the first barrier.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+
+  const int r = lane & 31, h = lane >> 5, piece = wave & 3, iw = r & 7;
+  const int tok = 4 * G + ((r & 15) >> 3);                // token chunk of this lane
+  const int code_slot = dl_slot(iw, 2 * piece + h);
+  const uint32_t ssh = 8u * (uint32_t)((2 * piece + h) & 3);
+  f32x16_t acc[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) acc[i] = f32x16_t{};
+
+  for (int t0 = 0; t0 < nst; t0 += S) {
+    // Stages t0 .. t0+S-1 must be complete; copies issued after them (up to stage
+    // t0 + D - S - 1, at most D - 2S stages) may still be in flight.
+    mx_dw_wait_stages<C::kPerWave>(min(t0 + D - S - 1, nst - 1) - min(t0 + S - 1, nst - 1));
+    asm volatile("" ::: "memory");
+    __syncthreads();            // this step's stages copied by every wavefront; the last step's read by all
+    if (copier) {
+#pragma unroll
+      for (int u = 0; u < S; ++u)
+        if (t0 + D - S + u < nst) copy_codes(t0 + D - S + u);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      const int t = t0 + u;
+      if (t < nst) {
+        const uint8_t* stage = lds + (t % D) * C::kStageBytes;
+        const uint8_t* sc = lds + C::kScales + (t >> 4) * C::kChunks * 1024;
+        const int sp = dl_slot(iw, (t & 15) >> 1) + 8 * (t & 1) + 4 * (piece >> 1);
+        const uint4 a = *reinterpret_cast<const uint4*>(stage + tok * 1024 + code_slot);
+        const uint32_t as = *reinterpret_cast<const uint32_t*>(sc + tok * 1024 + sp) >> ssh;
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+          const int j = (wave >> 2) + 2 * i;              // W group
+          if (j < G) {
+            const int wc = 4 * j + (r >> 3);
+            const uint4 w = *reinterpret_cast<const uint4*>(stage + wc * 1024 + code_slot);
+            const uint32_t ws = *reinterpret_cast<const uint32_t*>(sc + wc * 1024 + sp) >> ssh;
+            acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4_operand(a), fp4_operand(w), acc[i], 4, 4,
+                                                                     0, (int)as, 0, (int)ws);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // Sum the four wavefronts of each group in a fixed order, then scale and store.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  asm volatile("" ::: "memory");
+  __syncthreads();              // every wavefront is done with the ring
+  f32x16_t* red = reinterpret_cast<f32x16_t*>(lds);
+#pragma unroll
+  for (int i = 0; i < NA; ++i) red[(wave * NA + i) * 64 + lane] = acc[i];
+  __syncthreads();
+  if (wave < G) {
+    const int j = wave, half = j & 1, i = j >> 1;
+    f32x16_t sum = red[((4 * half) * NA + i) * 64 + lane];
+    for (int p = 1; p < 4; ++p) sum += red[((4 * half + p) * NA + i) * 64 + lane];
+    const int nl = 32 * j + r, n = r0 + nl;
+    if (nl < rw) {
+      const float sw = w_global_at(g, n);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int m = 8 * (q >> 2) + 4 * h + (q & 3);
+        if (m < g.M) store_out(g, m, n, (sum[q] * g.a_global[g.a_per_row ? m : 0]) * sw);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ plain kernel
 
 __device__ __forceinline__ float e2m1_value(uint32_t c) {
@@ -1767,6 +1937,12 @@ int decode_kernels_ready(int& cus) {
     if (st == NVFP4_OK) st = set_decode_rows_lds<4>();
     if (st == NVFP4_OK) st = set_decode_rows_lds<5>();
     if (st == NVFP4_OK) st = set_decode_rows_lds<kDwPairG>();
+    if (st == NVFP4_OK &&
+        (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_mx_decode_rows_kernel<2>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess ||
+         hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_mx_decode_rows_kernel<3>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess))
+      st = NVFP4_ERR_HIP;
     if (st != NVFP4_OK) return st;
     if (hipDeviceGetAttribute(&cu_count[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return NVFP4_ERR_HIP;
@@ -1774,6 +1950,19 @@ int decode_kernels_ready(int& cus) {
   }
   cus = cu_count[dev];
   return NVFP4_OK;
+}
+
+// Rows per workgroup of the balanced MXFP4 decode kernel: the fewest rounds over the CUs with at
+// most 96 rows per workgroup (64 where K leaves no room for three groups in LDS), the rows then
+// spread evenly over the workgroups of those rounds.  Returns the kernel's LDS bytes, 0 when it
+// does not apply (one group is enough, or K does not fit).
+int mx_decode_rows_plan(int64_t N, int64_t K, int cus, int& rows, int& groups) {
+  const int64_t cap = mx_dw_lds_bytes_g<3>(K) ? 96 : 64;
+  const int64_t rounds = (N + cus * cap - 1) / (cus * cap);
+  const int64_t r = (N + cus * rounds - 1) / (cus * rounds);
+  rows = (int)r;
+  groups = (int)((r + 31) / 32);
+  return groups == 3 ? mx_dw_lds_bytes_g<3>(K) : groups == 2 ? mx_dw_lds_bytes_g<2>(K) : 0;
 }
 
 template <int G>
@@ -1897,12 +2086,25 @@ int launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, cons
   const GemmArgs g = gemm_args(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales,
                                w_globals, seg, y, y_dtype, ldy);
   if (M <= 16 && K % 512 == 0) {
-    // Rows per workgroup: the fewest rounds of 32-row workgroups over the CUs, the rows then
-    // spread evenly over the workgroups of those rounds (16 to 32 rows), so that no CU takes a
-    // whole extra workgroup in a short last round.
     int cus = 0;
     const int st = decode_kernels_ready(cus);
     if (st != NVFP4_OK) return st;
+    if (N > 32 * (int64_t)cus) {
+      // More rows than one round of 32-row workgroups: the balanced kernel.
+      int rows = 0, groups = 0;
+      const int lds_bytes = mx_decode_rows_plan(N, K, cus, rows, groups);
+      if (lds_bytes > 0) {
+        const unsigned grid = (unsigned)((N + rows - 1) / rows);
+        if (groups == 3)
+          gemm_mx_decode_rows_kernel<3><<<grid, kDwThreads, lds_bytes, stream>>>(g, rows);
+        else
+          gemm_mx_decode_rows_kernel<2><<<grid, kDwThreads, lds_bytes, stream>>>(g, rows);
+        return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+      }
+    }
+    // Rows per workgroup: the fewest rounds of 32-row workgroups over the CUs, the rows then
+    // spread evenly over the workgroups of those rounds (16 to 32 rows), so that no CU takes a
+    // whole extra workgroup in a short last round.
     const int64_t rounds = (N + 32 * cus - 1) / (32 * cus);
     const int r = (int)std::min<int64_t>(32, std::max<int64_t>(16, (N + cus * rounds - 1) / (cus * rounds)));
     gemm_mx_decode_lds_kernel<<<(unsigned)((N + r - 1) / r), kDecodeThreads, kDlLds, stream>>>(g, r);

@@ -106,9 +106,15 @@ def _mx_device(o: ref.MXFP4):
                             torch.from_numpy(np.asarray(o.global_scale, np.float32)).to(DEV))
 
 
-# M <= 16: the MXFP4 decode kernels.  K % 512 == 0: LDS rings (16 to 32 W rows per workgroup,
-# stage pairs split over 4 wavefronts, scale blocks of 16 stages); other K: from registers.
-@pytest.mark.parametrize("M,N,K", [(1, 17408, 5120), (16, 17408, 5120), (16, 5120, 17408),  # MLP up / down
+# M <= 16: the MXFP4 decode kernels.  K % 512 == 0: the balanced kernel when N > 32 x CUs (two
+# or three 32-row groups per workgroup, 8 wavefronts on one ring), else per-wavefront LDS rings
+# (16 to 32 W rows per workgroup, stage pairs split over 4 wavefronts); other K: from registers.
+@pytest.mark.parametrize("M,N,K", [(1, 17408, 5120), (16, 17408, 5120),   # MLP up: balanced, 3 groups
+                                   (4, 9000, 1024),     # balanced, 2 groups
+                                   (9, 30000, 512),     # balanced, 2 rounds; one stage pair
+                                   (16, 16700, 10240),  # balanced, 3 groups; last workgroup 2 rows
+                                   (2, 12000, 14336),   # balanced, 2 groups: K too long for 3
+                                   (16, 5120, 17408),   # MLP down: per-wavefront rings
                                    (7, 2000, 1536),     # 16-row workgroups, 3 stage pairs over 4 wavefronts
                                    (3, 640, 32768),     # 32 stages per wavefront: two scale blocks each
                                    (8, 1000, 1280),     # registers: 5 stages over 4 wavefronts
@@ -124,9 +130,9 @@ def test_mx_decode(M, N, K):
         assert_gemm_close(y, Y, T, f"mx decode {M}x{N}x{K} {out_dtype}")
 
 
-@pytest.mark.parametrize("K", [768, 1024])
-def test_mx_decode_segments(K):
-    M, widths = 4, (96, 48, 48, 40)
+@pytest.mark.parametrize("K,widths", [(768, (96, 48, 48, 40)), (1024, (96, 48, 48, 40)), (1024, (5000, 48, 4000))])
+def test_mx_decode_segments(K, widths):
+    M = 4
     g = np.random.default_rng(17)
     oa = _random_mx(g, M, K, per_row=True)
     segs = [_random_mx(g, n, K) for n in widths]
