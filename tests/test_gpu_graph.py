@@ -147,3 +147,28 @@ def test_graph_fp8_kv_and_mxfp4():
                 nv().mxfp4_gemm(ae, w.codes, w.scales, (N,), w.global_scale, torch.float32))
 
     _replay_and_compare(g, x, M, K, (q, back, am.codes, am.scales, y), eager)
+
+
+@pytest.mark.parametrize("N,K", [(9000, 1024), (2048, 1024), (1000, 1280)])
+def test_graph_mxfp4_decode(N, K):
+    # The three MXFP4 decode kernels under capture: balanced rows (N > 32 x CUs), per-wavefront
+    # LDS rings (K % 512 == 0), and streaming from registers (other K); per-token scales.
+    M = 4
+    w = nv().to_mxfp4(nv().quantize(to_gpu(workloads.weight(205, 1, N, K))))
+    x = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+    _fill(x, 299, M, K)
+    a = nv().quantize(x, "per_row")
+    am = nv().to_mxfp4(a)
+    y = nv().mxfp4_gemm(am, w.codes, w.scales, (N,), w.global_scale, torch.float32)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        nv().quantize(x, "per_row", out=a)
+        nv().to_mxfp4(a, out=am)
+        nv().mxfp4_gemm(am, w.codes, w.scales, (N,), w.global_scale, torch.float32, out=y)
+
+    def eager():
+        ae = nv().to_mxfp4(nv().quantize(x, "per_row"))
+        return ae.codes, ae.scales, nv().mxfp4_gemm(ae, w.codes, w.scales, (N,), w.global_scale, torch.float32)
+
+    _replay_and_compare(g, x, M, K, (am.codes, am.scales, y), eager)
