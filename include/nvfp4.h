@@ -14,7 +14,9 @@
  *   6. the fused Gated DeltaNet input projection whose two gate segments leave as the
  *      write strength and the log-space decay, in the same launch;
  *   7. a lossy variant: NVFP4 re-encoded to MXFP4 and multiplied with gfx950's native scaled
- *      FP4 matrix instructions.
+ *      FP4 matrix instructions;
+ *   8. the gated MLP input projection: the fused gate+up GEMM with its SwiGLU activation in
+ *      the same launch, the result optionally leaving as NVFP4 for the down projection.
  *
  * Sources: the element format (E2M1 values, one E4M3 scale per 16-element block) is from
  * "NVFP4 W4A4 Quantization Compresses 27B Hybrid Models" (thevalue.engineering), section
