@@ -11,7 +11,8 @@ The NVFP4 encoding of h is compared bit for bit with the oracle's GIVEN-mode qua
 the fp32 h the same launch stores (the encoding decision is taken in the kernel's precision).
 Covered: both prefill tile sizes (256 and the peeled 128 columns), ragged M and F, per-row
 activation scales, all three decode kernels (K-split, K / 128 odd, balanced rows), strided and
-unaligned h rows, and NVFP4-only output."""
+unaligned h rows, NVFP4-only output, and gate outputs far past +-88 (the exponential overflowing
+to infinity, or vanishing)."""
 import numpy as np
 import pytest
 import torch
@@ -167,6 +168,17 @@ def test_nvfp4_only_output(M, F, K):
     want = ref.quantize(h32.cpu().numpy(), ref.GIVEN, 0.01)
     assert np.array_equal(q_only.scales.cpu().numpy(), want.scales)
     assert np.array_equal(q_only.codes.cpu().numpy(), want.codes)
+
+
+@pytest.mark.parametrize("M,F,K", [(300, 512, 512), (5, 512, 512), (3, 4608, 512)])
+def test_extreme_gate_values(M, F, K):
+    # Gate outputs spread over several hundred: e^-y overflows to infinity for y < -88 (silu flushes
+    # to -0) and vanishes for y > 88 (silu(y) = y); prefill, K-split and balanced decode kernels.
+    oa, og, ou = _random_operands(40 + M, M, F, K)
+    og = ref.NVFP4(og.codes, og.scales, og.global_scale * np.float32(40.0), og.rows, og.cols)
+    H, yg, _, _, _ = ref.swiglu_mlp(oa, og, ou)
+    assert (yg < -88).mean() > 0.1 and (yg > 88).mean() > 0.1
+    _check(oa, og, ou, torch.float32, what=f"extreme gates {M}x{F}x{K}")
 
 
 def test_rejects_shapes_without_mfma_kernel():
