@@ -145,15 +145,56 @@ def _require(cond: bool, msg: str) -> None:
         raise ValueError(msg)
 
 
+def _require_bytes(t: torch.Tensor, shape: tuple, name: str, dev: torch.device) -> None:
+    """A contiguous uint8 tensor of exactly ``shape`` on ``dev``: the library reads and writes
+    codes and scale bytes at the pitch their width implies."""
+    _require(isinstance(t, torch.Tensor) and t.device == dev, f"{name}: a tensor on {dev}")
+    _require(t.dtype == torch.uint8 and t.is_contiguous(), f"{name}: contiguous uint8")
+    _require(tuple(t.shape) == tuple(shape), f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _require_f32(t: torch.Tensor, numel: int | tuple, name: str, dev: torch.device) -> None:
+    """A contiguous fp32 tensor on ``dev`` with ``numel`` elements (or one of several counts)."""
+    counts = numel if isinstance(numel, tuple) else (numel,)
+    _require(isinstance(t, torch.Tensor) and t.device == dev, f"{name}: a tensor on {dev}")
+    _require(t.dtype == torch.float32 and t.is_contiguous(), f"{name}: contiguous float32")
+    _require(t.numel() in counts, f"{name}: {t.numel()} elements, expected {' or '.join(map(str, counts))}")
+
+
+def _require_operand(t, name: str, group: int = 16) -> None:
+    """Codes [R, C/2] and scales [R, C/group] of one device, contiguous; the global scale is
+    checked by the caller (its count depends on the role)."""
+    _require(isinstance(t.codes, torch.Tensor) and t.codes.dim() == 2, f"{name}.codes: 2-D")
+    dev = t.codes.device
+    R, C = t.codes.shape[0], t.codes.shape[1] * 2
+    _require_bytes(t.codes, (R, C // 2), f"{name}.codes", dev)
+    _require_bytes(t.scales, (R, C // group), f"{name}.scales", dev)
+
+
+def _on_gpu(dev: torch.device) -> None:
+    """Checked last, after every shape and dtype check, so that those checks can be exercised
+    on a machine without a GPU: every tensor of a call is on ``dev``, which must be a GPU."""
+    _require(dev.type == "cuda", f"tensors must be on a GPU, not {dev}")
+
+
+def _a_global_per_row(a) -> int:
+    """1 when the activation carries one global scale per row, 0 for one per tensor; any
+    other count is an error (a row slice of a per-row tensor must slice its scales too)."""
+    M = a.rows
+    _require_f32(a.global_scale, (1, M), "a.global_scale", a.codes.device)
+    return int(a.global_scale.numel() == M and M != 1)
+
+
 def quantize(x: torch.Tensor, mode: str = "per_tensor", global_scale: torch.Tensor | None = None,
              out: NVFP4Tensor | None = None) -> NVFP4Tensor:
     """Quantize a 2-D bf16/fp32 CUDA tensor (row stride may exceed its width) to NVFP4.
 
     mode: "per_tensor" | "per_row" | "given" (then ``global_scale`` is a float32 CUDA tensor
     of one element)."""
-    _require(x.is_cuda and x.dim() == 2, "x must be a 2-D GPU tensor")
+    _require(isinstance(x, torch.Tensor) and x.dim() == 2, "x must be a 2-D tensor")
     _require(x.dtype in (torch.bfloat16, torch.float32), "x must be bf16 or fp32")
     _require(x.stride(1) == 1, "x must be row-contiguous")
+    _require(mode in _MODES, f"mode must be one of {sorted(_MODES)}")
     m = _MODES[mode]
     rows, cols = x.shape
     dev = x.device
@@ -168,10 +209,13 @@ def quantize(x: torch.Tensor, mode: str = "per_tensor", global_scale: torch.Tens
         out = NVFP4Tensor(codes, scales, g)
     elif m == GIVEN and global_scale is not None:
         out.global_scale = global_scale
-    _require(out.global_scale.dtype == torch.float32 and out.global_scale.is_cuda, "global scale: fp32 GPU")
+    _require_bytes(out.codes, (rows, cols // 2), "out.codes", dev)
+    _require_bytes(out.scales, (rows, cols // 16), "out.scales", dev)
+    _require_f32(out.global_scale, rows if m == PER_ROW else 1, "global scale", dev)
     ws_bytes = lib.nvfp4_quantize_workspace_size(rows, cols, m)
     ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev) if ws_bytes else None
     ldx = x.stride(0) if rows > 1 else max(x.stride(0), cols)
+    _on_gpu(dev)
     st = lib.nvfp4_quantize(_ptr(x), _BF16 if x.dtype == torch.bfloat16 else _F32, rows, cols, ldx,
                             _ptr(out.codes), _ptr(out.scales), _ptr(out.global_scale), m,
                             _ptr(ws), ws_bytes, _stream(dev))
@@ -179,9 +223,25 @@ def quantize(x: torch.Tensor, mode: str = "per_tensor", global_scale: torch.Tens
     return out
 
 
+def _fused_weight_checks(a, w_codes: torch.Tensor, w_scales: torch.Tensor, seg_widths: Sequence[int],
+                         w_globals: torch.Tensor, group: int = 16):
+    """Shapes and devices of a (fused) weight: codes [N, K/2], scale bytes [N, K/group], one
+    fp32 global scale per segment.  Returns (M, K, N, device)."""
+    _require_operand(a, "a", group)
+    M, K = a.rows, a.cols
+    _require(len(seg_widths) >= 1 and all(int(v) > 0 for v in seg_widths), "segment widths must be positive")
+    N = int(sum(int(v) for v in seg_widths))
+    dev = a.codes.device
+    _require_bytes(w_codes, (N, K // 2), "w_codes", dev)
+    _require_bytes(w_scales, (N, K // group), "w_scales", dev)
+    _require_f32(w_globals, len(seg_widths), "w_globals (one per segment)", dev)
+    return M, K, N, dev
+
+
 def _out_tensor(M: int, N: int, dtype: torch.dtype, dev, out: torch.Tensor | None) -> torch.Tensor:
     if out is None:
         return torch.empty((M, N), dtype=dtype, device=dev)
+    _require(out.device == dev, f"out: a tensor on {dev}")
     _require(out.shape == (M, N) and out.dtype == dtype and out.stride(1) == 1, "bad out tensor")
     return out
 
@@ -196,14 +256,18 @@ def _y_dtype(dtype: torch.dtype) -> int:
 def gemm(a: NVFP4Tensor, w: NVFP4Tensor, out_dtype: torch.dtype = torch.bfloat16,
          out: torch.Tensor | None = None) -> torch.Tensor:
     """Y[M, N] = A . W^T for NVFP4 A [M, K] and W [N, K]."""
+    _require_operand(a, "a")
+    _require_operand(w, "w")
     _require(a.cols == w.cols, "K mismatch")
-    _require(w.global_scale.numel() == 1, "W must have one global scale")
     M, N, K = a.rows, w.rows, a.cols
     dev = a.codes.device
+    _require(w.codes.device == dev, "a and w must be on one device")
+    _require_f32(w.global_scale, 1, "w.global_scale (one per tensor)", dev)
     y = _out_tensor(M, N, out_dtype, dev, out)
-    per_row = int(a.global_scale.numel() == M and M != 1)
+    per_row = _a_global_per_row(a)
     ws_bytes = lib.nvfp4_gemm_workspace_size(M, N, K)
     ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev) if ws_bytes else None
+    _on_gpu(dev)
     st = lib.nvfp4_gemm(M, N, K, _ptr(a.codes), _ptr(a.scales), _ptr(a.global_scale), per_row,
                         _ptr(w.codes), _ptr(w.scales), _ptr(w.global_scale), _ptr(y), _y_dtype(out_dtype),
                         y.stride(0) if M > 0 else N, _ptr(ws), ws_bytes, _stream(dev))
@@ -217,15 +281,13 @@ def gemm_fused_segments(a: NVFP4Tensor, w_codes: torch.Tensor, w_scales: torch.T
                         out: torch.Tensor | None = None) -> torch.Tensor:
     """Fused-module GEMM: W = concatenation (along N) of len(seg_widths) modules, each with its
     own global scale w_globals[i] (fp32 GPU tensor)."""
-    M, K = a.rows, a.cols
-    N = int(sum(seg_widths))
-    _require(w_codes.shape == (N, K // 2) and w_scales.shape == (N, K // 16), "bad fused weight shapes")
-    dev = a.codes.device
+    M, K, N, dev = _fused_weight_checks(a, w_codes, w_scales, seg_widths, w_globals)
     y = _out_tensor(M, N, out_dtype, dev, out)
-    per_row = int(a.global_scale.numel() == M and M != 1)
+    per_row = _a_global_per_row(a)
     widths = (ctypes.c_int64 * len(seg_widths))(*[int(v) for v in seg_widths])
     ws_bytes = lib.nvfp4_gemm_workspace_size(M, N, K)
     ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev) if ws_bytes else None
+    _on_gpu(dev)
     st = lib.nvfp4_gemm_fused_segments(M, K, _ptr(a.codes), _ptr(a.scales), _ptr(a.global_scale), per_row,
                                        len(seg_widths), ctypes.cast(widths, ctypes.c_void_p),
                                        _ptr(w_codes), _ptr(w_scales), _ptr(w_globals), _ptr(y),
@@ -241,16 +303,16 @@ def gemm_nvfp4_out(a: NVFP4Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor
     """(Fused-module) GEMM whose output is quantized to NVFP4 in the same launch, under the
     given output global scale y_global (fp32 GPU tensor of one element).  With one segment
     it is a plain GEMM.  Returns NVFP4Tensor(codes [M, N/2], scales [M, N/16], y_global)."""
-    M, K = a.rows, a.cols
-    N = int(sum(seg_widths))
-    _require(w_codes.shape == (N, K // 2) and w_scales.shape == (N, K // 16), "bad weight shapes")
-    _require(y_global.dtype == torch.float32 and y_global.is_cuda and y_global.numel() == 1, "y_global: fp32 [1]")
-    dev = a.codes.device
+    M, K, N, dev = _fused_weight_checks(a, w_codes, w_scales, seg_widths, w_globals)
+    _require_f32(y_global, 1, "y_global", dev)
     if out is None:
         out = NVFP4Tensor(torch.empty((M, N // 2), dtype=torch.uint8, device=dev),
                           torch.empty((M, N // 16), dtype=torch.uint8, device=dev), y_global)
-    per_row = int(a.global_scale.numel() == M and M != 1)
+    _require_bytes(out.codes, (M, N // 2), "out.codes", dev)
+    _require_bytes(out.scales, (M, N // 16), "out.scales", dev)
+    per_row = _a_global_per_row(a)
     widths = (ctypes.c_int64 * len(seg_widths))(*[int(v) for v in seg_widths])
+    _on_gpu(dev)
     st = lib.nvfp4_gemm_nvfp4_out(M, K, _ptr(a.codes), _ptr(a.scales), _ptr(a.global_scale), per_row,
                                   len(seg_widths), ctypes.cast(widths, ctypes.c_void_p), _ptr(w_codes),
                                   _ptr(w_scales), _ptr(w_globals), _ptr(y_global), _ptr(out.codes),
@@ -268,22 +330,20 @@ def gemm_fused_gdn_gates(a: NVFP4Tensor, w_codes: torch.Tensor, w_scales: torch.
     segments (equal widths H) are the write-strength and decay projections; a_log and dt_bias
     are fp32 GPU tensors [H].  Returns (Y [M, N] as gemm_fused_segments writes it, g [M, H]
     fp32 log decay, beta [M, H] fp32 write strength)."""
-    M, K = a.rows, a.cols
-    N = int(sum(seg_widths))
     _require(len(seg_widths) >= 2 and seg_widths[-1] == seg_widths[-2], "the last two segments are the gates")
+    M, K, N, dev = _fused_weight_checks(a, w_codes, w_scales, seg_widths, w_globals)
     H = int(seg_widths[-1])
-    _require(w_codes.shape == (N, K // 2) and w_scales.shape == (N, K // 16), "bad fused weight shapes")
-    for t, name in ((a_log, "a_log"), (dt_bias, "dt_bias")):
-        _require(t.is_cuda and t.dtype == torch.float32 and t.is_contiguous() and t.numel() == H, f"{name}: fp32 [H]")
-    dev = a.codes.device
+    _require_f32(a_log, H, "a_log [H]", dev)
+    _require_f32(dt_bias, H, "dt_bias [H]", dev)
     y = _out_tensor(M, N, out_dtype, dev, out)
     g = _out_tensor(M, H, torch.float32, dev, g_out)
     beta = _out_tensor(M, H, torch.float32, dev, beta_out)
     _require(g.is_contiguous() and beta.is_contiguous(), "g and beta must be contiguous")
-    per_row = int(a.global_scale.numel() == M and M != 1)
+    per_row = _a_global_per_row(a)
     widths = (ctypes.c_int64 * len(seg_widths))(*[int(v) for v in seg_widths])
     ws_bytes = lib.nvfp4_gemm_workspace_size(M, N, K)
     ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev) if ws_bytes else None
+    _on_gpu(dev)
     st = lib.nvfp4_gemm_fused_gdn_gates(M, K, _ptr(a.codes), _ptr(a.scales), _ptr(a.global_scale), per_row,
                                         len(seg_widths), ctypes.cast(widths, ctypes.c_void_p), _ptr(w_codes),
                                         _ptr(w_scales), _ptr(w_globals), _ptr(y), _y_dtype(out_dtype),
@@ -313,14 +373,16 @@ class MXFP4Tensor:
 def to_mxfp4(t: NVFP4Tensor, out: MXFP4Tensor | None = None) -> MXFP4Tensor:
     """Lossy re-encoding of an NVFP4 tensor to MXFP4 (E8M0 scale per 32 elements); the global
     scale tensor is shared with the input."""
+    _require_operand(t, "t")
     R, C = t.rows, t.cols
     _require(C % 32 == 0, "cols must be a multiple of 32")
-    _require(t.codes.is_contiguous() and t.scales.is_contiguous(), "contiguous NVFP4 tensor")
     dev = t.codes.device
     if out is None:
         out = MXFP4Tensor(torch.empty((R, C // 2), dtype=torch.uint8, device=dev),
                           torch.empty((R, C // 32), dtype=torch.uint8, device=dev), t.global_scale)
-    _require(out.codes.shape == (R, C // 2) and out.scales.shape == (R, C // 32), "bad out tensor")
+    _require_bytes(out.codes, (R, C // 2), "out.codes", dev)
+    _require_bytes(out.scales, (R, C // 32), "out.scales", dev)
+    _on_gpu(dev)
     st = lib.nvfp4_to_mxfp4(R, C, _ptr(t.codes), _ptr(t.scales), _ptr(out.codes), _ptr(out.scales), _stream(dev))
     _check(st, "nvfp4_to_mxfp4")
     return out
@@ -331,13 +393,11 @@ def mxfp4_gemm(a: MXFP4Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, se
                out: torch.Tensor | None = None) -> torch.Tensor:
     """(Fused-module) GEMM on MXFP4 operands with the scaled FP4 MFMA: W = concatenation of the
     segments' MXFP4 codes [N, K/2] and E8M0 scales [N, K/32], one global scale per segment."""
-    M, K = a.rows, a.cols
-    N = int(sum(seg_widths))
-    _require(w_codes.shape == (N, K // 2) and w_scales.shape == (N, K // 32), "bad MXFP4 weight shapes")
-    dev = a.codes.device
+    M, K, N, dev = _fused_weight_checks(a, w_codes, w_scales, seg_widths, w_globals, group=32)
     y = _out_tensor(M, N, out_dtype, dev, out)
-    per_row = int(a.global_scale.numel() == M and M != 1)
+    per_row = _a_global_per_row(a)
     widths = (ctypes.c_int64 * len(seg_widths))(*[int(v) for v in seg_widths])
+    _on_gpu(dev)
     st = lib.nvfp4_mxfp4_gemm(M, K, _ptr(a.codes), _ptr(a.scales), _ptr(a.global_scale), per_row, len(seg_widths),
                               ctypes.cast(widths, ctypes.c_void_p), _ptr(w_codes), _ptr(w_scales), _ptr(w_globals),
                               _ptr(y), _y_dtype(out_dtype), y.stride(0) if M > 0 else N, _stream(dev))
@@ -349,13 +409,15 @@ def interleave_gate_up(gate: NVFP4Tensor, up: NVFP4Tensor) -> tuple[torch.Tensor
     """The weight layout gemm_swiglu takes: rows 32p .. 32p+15 are gate rows 16p .. 16p+15,
     rows 32p+16 .. 32p+31 the up rows 16p .. 16p+15.  Returns (codes [2F, K/2], scales
     [2F, K/16]); the global scales stay the projections' own (pass them as {gate, up})."""
+    _require_operand(gate, "gate")
+    _require_operand(up, "up")
     F, K = gate.rows, gate.cols
     _require(up.rows == F and up.cols == K, "gate and up must have the same shape")
-    for t in (gate.codes, gate.scales, up.codes, up.scales):
-        _require(t.is_cuda and t.is_contiguous(), "contiguous GPU NVFP4 tensors")
     dev = gate.codes.device
+    _require(up.codes.device == dev, "gate and up must be on one device")
     w_codes = torch.empty((2 * F, K // 2), dtype=torch.uint8, device=dev)
     w_scales = torch.empty((2 * F, K // 16), dtype=torch.uint8, device=dev)
+    _on_gpu(dev)
     st = lib.nvfp4_interleave_gate_up(F, K, _ptr(gate.codes), _ptr(gate.scales), _ptr(up.codes), _ptr(up.scales),
                                       _ptr(w_codes), _ptr(w_scales), _stream(dev))
     _check(st, "nvfp4_interleave_gate_up")
@@ -370,22 +432,23 @@ def gemm_swiglu(a: NVFP4Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, w
     weights in interleave_gate_up's layout and w_globals = fp32 GPU tensor [2] = {gate, up}.
     h is returned as h_dtype [M, F] unless h_dtype is None, and as NVFP4 under the given
     h_global (fp32 GPU tensor of one element) when h_global is set.  Returns (h, h_nvfp4)."""
-    M, K = a.rows, a.cols
-    _require(w_codes.dim() == 2 and w_codes.shape[0] % 32 == 0, "w_codes: [2F, K/2], F a multiple of 16")
+    _require(isinstance(w_codes, torch.Tensor) and w_codes.dim() == 2 and w_codes.shape[0] % 32 == 0,
+             "w_codes: [2F, K/2], F a multiple of 16")
     F = w_codes.shape[0] // 2
-    _require(w_codes.shape == (2 * F, K // 2) and w_scales.shape == (2 * F, K // 16), "bad interleaved weight shapes")
-    _require(w_globals.dtype == torch.float32 and w_globals.is_cuda and w_globals.numel() == 2, "w_globals: fp32 [2]")
+    M, K, _, dev = _fused_weight_checks(a, w_codes, w_scales, (F, F), w_globals)
     _require(h_dtype is not None or h_global is not None, "ask for h, its NVFP4 encoding, or both")
-    dev = a.codes.device
     h = _out_tensor(M, F, h_dtype, dev, out) if h_dtype is not None else None
     q = None
     if h_global is not None:
-        _require(h_global.dtype == torch.float32 and h_global.is_cuda and h_global.numel() == 1, "h_global: fp32 [1]")
+        _require_f32(h_global, 1, "h_global", dev)
         q = q_out if q_out is not None else NVFP4Tensor(
             torch.empty((M, F // 2), dtype=torch.uint8, device=dev),
             torch.empty((M, F // 16), dtype=torch.uint8, device=dev), h_global)
+        _require_bytes(q.codes, (M, F // 2), "q_out.codes", dev)
+        _require_bytes(q.scales, (M, F // 16), "q_out.scales", dev)
         q.global_scale = h_global
-    per_row = int(a.global_scale.numel() == M and M != 1)
+    per_row = _a_global_per_row(a)
+    _on_gpu(dev)
     st = lib.nvfp4_gemm_swiglu(M, F, K, _ptr(a.codes), _ptr(a.scales), _ptr(a.global_scale), per_row,
                                _ptr(w_codes), _ptr(w_scales), _ptr(w_globals), _ptr(h),
                                _y_dtype(h_dtype) if h is not None else _BF16,
@@ -398,10 +461,11 @@ def gemm_swiglu(a: NVFP4Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, w
 def fp8_kv_quantize(x: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """FP8 (E4M3FN) bytes of a contiguous bf16/fp32 GPU tensor under the calibrated scale
     (fp32 GPU tensor of one element); the result has x's shape, dtype uint8."""
-    _require(x.is_cuda and x.is_contiguous() and x.dtype in (torch.bfloat16, torch.float32), "x: contiguous bf16/fp32 GPU")
-    _require(scale.dtype == torch.float32 and scale.is_cuda and scale.numel() == 1, "scale: fp32 [1]")
+    _require(x.is_contiguous() and x.dtype in (torch.bfloat16, torch.float32), "x: contiguous bf16/fp32")
+    _require_f32(scale, 1, "scale", x.device)
     q = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
-    _require(q.shape == x.shape and q.dtype == torch.uint8 and q.is_contiguous(), "bad out tensor")
+    _require_bytes(q, tuple(x.shape), "out", x.device)
+    _on_gpu(x.device)
     st = lib.nvfp4_fp8_kv_quantize(_ptr(x), _BF16 if x.dtype == torch.bfloat16 else _F32, x.numel(), _ptr(scale),
                                    _ptr(q), _stream(x.device))
     _check(st, "nvfp4_fp8_kv_quantize")
@@ -411,10 +475,12 @@ def fp8_kv_quantize(x: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | No
 def fp8_kv_dequantize(q: torch.Tensor, scale: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
                       out: torch.Tensor | None = None) -> torch.Tensor:
     """Values fl32(E4M3(q) * scale) of FP8 bytes, as bf16 or fp32 (same shape as q)."""
-    _require(q.is_cuda and q.is_contiguous() and q.dtype == torch.uint8, "q: contiguous uint8 GPU")
-    _require(scale.dtype == torch.float32 and scale.is_cuda and scale.numel() == 1, "scale: fp32 [1]")
+    _require_bytes(q, tuple(q.shape), "q", q.device)
+    _require_f32(scale, 1, "scale", q.device)
     y = torch.empty(q.shape, dtype=out_dtype, device=q.device) if out is None else out
+    _require(y.device == q.device, "out: a tensor on q's device")
     _require(y.shape == q.shape and y.dtype == out_dtype and y.is_contiguous(), "bad out tensor")
+    _on_gpu(q.device)
     st = lib.nvfp4_fp8_kv_dequantize(_ptr(q), q.numel(), _ptr(scale), _ptr(y), _y_dtype(out_dtype), _stream(q.device))
     _check(st, "nvfp4_fp8_kv_dequantize")
     return y

@@ -17,10 +17,10 @@ Sources (the pages this follows):
     four-bit storage with one shared scale per sixteen-element block; W4A4 (weights and
     activations both four-bit) on every linear layer; block scaling confines an outlier to
     its own block of sixteen.
-  * The paper abstract (Lattice and kipquest pages): the global-scale mismatch that appears
-    when per-module-calibrated NVFP4 checkpoints are served by kernels that fuse modules
-    into one GEMM, which the authors repair.  A per-module global scale is therefore part
-    of the format; each fused segment keeps its own.
+  * The paper abstract (Lattice and kipquest pages): modules that were calibrated one by one
+    but run together as a single fused GEMM lose accuracy when the kernel applies one global
+    scale to all of them, and the authors repair that.  A per-module global scale is
+    therefore part of the format; each fused segment keeps its own.
 
 Readings where the pages are silent (each is listed with its justification in the design
 notes of this repository):

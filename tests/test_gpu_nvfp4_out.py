@@ -3,8 +3,9 @@ launch, under a given output global scale).
 
 For every output element the kernel's fp32 value is the one the same kernel stores as fp32
 output (nvfp4_gemm_fused_segments with out_dtype float32, same shape, same accumulation
-order); the oracle quantizes those fp32 values in GIVEN mode, and codes and scale bytes must
-match bit for bit.  Both prefill tile sizes (256 and the peeled 128 columns), fused
+order); those fp32 values are checked against the oracle's Y within 1e-4 * sum_k |a_k w_k|,
+then the oracle quantizes them in GIVEN mode, and codes and scale bytes must match bit for
+bit.  Both prefill tile sizes (256 and the peeled 128 columns), fused
 segments, and both decode kernels (K a multiple of 256, and K / 128 odd) are covered."""
 import numpy as np
 import pytest
@@ -12,15 +13,22 @@ import torch
 
 import workloads
 from oracle import nvfp4_ref as ref
-from tests.gpu_helpers import DEV, nv, to_gpu
+from tests.gpu_helpers import DEV, assert_gemm_close, assert_quant_equal, nv, to_gpu
 
 pytestmark = pytest.mark.gpu
 
 
-def _weights(seed, widths, K, sigma=0.02):
+def _weights(seed, widths, K, sigma=0.02, oracle=None):
+    """Quantized weight segments on the GPU; with a list for ``oracle``, the oracle's
+    quantizations of the same bf16 weights are appended to it (and checked bit-exact)."""
     gq, codes, scales, globs = [], [], [], []
     for i, n in enumerate(widths):
-        q = nv().quantize(to_gpu(workloads.weight(seed, 50 + i, n, K, sigma=sigma * (1 + 0.5 * i))))
+        wg = to_gpu(workloads.weight(seed, 50 + i, n, K, sigma=sigma * (1 + 0.5 * i)))
+        q = nv().quantize(wg)
+        if oracle is not None:
+            o = ref.quantize(wg.float().cpu().numpy())
+            assert_quant_equal(q, o, what=f"w{i}")
+            oracle.append(o)
         codes.append(q.codes)
         scales.append(q.scales)
         globs.append(q.global_scale)
@@ -29,10 +37,17 @@ def _weights(seed, widths, K, sigma=0.02):
 
 def _check(M, K, widths, a_mode="per_tensor", rows=None, y_scale_factor=1.0, seed=41):
     x = workloads.activation(seed, M, M, K, outlier_frac=0.01)
-    a = nv().quantize(to_gpu(x), a_mode)
-    wc, ws, wg = _weights(seed, widths, K)
+    xg = to_gpu(x)
+    a = nv().quantize(xg, a_mode)
+    oa = ref.quantize(xg.float().cpu().numpy(), ref.PER_ROW if a_mode == "per_row" else ref.PER_TENSOR)
+    assert_quant_equal(a, oa, what="x")
+    ows = []
+    wc, ws, wg = _weights(seed, widths, K, oracle=ows)
     y32 = nv().gemm_fused_segments(a, wc, ws, widths, wg, torch.float32)
     ysel = y32 if rows is None else y32[torch.from_numpy(rows).to(DEV)]
+    # The fp32 values the encoding starts from are themselves within the GEMM tolerance.
+    Y, T = ref.fused_segments(oa, ows, rows)
+    assert_gemm_close(ysel, Y, T, f"fp32 values M={M} K={K} widths={widths} {a_mode}")
     yh = ysel.cpu().numpy()
     amax = float(np.max(np.abs(y32.cpu().numpy()))) if rows is None else float(y32.abs().max().item())
     s = np.float32(amax / 2688.0 * y_scale_factor)
@@ -65,8 +80,14 @@ def test_prefill_full_shape_sampled_rows():
     rows = np.concatenate([[0, 1, 255, 256, 4095], np.random.default_rng(7).choice(4096, 27, replace=False)])
     x = to_gpu(p.x())
     a = nv().quantize(x)
-    w = nv().quantize(to_gpu(p.w()))
+    wt = to_gpu(p.w())
+    w = nv().quantize(wt)
     y32 = nv().gemm(a, w, torch.float32)
+    oa, ow = ref.quantize(x.float().cpu().numpy()), ref.quantize(wt.float().cpu().numpy())
+    assert_quant_equal(a, oa, what="x")
+    assert_quant_equal(w, ow, what="w")
+    Y, T = ref.gemm(oa, ow, rows)
+    assert_gemm_close(y32[torch.from_numpy(rows).to(DEV)], Y, T, "fp32 values, prefill")
     s = np.float32(float(y32.abs().max().item()) / 2688.0)
     sg = torch.tensor([s], dtype=torch.float32, device=DEV)
     yq = nv().gemm_nvfp4_out(a, w.codes, w.scales, (p.N,), w.global_scale, sg)
