@@ -1865,30 +1865,6 @@ GemmArgs gemm_args(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, cons
   return g;
 }
 
-// Once per device: raise the tile kernels' dynamic LDS limit (their 146 KB exceed the default)
-// and read the CU count.
-int tile_kernels_ready(int& cus) {
-  static bool ready[64] = {};
-  static int cu_count[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return NVFP4_ERR_HIP;
-  if (!ready[dev]) {
-    const void* kernels[] = {reinterpret_cast<const void*>(gemm_prefill_kernel<kEpiStore>),
-                             reinterpret_cast<const void*>(gemm_prefill_kernel<kEpiNvfp4>),
-                             reinterpret_cast<const void*>(gemm_prefill_kernel<kEpiGates>),
-                             reinterpret_cast<const void*>(gemm_prefill_kernel<kEpiSwiglu>),
-                             reinterpret_cast<const void*>(gemm_mx_kernel)};
-    for (const void* k : kernels)
-      if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kPrefillLds) != hipSuccess)
-        return NVFP4_ERR_HIP;
-    if (hipDeviceGetAttribute(&cu_count[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return NVFP4_ERR_HIP;
-    ready[dev] = true;
-  }
-  cus = cu_count[dev];
-  return NVFP4_OK;
-}
-
 // Rows per workgroup of the balanced decode kernel: the fewest rounds over the CUs with at
 // most cap rows per workgroup (the largest multiple of unit up to 16 kDwMaxG), the rows then
 // spread evenly over the workgroups of those rounds and rounded up to a multiple of unit (16
@@ -1914,41 +1890,6 @@ int set_decode_rows_lds() {
       hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_decode_rows_kernel<G, true>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
     return NVFP4_ERR_HIP;
-  return NVFP4_OK;
-}
-
-// Device set-up of the decode kernels (once per device): LDS limits and the CU count.
-int decode_kernels_ready(int& cus) {
-  static bool ready[64] = {};
-  static int cu_count[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return NVFP4_ERR_HIP;
-  if (!ready[dev]) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_decode_lds_kernel<false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kDlLds) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_decode_lds_kernel<true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kDlLds) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_mx_decode_lds_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kDlLds) != hipSuccess)
-      return NVFP4_ERR_HIP;
-    int st = set_decode_rows_lds<1>();
-    if (st == NVFP4_OK) st = set_decode_rows_lds<2>();
-    if (st == NVFP4_OK) st = set_decode_rows_lds<3>();
-    if (st == NVFP4_OK) st = set_decode_rows_lds<4>();
-    if (st == NVFP4_OK) st = set_decode_rows_lds<5>();
-    if (st == NVFP4_OK) st = set_decode_rows_lds<kDwPairG>();
-    if (st == NVFP4_OK &&
-        (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_mx_decode_rows_kernel<2>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess ||
-         hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_mx_decode_rows_kernel<3>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess))
-      st = NVFP4_ERR_HIP;
-    if (st != NVFP4_OK) return st;
-    if (hipDeviceGetAttribute(&cu_count[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return NVFP4_ERR_HIP;
-    ready[dev] = true;
-  }
-  cus = cu_count[dev];
   return NVFP4_OK;
 }
 
@@ -1993,6 +1934,38 @@ void tile_grid(int64_t M, int64_t N, int cus, int64_t& n_split, int64_t& big, in
 
 }  // namespace
 
+// Once per device (device.hip), with the device current: raise the dynamic LDS limit of every
+// kernel whose LDS exceeds the default.
+int gemm_device_setup() {
+  const void* tiles[] = {reinterpret_cast<const void*>(gemm_prefill_kernel<kEpiStore>),
+                         reinterpret_cast<const void*>(gemm_prefill_kernel<kEpiNvfp4>),
+                         reinterpret_cast<const void*>(gemm_prefill_kernel<kEpiGates>),
+                         reinterpret_cast<const void*>(gemm_prefill_kernel<kEpiSwiglu>),
+                         reinterpret_cast<const void*>(gemm_mx_kernel)};
+  for (const void* k : tiles)
+    if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kPrefillLds) != hipSuccess)
+      return NVFP4_ERR_HIP;
+  const void* decode[] = {reinterpret_cast<const void*>(gemm_decode_lds_kernel<false>),
+                          reinterpret_cast<const void*>(gemm_decode_lds_kernel<true>),
+                          reinterpret_cast<const void*>(gemm_mx_decode_lds_kernel)};
+  for (const void* k : decode)
+    if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kDlLds) != hipSuccess)
+      return NVFP4_ERR_HIP;
+  int st = set_decode_rows_lds<1>();
+  if (st == NVFP4_OK) st = set_decode_rows_lds<2>();
+  if (st == NVFP4_OK) st = set_decode_rows_lds<3>();
+  if (st == NVFP4_OK) st = set_decode_rows_lds<4>();
+  if (st == NVFP4_OK) st = set_decode_rows_lds<5>();
+  if (st == NVFP4_OK) st = set_decode_rows_lds<kDwPairG>();
+  if (st != NVFP4_OK) return st;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_mx_decode_rows_kernel<2>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess ||
+      hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_mx_decode_rows_kernel<3>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+    return NVFP4_ERR_HIP;
+  return NVFP4_OK;
+}
+
 int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
                 const float* a_global, int a_global_per_row, const uint8_t* w_codes, const uint8_t* w_scales,
                 const float* w_globals, const SegmentTable& seg, void* y, int y_dtype, int64_t ldy, void* workspace,
@@ -2021,9 +1994,10 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
     const int64_t total = M * N;
     gemm_plain_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(g);
   } else if (M <= 16 && K % 256 == 0) {
-    int cus = 0;
-    const int st = decode_kernels_ready(cus);
+    DeviceInfo dev;
+    const int st = device_info(stream, dev);
     if (st != NVFP4_OK) return st;
+    const int cus = dev.cus;
     // Up to one round of 32-row workgroups the K-split kernel is the faster; past it, the
     // balanced kernel avoids the partial last round.
     int rows = 0, groups = 0;
@@ -2059,11 +2033,11 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
     else
       gemm_decode_kernel<false><<<grid, kDecodeThreads, 0, stream>>>(g);
   } else {
-    int cus = 0;
-    const int st = tile_kernels_ready(cus);
+    DeviceInfo dev;
+    const int st = device_info(stream, dev);
     if (st != NVFP4_OK) return st;
     int64_t n_split, big, small;
-    tile_grid(M, N, cus, n_split, big, small);
+    tile_grid(M, N, dev.cus, n_split, big, small);
     const unsigned grid = (unsigned)(big + small);
     if (swiglu)
       gemm_prefill_kernel<kEpiSwiglu><<<grid, kPrefillThreads, kPrefillLds, stream>>>(g, (int)n_split, (int)big);
@@ -2086,9 +2060,10 @@ int launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, cons
   const GemmArgs g = gemm_args(M, N, K, a_codes, a_scales, a_global, a_global_per_row, w_codes, w_scales,
                                w_globals, seg, y, y_dtype, ldy);
   if (M <= 16 && K % 512 == 0) {
-    int cus = 0;
-    const int st = decode_kernels_ready(cus);
+    DeviceInfo dev;
+    const int st = device_info(stream, dev);
     if (st != NVFP4_OK) return st;
+    const int cus = dev.cus;
     if (N > 32 * (int64_t)cus) {
       // More rows than one round of 32-row workgroups: the balanced kernel.
       int rows = 0, groups = 0;
@@ -2114,11 +2089,11 @@ int launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, cons
     gemm_mx_decode_kernel<<<(unsigned)((N + kMxDecodeRows - 1) / kMxDecodeRows), kMxDecodeThreads, 0, stream>>>(g);
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
   }
-  int cus = 0;
-  const int st = tile_kernels_ready(cus);
+  DeviceInfo dev;
+  const int st = device_info(stream, dev);
   if (st != NVFP4_OK) return st;
   int64_t n_split, big, small;
-  tile_grid(M, N, cus, n_split, big, small);
+  tile_grid(M, N, dev.cus, n_split, big, small);
   gemm_mx_kernel<<<(unsigned)(big + small), kPrefillThreads, kPrefillLds, stream>>>(g, (int)n_split, (int)big);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }

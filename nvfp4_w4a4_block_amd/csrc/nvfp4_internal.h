@@ -35,6 +35,18 @@ __host__ __device__ inline uint32_t fastdiv(uint32_t n, const FastDivU32& f) {
   return (t1 + ((n - t1) >> f.s1)) >> f.s2;
 }
 
+// Per-device facts (device.hip), set up once per device by the first call that launches work
+// on it; safe to call from several host threads at once.
+struct DeviceInfo {
+  int cus;               // compute units
+};
+
+// The device `stream` belongs to (the current device for the null stream) and its facts.
+int device_info(hipStream_t stream, DeviceInfo& info);
+
+// Set-up steps of the kernel files, each run once per device with that device current.
+int gemm_device_setup();                    // gemm.hip: LDS limits of the kernels that need more
+
 // Quantize launchers (quantize.hip).  All validation is done by the caller.
 int launch_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
                     uint8_t* codes, uint8_t* scales, float* global_scale, int mode,

@@ -285,15 +285,6 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const T* __restrict__ 
   }
 }
 
-int num_cus() {
-  static int cus[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cus[dev] && hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 256;
-  return cus[dev];
-}
-
 template <typename T>
 int launch_typed(const T* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* codes,
                  uint8_t* scales, float* global_scale, int mode, void* workspace,
@@ -308,7 +299,10 @@ int launch_typed(const T* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* c
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
   }
   if (rows == 0) return NVFP4_OK;
-  const int cus = num_cus();
+  DeviceInfo dev;
+  const int st = device_info(stream, dev);
+  if (st != NVFP4_OK) return st;
+  const int cus = dev.cus;
   const uint32_t want = (uint32_t)((total + kThreads - 1) / kThreads);
   const uint32_t grid = want < (uint32_t)(8 * cus) ? want : (uint32_t)(8 * cus);
   const FastDivU32 fd = make_fastdiv(bpr);

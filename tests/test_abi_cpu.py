@@ -139,19 +139,12 @@ def test_m0_is_only_set_for_lds_copies(tmp_path):
     r = subprocess.run([b.hipcc(), *flags, "--cuda-device-only", "-S", "-I", os.path.join(ROOT, "include"),
                         os.path.join(b.CSRC, "gemm.hip"), "-o", str(out)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
-    lines = [l.strip() for l in out.read_text().splitlines()]
-    code = [l for l in lines if l and not l.startswith((";", "."))]
-    writes = 0
-    for i, l in enumerate(code):
-        if not re.search(r"\bm0\b", l):
-            continue
-        assert re.fullmatch(r"s_mov_b32 m0, s\d+", l), l
-        assert code[i + 1].startswith("global_load_lds_dword"), (l, code[i + 1])
-        writes += 1
-    assert writes > 0
-    # global_load_lds reads M0 implicitly: each one must follow its own M0 write.
-    loads = [i for i, l in enumerate(code) if l.startswith("global_load_lds")]
-    assert all(code[i - 1].startswith("s_mov_b32 m0,") for i in loads)
+    assert b.check_m0(out.read_text()) > 0
+    # the check rejects a stray M0 use and a copy without its own M0 write
+    with pytest.raises(RuntimeError):
+        b.check_m0("s_mov_b32 m0, s4\nglobal_load_lds_dwordx4 v1, off\ns_add_u32 s0, m0, 1\n")
+    with pytest.raises(RuntimeError):
+        b.check_m0("s_mov_b32 m0, s4\nglobal_load_lds_dwordx4 v1, off\nglobal_load_lds_dwordx4 v2, off\n")
 
 
 def test_nvfp4_out_argument_errors(nv):
