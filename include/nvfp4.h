@@ -99,6 +99,21 @@ int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64
 size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols, int mode);
 
 /*
+ * nvfp4_quantize for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments, results and errors as
+ * nvfp4_quantize, without the workspace: the per-tensor mode's partial maxima go to a static
+ * device array of the library (4 KB per GPU, held until the process ends) instead.  Allocates
+ * nothing, on the host or the device.
+ *   Every call on one GPU shares that GPU's array, so calls that overlap in time on one GPU
+ *   (different streams, or threads without ordering) race and may return wrong results;
+ *   serialise them.  Calls on one stream are ordered and safe.
+ *   A shape whose workspace need exceeds the array returns NVFP4_ERR_WORKSPACE (no shape
+ *   does at present: the need is at most 4 KB).
+ */
+int nvfp4_quantize_no_alloc(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                            uint8_t* codes, uint8_t* scales, float* global_scale, int mode, void* stream);
+
+/*
  * Y[M, N] = A . W^T with A = NVFP4 [M, K] activations and W = NVFP4 [N, K] weights, both
  * K-major; FP32 accumulation of the exactly dequantized operands, then
  * y = (acc * a_global[m or 0]) * w_global[0], stored as y_dtype (bf16: round to nearest

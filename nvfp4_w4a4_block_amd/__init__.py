@@ -51,7 +51,7 @@ _MODES = {"per_tensor": PER_TENSOR, "per_row": PER_ROW, "given": GIVEN}
 _F32, _BF16 = 0, 1
 MAX_SEGMENTS = 64
 EXPORTED_SYMBOLS = (
-    "nvfp4_quantize", "nvfp4_quantize_workspace_size", "nvfp4_gemm", "nvfp4_gemm_fused_segments",
+    "nvfp4_quantize", "nvfp4_quantize_workspace_size", "nvfp4_quantize_no_alloc", "nvfp4_gemm", "nvfp4_gemm_fused_segments",
     "nvfp4_gemm_nvfp4_out", "nvfp4_gemm_fused_gdn_gates", "nvfp4_to_mxfp4", "nvfp4_mxfp4_gemm",
     "nvfp4_gemm_workspace_size", "nvfp4_fp8_kv_quantize", "nvfp4_fp8_kv_dequantize",
     "nvfp4_interleave_gate_up", "nvfp4_gemm_swiglu", "nvfp4_status_string", "nvfp4_version",
@@ -69,6 +69,8 @@ def _load() -> ctypes.CDLL:
     p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     L.nvfp4_quantize.argtypes = [p, i32, i64, i64, i64, p, p, p, i32, p, sz, p]
     L.nvfp4_quantize.restype = i32
+    L.nvfp4_quantize_no_alloc.argtypes = [p, i32, i64, i64, i64, p, p, p, i32, p]
+    L.nvfp4_quantize_no_alloc.restype = i32
     L.nvfp4_quantize_workspace_size.argtypes = [i64, i64, i32]
     L.nvfp4_quantize_workspace_size.restype = sz
     L.nvfp4_gemm.argtypes = [i64, i64, i64, p, p, p, i32, p, p, p, p, i32, i64, p, sz, p]

@@ -27,6 +27,7 @@ int setup_device(int dev, DeviceInfo& info) {
   if (hipGetDevice(&prev) != hipSuccess) return NVFP4_ERR_HIP;
   if (prev != dev && hipSetDevice(dev) != hipSuccess) return NVFP4_ERR_HIP;
   int st = gemm_device_setup();
+  if (st == NVFP4_OK) st = quantize_device_setup(&info.quant_scratch);
   if (st == NVFP4_OK &&
       (hipDeviceGetAttribute(&info.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || info.cus <= 0))
     st = NVFP4_ERR_HIP;

@@ -39,6 +39,7 @@ __host__ __device__ inline uint32_t fastdiv(uint32_t n, const FastDivU32& f) {
 // on it; safe to call from several host threads at once.
 struct DeviceInfo {
   int cus;               // compute units
+  void* quant_scratch;   // this device's copy of the quantizer's static scratch array
 };
 
 // The device `stream` belongs to (the current device for the null stream) and its facts.
@@ -46,12 +47,15 @@ int device_info(hipStream_t stream, DeviceInfo& info);
 
 // Set-up steps of the kernel files, each run once per device with that device current.
 int gemm_device_setup();                    // gemm.hip: LDS limits of the kernels that need more
+int quantize_device_setup(void** scratch);  // quantize.hip: device address of the static scratch
 
 // Quantize launchers (quantize.hip).  All validation is done by the caller.
 int launch_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
                     uint8_t* codes, uint8_t* scales, float* global_scale, int mode,
                     void* workspace, hipStream_t stream);
 size_t quantize_workspace_bytes(int64_t rows, int64_t cols, int mode);
+// Size of the static scratch array nvfp4_quantize_no_alloc uses in place of a workspace.
+size_t quantize_scratch_bytes();
 
 // GEMM launchers (gemm.hip).
 struct SegmentTable {

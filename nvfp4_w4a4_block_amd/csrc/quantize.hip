@@ -354,6 +354,19 @@ int launch_typed(const T* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* c
 
 }  // namespace
 
+// The scratch array of nvfp4_quantize_no_alloc, which stands in for the caller's workspace:
+// one partial max per pass-1 workgroup (4 KB).  Every GPU the library runs on holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in, never the device
+// memory: launches use the address quantize_device_setup looks up once per device.
+static __device__ __align__(256) uint32_t scratch[kMaxPartials];
+
+int quantize_device_setup(void** scratch_ptr) {
+  return hipGetSymbolAddress(scratch_ptr, HIP_SYMBOL(scratch)) == hipSuccess && *scratch_ptr ? NVFP4_OK
+                                                                                            : NVFP4_ERR_HIP;
+}
+
+size_t quantize_scratch_bytes() { return sizeof(scratch); }
+
 size_t quantize_workspace_bytes(int64_t, int64_t, int mode) {
   // one partial max per pass-1 workgroup, at most kMaxPartials of them
   return mode == kPerTensor ? (size_t)kMaxPartials * sizeof(uint32_t) : 0;
