@@ -127,6 +127,66 @@ def summarize(prof_dir: str, out: str | None, command: str, copy_mb: int) -> int
     return 0
 
 
+def _calib_lib():
+    """The calibration kernels (streaming read, copy, fp16 MFMA loop), built beside the library."""
+    import ctypes
+    path = os.path.join(ROOT, "nvfp4_w4a4_block_amd", "libnvfp4_calib.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python nvfp4_w4a4_block_amd/build.py`")
+    L = ctypes.CDLL(path)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.nvfp4_calib_read.argtypes = [p, i64, p, p]
+    L.nvfp4_calib_copy.argtypes = [p, p, i64, p]
+    L.nvfp4_calib_mfma.argtypes = [i32, i32, p, p]
+    for f in (L.nvfp4_calib_read, L.nvfp4_calib_copy, L.nvfp4_calib_mfma):
+        f.restype = i32
+    return L
+
+
+def calibration(steps: int, warmup: int, sizes: dict) -> dict:
+    """Measured ceilings on this GPU (buffers rotating over more than the 256 MB last-level
+    cache): a plain streaming read and a plain copy of each named byte count (the copy reads half
+    of it and writes half), timed back to back from a HIP graph like the decode kernels, and a loop
+    of nothing but fp16 MFMAs (v_mfma_f32_32x32x16_f16, two wavefronts per SIMD), timed with events
+    around each launch."""
+    L = _calib_lib()
+    dev = torch.device("cuda:0")
+
+    def stream():            # the current stream at launch time (a graph captures on its own)
+        return torch.cuda.current_stream(dev).cuda_stream
+
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = {}
+    for name, nbytes in sizes.items():
+        nb = int(nbytes) // 32 * 32
+        copies = max(2, -(-(320 << 20) // nb))                      # > 256 MB in rotation
+        bufs = [torch.empty(nb, dtype=torch.uint8, device=dev).fill_(i) for i in range(copies)]
+        dsts = [torch.empty(nb // 2, dtype=torch.uint8, device=dev) for _ in range(copies)]
+
+        def rd(i):
+            assert L.nvfp4_calib_read(bufs[i % copies].data_ptr(), nb, sink.data_ptr(), stream()) == 0
+
+        def cp(i):
+            assert L.nvfp4_calib_copy(bufs[i % copies].data_ptr(), dsts[i % copies].data_ptr(), nb // 2, stream()) == 0
+
+        r_ms = _graph_us(rd, 2 * copies, max(4, steps // 5), 0.2) * 1e-3
+        c_ms = _graph_us(cp, 2 * copies, max(4, steps // 5), 0.2) * 1e-3
+        out[name] = {"bytes": nb,
+                     "read_us": round(r_ms * 1e3, 2), "read_gbs": round(nb / (r_ms * 1e-3) / 1e9, 1),
+                     "read_frac_hbm": round(nb / (r_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "copy_us": round(c_ms * 1e3, 2), "copy_gbs": round(nb / (c_ms * 1e-3) / 1e9, 1),
+                     "copy_frac_hbm": round(nb / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del bufs, dsts
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    waves, iters = cus * 4 * 2, 2000
+    m_ms = _mean_ms(lambda i: L.nvfp4_calib_mfma(waves, iters, sink.data_ptr(), stream()), max(5, steps // 5), 2, 0.2)
+    flops = waves * iters * 4 * 32768.0
+    out["mfma_f16"] = {"tflops": round(flops / (m_ms * 1e-3) / 1e12, 1),
+                       "frac_peak": round(flops / (m_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                       "what": f"{waves} wavefronts x {4 * iters} independent 32x32x16 fp16 MFMAs"}
+    return out
+
+
 def _events(n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
@@ -210,10 +270,47 @@ def bench_prefill(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: in
     return res, (p, w)
 
 
-def cpu_baseline_prefill(p, sample_rows: int = 4096):
-    """The oracle as it stands, on a bounded sample: quantize `sample_rows` rows of X under
-    the tensor's global scale and compute those rows of Y against the oracle-quantized W."""
+def _blas_threads() -> int:
     import threadpoolctl
+    info = threadpoolctl.threadpool_info()
+    return int(max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1]))
+
+
+def bench_quantize_modes(nv, steps: int, settle_s: float, rotate: int = 8) -> dict:
+    """The prefill activation's quantizer on its own, back to back from a HIP graph (8 rotating
+    copies of X): per tensor (two passes over X: the grid-wide max, then the encoding) and with a
+    calibrated (given) global scale (one pass)."""
+    p = workloads.PREFILL
+    dev = torch.device("cuda:0")
+    x0 = torch.from_numpy(p.x()).to(dev).to(torch.bfloat16)
+    xs = [x0] + [x0.roll(i + 1, dims=0).contiguous() for i in range(rotate - 1)]
+    outs = [nv.quantize(x) for x in xs]
+    given = outs[0].global_scale.clone()
+    gouts = [nv.quantize(x, "given", global_scale=given) for x in xs]
+
+    def two_pass(i):
+        nv.quantize(xs[i % rotate], out=outs[i % rotate])
+
+    def given_scale(i):
+        nv.quantize(xs[i % rotate], "given", global_scale=given, out=gouts[i % rotate])
+
+    qbytes = _bytes_quantize(p.M, p.K)
+    out = {"algorithmic_bytes": qbytes}
+    for name, fn in (("per_tensor", two_pass), ("given_scale", given_scale)):
+        us = _graph_us(fn, 2 * rotate, max(4, steps // 5), settle_s)
+        out[name] = {"us": round(us, 2), "gbs": round(qbytes / (us * 1e-6) / 1e9, 1),
+                     "frac_hbm": round(qbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    return out
+
+
+def cpu_baseline(p, sample_rows: int = 4096, decode_m: int = 16, d=None):
+    """The oracle as it stands, timed on the host's cores on bounded samples of the workloads:
+    (1) prefill: quantize `sample_rows` rows of X under the tensor's global scale and compute
+    those rows of Y against the oracle-quantized W (the headline value, in GEMM TFLOP/s);
+    (2) the quantizer alone on those rows (GB/s of algorithmic bytes); (3) a decode step at
+    M = `decode_m` on the MLP down projection: per-token quantize plus the GEMM against the whole
+    oracle-quantized W[5120 x 17408] (GB/s of the GPU path's algorithmic bytes).  numpy's
+    elementwise quantize runs on one thread; the fp64 matmuls on the BLAS thread pool."""
     from oracle import nvfp4_ref as ref
 
     x = p.x()
@@ -222,27 +319,75 @@ def cpu_baseline_prefill(p, sample_rows: int = 4096):
     rows = np.arange(sample_rows)
     t0 = time.perf_counter()
     aq = ref.quantize(x[rows], ref.GIVEN, float(sg[0]))
+    tq = time.perf_counter() - t0
     ref.gemm(aq, wq)
     dt = time.perf_counter() - t0
-    info = threadpoolctl.threadpool_info()
-    cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    threads = _blas_threads()
+    host_cores = len(os.sched_getaffinity(0))
     flops = 2.0 * sample_rows * p.N * p.K
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    d = d or workloads.DECODE
+    dwq = ref.quantize(d.w())                                     # offline, untimed
+    xd = d.x(decode_m)
+    t1 = time.perf_counter()
+    ref.gemm(ref.quantize(xd, ref.PER_ROW), dwq)
+    td = time.perf_counter() - t1
+    dbytes = d.N * d.K * (0.5 + 1 / 16) + decode_m * d.K * (2 + 0.5 + 1 / 16) + decode_m * d.N * 2
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "host_cores": host_cores,
             "sample": f"{sample_rows} of {p.M} rows of X: quantize (numpy, 1 thread) + fp64 GEMM against "
-                      f"all {p.N} W rows (dequantize W + BLAS matmul, {cores} threads); {dt:.1f} s"}
+                      f"all {p.N} W rows (dequantize W + BLAS matmul, {threads} threads); {dt:.1f} s",
+            "quantize": {"gbs": round(_bytes_quantize(sample_rows, p.K) / tq / 1e9, 4), "threads": 1,
+                         "sample": f"{sample_rows} x {p.K} bf16 rows of the prefill X, {tq:.2f} s"},
+            "decode": {"gbs": round(dbytes / td / 1e9, 4), "us": round(td * 1e6, 1), "threads": threads,
+                       "sample": f"M = {decode_m} per-token quantize + fp64 GEMM against W[{d.N} x {d.K}] "
+                                 f"(whole step), {td:.2f} s"}}
 
 
 def bench_decode(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: int = 8):
     """Per-token quantize + decode GEMM for M in {1, 4, 16} on two weight shapes: the MLP down
     projection W[5120 x 17408] (K-split kernel) and the up projection W[17408 x 5120] (balanced
-    kernel), each with 8 distinct weight copies rotating so W never comes from the cache."""
+    kernel), each with 8 distinct weight copies rotating so W never comes from the cache.  Each
+    figure is the mean over back-to-back launches replayed from a HIP graph (the quantize alone,
+    the GEMM alone, and the step of both)."""
     out = {}
     for label, d in (("down", workloads.DECODE), ("up", workloads.DECODE_UP)):
         out[label] = _bench_decode_shape(nv, d, steps, warmup, settle_s, rotate)
     return out
 
 
-def _bench_decode_shape(nv, d, steps: int, warmup: int, settle_s: float, rotate: int):
+def _graph_us(fn, reps: int = 20, replays: int = 10, settle_s: float = 0.3) -> float:
+    """Mean GPU time of one fn(i) call: `reps` calls captured in one HIP graph, the graph replayed
+    `replays` times between two events.  Kernels of a few microseconds would otherwise be timed
+    with the host's launch latency in between (the GPU outruns the Python launcher); inside a
+    graph they run back to back, as in a serving loop, and the figure includes the GPU's own
+    gaps between dependent kernels."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(reps):
+            fn(i)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        graph.replay()
+        torch.cuda.synchronize()
+    e0, e1 = _events(2)
+    e0.record()
+    for _ in range(replays):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (replays * reps)
+    del graph
+    return us
+
+
+def _bench_decode_shape(nv, d, steps: int, warmup: int, settle_s: float, rotate: int, Ms=None):
     dev = torch.device("cuda:0")
     w0 = torch.from_numpy(d.w()).to(dev).to(torch.bfloat16)
     ws = [nv.quantize(w0)]
@@ -250,34 +395,34 @@ def _bench_decode_shape(nv, d, steps: int, warmup: int, settle_s: float, rotate:
         q = ws[0]
         ws.append(nv.NVFP4Tensor(q.codes.clone(), q.scales.clone(), q.global_scale.clone()))
     out = {"N": d.N, "K": d.K}
-    for M in d.Ms:
+    for M in Ms or d.Ms:
         x = torch.from_numpy(d.x(M)).to(dev).to(torch.bfloat16)
         a = nv.quantize(x, "per_row")
         y = torch.empty((M, d.N), dtype=torch.bfloat16, device=dev)
-        _settle(lambda i: (nv.quantize(x, "per_row", out=a), nv.gemm(a, ws[i % rotate], torch.bfloat16, out=y)),
-                settle_s)
-        for i in range(warmup):
+        reps = max(2 * rotate, 16)
+
+        def quant(i):
             nv.quantize(x, "per_row", out=a)
+
+        def gemm(i):
             nv.gemm(a, ws[i % rotate], torch.bfloat16, out=y)
-        torch.cuda.synchronize()
-        evs = [_events(3) for _ in range(steps)]
-        for i in range(steps):
-            evs[i][0].record()
-            nv.quantize(x, "per_row", out=a)
-            evs[i][1].record()
-            nv.gemm(a, ws[i % rotate], torch.bfloat16, out=y)
-            evs[i][2].record()
-        torch.cuda.synchronize()
-        q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-        g_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+        def step(i):
+            quant(i)
+            gemm(i)
+
+        q_ms = _graph_us(quant, reps, max(4, steps // 5), settle_s) * 1e-3
+        g_ms = _graph_us(gemm, reps, max(4, steps // 5), settle_s) * 1e-3
+        s_ms = _graph_us(step, reps, max(4, steps // 5), settle_s) * 1e-3
         wbytes = d.N * d.K * (0.5 + 1 / 16) + 4
         abytes = M * d.K * (0.5 + 1 / 16) + 4 * M
         ybytes = M * d.N * 2
         gb = (wbytes + abytes + ybytes)
-        out[f"M={M}"] = {"gemm_us": g_ms * 1e3, "quant_us": q_ms * 1e3,
-                         "gemm_gbs": gb / (g_ms * 1e-3) / 1e9,
-                         "gemm_frac_hbm": gb / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                         "quant_gbs": _bytes_quantize(M, d.K) / (q_ms * 1e-3) / 1e9}
+        out[f"M={M}"] = {"gemm_us": round(g_ms * 1e3, 2), "quant_us": round(q_ms * 1e3, 2),
+                         "step_us": round(s_ms * 1e3, 2), "gemm_bytes": gb,
+                         "gemm_gbs": round(gb / (g_ms * 1e-3) / 1e9, 1),
+                         "gemm_frac_hbm": round(gb / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "quant_gbs": round(_bytes_quantize(M, d.K) / (q_ms * 1e-3) / 1e9, 1)}
     return out
 
 
@@ -731,6 +876,26 @@ def main() -> int:
                 traffic = t.get("prefill_gemm_bytes_per_launch")
         except (ValueError, OSError):
             traffic = None
+    print("[bench] decode (config: X[M x K] bf16 per-token quantize + GEMM, M in {1, 4, 16})", file=sys.stderr,
+          flush=True)
+    decode = bench_decode(nv, args.steps, args.warmup, min(args.settle_s, 0.3))
+    decode["down"]["kernel"] = "K-split decode kernel (N <= 32 x CUs)"
+    decode["up"]["kernel"] = "balanced-rows decode kernel (N > 32 x CUs)"
+    print("[bench] quantize modes", file=sys.stderr, flush=True)
+    qmodes = bench_quantize_modes(nv, args.steps, min(args.settle_s, 0.3))
+    print("[bench] calibration", file=sys.stderr, flush=True)
+    calib = calibration(args.steps, args.warmup, {"quantize_bytes": res["qbytes"],
+                                                  "decode_weight_bytes": workloads.DECODE.N * workloads.DECODE.K
+                                                  * (0.5 + 1 / 16)})
+    read_q = calib["quantize_bytes"]["read_gbs"]
+    read_w = calib["decode_weight_bytes"]["read_gbs"]
+    for shape in ("down", "up"):
+        for k, v in decode[shape].items():
+            if k.startswith("M="):
+                v["gemm_frac_measured_read"] = round(v["gemm_gbs"] / read_w, 4)
+    for k, v in qmodes.items():
+        if isinstance(v, dict):
+            v["frac_measured_read"] = round(v["gbs"] / read_q, 4)
     value = res["flops"] / (res["ms_per_step"] * 1e-3) / 1e12
     line = {
         "metric": "NVFP4 W4A4 GEMM TFLOP/s @M=4096 + quantize GB/s, as % of roofline",
@@ -758,14 +923,20 @@ def main() -> int:
                      "frac_mfma_f16": round(res["gemm_tflops"] / MFMA_F16_PEAK_TFLOPS, 4)},
             "quantize": {"us": round(res["quant_ms"] * 1e3, 2), "gbs": round(res["quant_gbs"], 1),
                          "frac_hbm": round(res["quant_gbs"] / HBM_PEAK_GBS, 4),
+                         "frac_measured_read": round(res["quant_gbs"] / read_q, 4),
                          "algorithmic_bytes": res["qbytes"]},
+            "quantize_modes": qmodes,
+            "decode": decode,
         },
+        "calibration": {**calib,
+                        "gemm_frac_measured_mfma": round(res["gemm_tflops"] / calib["mfma_f16"]["tflops"], 4)},
         "context": {"pages": "17.5 GiB NVFP4 checkpoint and +14-19% prefill vs the other recipes compared; "
                              "hardware not stated",
                     "bf16_library_gemm": bf16_library_gemm(min(args.steps, 20), args.warmup, args.settle_s)},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_prefill(p)
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(p)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -27,7 +27,10 @@ def test_source_digest_ignores_comments_and_whitespace(tmp_path):
 
 
 def test_cpu_baseline_record():
-    r = bench.cpu_baseline_prefill(workloads.TINY, sample_rows=16)
+    small_decode = workloads.Decode(N=64, K=512)
+    r = bench.cpu_baseline(workloads.TINY, sample_rows=16, decode_m=4, d=small_decode)
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
-    assert r["value"] > 0 and r["cores"] >= 1
+    assert r["value"] > 0 and r["cores"] >= 1 and r["host_cores"] >= 1
     assert "16 of 16 rows" in r["sample"]
+    assert r["quantize"]["gbs"] > 0 and r["quantize"]["threads"] == 1
+    assert r["decode"]["gbs"] > 0 and "M = 4" in r["decode"]["sample"]

@@ -2,9 +2,8 @@
 per-tensor partial maxima live in a static device array of the library): called through the C
 ABI, its codes, scale bytes and global scales equal those of nvfp4_quantize with a workspace,
 bit for bit, on two calls in a row (the second smaller, so stale contents of the shared array
-from the first call would show), in every scale mode."""
-import ctypes
-
+from the first call would show), in every scale mode, and per tensor on bf16 and fp32 shapes
+from one block to 16384 x 5120."""
 import numpy as np
 import pytest
 import torch
@@ -61,6 +60,20 @@ def test_no_alloc_matches_workspace_entry(mode):
         for a, b, name in zip(got, want, ("codes", "scales", "global scale")):
             assert torch.equal(a.view(torch.uint8) if a.dtype != torch.uint8 else a,
                                b.view(torch.uint8) if b.dtype != torch.uint8 else b), (rows, cols, mode, name)
+
+
+# Per-tensor shapes from one 16-element block to the sweep's 16384 x 5120 activation, bf16 and fp32.
+@pytest.mark.parametrize("rows,cols,bf16", [(4096, 5120, True), (8192, 5120, True), (16384, 5120, True),
+                                            (1000, 4096, False), (5120, 4096, False), (3, 48, True),
+                                            (1, 16, False)])
+def test_no_alloc_per_tensor_shapes(rows, cols, bf16):
+    x = to_gpu(workloads.activation(6, rows, rows, cols, outlier_frac=0.01), bf16)
+    for _ in range(2):                       # the second call finds what the first left in the array
+        got = _no_alloc(x, 0)
+        want = _with_workspace(x, 0)
+        torch.cuda.synchronize()
+        for a, b, name in zip(got, want, ("codes", "scales", "global scale")):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), (rows, cols, bf16, name)
 
 
 def test_no_alloc_second_call_smaller_max():
