@@ -557,6 +557,17 @@ def bench_gdn_gates(nv, steps: int, warmup: int, settle_s: float = 0.0):
 MFMA_FP4_PEAK_TFLOPS = 10100.0   # MI355X dense FP4 / FP6
 
 
+def sweep_weight_draws(sw, launches, dev):
+    """The sweep's weights as the bench draws them, launch by launch: bf16 N(0, 0.02) tensors per
+    segment from one seeded torch generator on the GPU (drawing 22.8 G values on the host would
+    take minutes).  Yields (launch index, launch, [bf16 weight per segment]); the same seed gives
+    the same tensors to every caller, so the parity test checks exactly what the bench times."""
+    gen = torch.Generator(device=dev).manual_seed(sw.seed)
+    for li, L in enumerate(launches):
+        yield li, L, [torch.randn(n, L.K, device=dev, dtype=torch.bfloat16, generator=gen).mul_(sw.w_sigma)
+                      for n in L.widths]
+
+
 def bench_sweep(nv, steps: int, warmup: int, settle_s: float = 0.0):
     """Every linear GEMM of the synthetic 64-layer hybrid (48 GDN + 16 attention layers, hidden
     5120, MLP 17408) at M = 16384 prefill tokens: per launch, the per-tensor NVFP4 quantize of
@@ -566,16 +577,12 @@ def bench_sweep(nv, steps: int, warmup: int, settle_s: float = 0.0):
     sw = workloads.SWEEP
     dev = torch.device("cuda:0")
     launches = workloads.sweep_launches(sw)
-    gen = torch.Generator(device=dev).manual_seed(sw.seed)
     weights = []
-    for li, L in enumerate(launches):
+    for li, L, segs in sweep_weight_draws(sw, launches, dev):
         if li % 32 == 0:
             print(f"[sweep] quantizing weights of launch {li}/{len(launches)}", file=sys.stderr, flush=True)
-        qs = []
-        for n in L.widths:
-            w = torch.randn(n, L.K, device=dev, dtype=torch.bfloat16, generator=gen).mul_(sw.w_sigma)
-            qs.append(nv.quantize(w))
-            del w
+        qs = [nv.quantize(w) for w in segs]
+        del segs
         weights.append((torch.cat([q.codes for q in qs]), torch.cat([q.scales for q in qs]),
                         torch.cat([q.global_scale for q in qs])))
     xs = {K: torch.from_numpy(sw.x(0, K)).to(dev).to(torch.bfloat16) for K in sorted({L.K for L in launches})}
