@@ -22,9 +22,9 @@
  * "NVFP4 W4A4 Quantization Compresses 27B Hybrid Models" (thevalue.engineering), section
  * "Challenging the Recurrence Fragility Assumption"; W4A4 on every linear layer and the
  * 16-element block from "Why Gated DeltaNet Survives 4-Bit Quantization" (kipquest),
- * "The deep dive"; the global-scale mismatch between per-module-calibrated checkpoints and
- * fused-module GEMM kernels, and its repair, from the paper's abstract (Lattice and
- * kipquest pages).
+ * "The deep dive"; the global-scale mismatch (modules calibrated one by one, run as one
+ * fused GEMM under a single scale) and its repair from the paper's abstract (Lattice and
+ * kipquest pages).  Each declaration below names the passage its operation follows.
  *
  * Data format (identical for activations and weights):
  *   codes [rows, cols/2]  uint8, row-major, contiguous; two 4-bit E2M1 codes per byte, the
@@ -78,7 +78,13 @@ typedef enum {
 #define NVFP4_MAX_SEGMENTS 64
 
 /*
- * Quantize X[rows, cols] to NVFP4 (format above).
+ * Quantize X[rows, cols] to NVFP4 (format above).  The element format -- E2M1 values with one
+ * E4M3 scale per 16-element block -- is the one "NVFP4 W4A4 Quantization Compresses 27B Hybrid
+ * Models" describes ("Challenging the Recurrence Fragility Assumption"); "Why Gated DeltaNet
+ * Survives 4-Bit Quantization" ("The deep dive") quantizes activations this way at every
+ * linear layer, the block of sixteen confining an outlier channel's damage to its own block.
+ * The pages imply an FP32 per-module global scale (the mismatch in the paper abstract) without
+ * its formula: s_g = fl32(max|x| / 2688) is this library's reading.
  *   x             [rows, ldx] of x_dtype (NVFP4_BF16 or NVFP4_F32); 16-byte aligned, and
  *                 ldx * element size a multiple of 16 bytes; ldx >= cols.
  *   rows >= 0     rows == 0 is a no-op except that PER_TENSOR writes s_g = 0.
@@ -96,6 +102,8 @@ int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64
                    uint8_t* codes, uint8_t* scales, float* global_scale, int mode,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace nvfp4_quantize needs for this shape and mode (4 KB per tensor, 0
+ * per row or given); 0 for a bad shape. */
 size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols, int mode);
 
 /*
@@ -114,6 +122,9 @@ int nvfp4_quantize_no_alloc(const void* x, int x_dtype, int64_t rows, int64_t co
                             uint8_t* codes, uint8_t* scales, float* global_scale, int mode, void* stream);
 
 /*
+ * The W4A4 linear layer: weights and activations both in the 4-bit block format, as "Why Gated
+ * DeltaNet Survives 4-Bit Quantization" ("The deep dive") runs every linear layer of the hybrid
+ * model; the paper abstract credits this recipe with the fastest prefill of those compared.
  * Y[M, N] = A . W^T with A = NVFP4 [M, K] activations and W = NVFP4 [N, K] weights, both
  * K-major; FP32 accumulation of the exactly dequantized operands, then
  * y = (acc * a_global[m or 0]) * w_global[0], stored as y_dtype (bf16: round to nearest
@@ -134,7 +145,11 @@ int nvfp4_gemm(int64_t M, int64_t N, int64_t K,
                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The fused-module GEMM: W is the concatenation along N of num_segments separately
+ * The fused-module GEMM, the repair of the global-scale mismatch the paper abstract reports
+ * (modules calibrated one by one, each with its own global scale, served by a kernel that fuses
+ * them into one GEMM); "Quantizing All Layers Reveals Recurrent Memory Is Robust" ("Block
+ * Scaling and the Geography of Outliers") describes the bug as a single scale applied to every
+ * fused module.  W is the concatenation along N of num_segments separately
  * quantized modules (codes [sum N_i, K/2], scales [sum N_i, K/16]); output column n of
  * segment i is scaled by that module's own global scale w_globals[i]:
  *   Y[:, off_i : off_i + N_i] = A . W_i^T,  off_i = N_0 + ... + N_{i-1}.
@@ -156,7 +171,9 @@ int nvfp4_gemm_fused_segments(int64_t M, int64_t K,
 
 /*
  * The (fused-module) GEMM with its output quantized to NVFP4 for the next linear layer, in
- * the same launch: Y is never written in bf16 or fp32.  For every output element the fp32
+ * the same launch: Y is never written in bf16 or fp32.  Every linear layer takes 4-bit
+ * activations ("Why Gated DeltaNet Survives 4-Bit Quantization", "The deep dive"), so a layer
+ * whose output feeds another linear layer can hand it over already quantized.  For every output element the fp32
  * value y = (acc * a_global[m or 0]) * w_globals[seg(n)] is the one nvfp4_gemm_fused_segments
  * would store as fp32 for the same shape; each 16-column block of an output row is then
  * encoded exactly as nvfp4_quantize in NVFP4_SCALE_GIVEN mode encodes it under
@@ -211,6 +228,8 @@ int nvfp4_gemm_fused_gdn_gates(int64_t M, int64_t K,
                                const float* a_log, const float* dt_bias, float* g, float* beta,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace the GEMM entry points need for this shape: 0 for every shape at
+ * present (decode reduces K inside the workgroup); kept so the ABI need not change. */
 size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /*
