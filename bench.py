@@ -825,6 +825,9 @@ def main() -> int:
                                            "sweep", "swiglu"],
                     default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-step", action="store_true",
+                    help="time the prefill step alone (for profiling runs): no decode, quantize modes, "
+                         "calibration, library GEMM or CPU baseline")
     ap.add_argument("--traffic-json", default=TRAFFIC_JSON,
                     help="HBM bytes per GEMM launch measured with rocprofv3 counters")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -883,6 +886,11 @@ def main() -> int:
                 traffic = t.get("prefill_gemm_bytes_per_launch")
         except (ValueError, OSError):
             traffic = None
+    if args.only_step:
+        print(json.dumps({"workload": "prefill step only", "ms_per_step": round(res["ms_per_step"], 4),
+                          "gemm_ms": round(res["gemm_ms"], 4), "quant_us": round(res["quant_ms"] * 1e3, 2),
+                          "gemm_tflops": round(res["gemm_tflops"], 2), "traffic": traffic}), flush=True)
+        return 0
     print("[bench] decode (config: X[M x K] bf16 per-token quantize + GEMM, M in {1, 4, 16})", file=sys.stderr,
           flush=True)
     decode = bench_decode(nv, args.steps, args.warmup, min(args.settle_s, 0.3))
