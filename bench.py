@@ -303,6 +303,80 @@ def bench_quantize_modes(nv, steps: int, settle_s: float, rotate: int = 8) -> di
     return out
 
 
+def oracle_configs(fused_rows: int = 1024, sweep_rows: int = 64) -> dict:
+    """The oracle on every workload config, for the baseline table: per config the quantizer
+    (per-tensor on X; per-row for decode) in GB/s of algorithmic bytes and the fp64 GEMM in
+    GFLOP/s, on bounded samples (whole tensors where they take seconds).  Weights are quantized
+    first, untimed (offline in the served model).  Sweep: the first launch of each kind, its
+    activation quantized in full and `sweep_rows` output rows computed."""
+    from oracle import nvfp4_ref as ref
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        out = fn()
+        return out, time.perf_counter() - t0
+
+    def note(what):
+        print(f"[oracle] {what}", file=sys.stderr, flush=True)
+
+    res = {"threads_quantize": 1, "threads_gemm": _blas_threads(), "host_cores": len(os.sched_getaffinity(0))}
+    t = workloads.TINY
+    wq = ref.quantize(t.w())
+    aq, tq = timed(lambda: ref.quantize(t.x()))
+    _, tg = timed(lambda: ref.gemm(aq, wq))
+    res["tiny"] = {"quantize_gbs": _bytes_quantize(t.M, t.K, 4) / tq / 1e9, "gemm_gflops": 2.0 * t.M * t.N * t.K / tg / 1e9,
+                   "sample": "whole"}
+    note("prefill")
+    p = workloads.PREFILL
+    wq = ref.quantize(p.w())
+    x = p.x()
+    aq, tq = timed(lambda: ref.quantize(x))
+    _, tg = timed(lambda: ref.gemm(aq, wq))
+    res["prefill"] = {"quantize_gbs": _bytes_quantize(p.M, p.K) / tq / 1e9, "gemm_gflops": p.flops / tg / 1e9,
+                      "sample": "whole"}
+    note("decode")
+    d = workloads.DECODE
+    wq = ref.quantize(d.w())
+    for M in d.Ms:
+        xd = d.x(M)
+        aq, tq = timed(lambda: ref.quantize(xd, ref.PER_ROW))
+        _, tg = timed(lambda: ref.gemm(aq, wq))
+        res[f"decode_M{M}"] = {"quantize_gbs": _bytes_quantize(M, d.K) / tq / 1e9,
+                               "gemm_gflops": 2.0 * M * d.N * d.K / tg / 1e9, "sample": "whole"}
+    note("fused")
+    f = workloads.FUSED
+    segs = [ref.quantize(f.w(i)) for i in range(len(f.widths))]
+    x = f.x()
+    aq, tq = timed(lambda: ref.quantize(x))
+    rows = np.arange(fused_rows)
+    _, tg = timed(lambda: ref.fused_segments(aq, segs, rows))
+    res["fused"] = {"quantize_gbs": _bytes_quantize(f.M, f.K) / tq / 1e9,
+                    "gemm_gflops": 2.0 * fused_rows * f.N * f.K / tg / 1e9,
+                    "sample": f"quantize whole X; GEMM {fused_rows} of {f.M} rows"}
+    sw = workloads.SWEEP
+    launches = workloads.sweep_launches(sw)
+    kinds = {}
+    for idx, L in enumerate(launches):
+        if L.kind in kinds:
+            continue
+        note(f"sweep {L.kind}")
+        segs = [ref.quantize(sw.w(idx, s_, n, L.K)) for s_, n in enumerate(L.widths)]
+        x = sw.x(idx, L.K)
+        aq, tq = timed(lambda: ref.quantize(x))
+        _, tg = timed(lambda: ref.fused_segments(aq, segs, np.arange(sweep_rows)))
+        kinds[L.kind] = {"quantize_gbs": _bytes_quantize(sw.M, L.K) / tq / 1e9,
+                         "gemm_gflops": 2.0 * sweep_rows * L.N * L.K / tg / 1e9}
+        del segs, x, aq
+    res["sweep"] = {"per_kind": kinds, "sample": f"first launch of each kind: quantize whole X (M = {sw.M}); "
+                                                 f"GEMM {sweep_rows} rows"}
+    for v in res.values():
+        if isinstance(v, dict):
+            for k in ("quantize_gbs", "gemm_gflops"):
+                if k in v:
+                    v[k] = round(v[k], 4)
+    return res
+
+
 def cpu_baseline(p, sample_rows: int = 4096, decode_m: int = 16, d=None):
     """The oracle as it stands, timed on the host's cores on bounded samples of the workloads:
     (1) prefill: quantize `sample_rows` rows of X under the tensor's global scale and compute
@@ -485,18 +559,21 @@ def bench_nvfp4_out(nv, steps: int, warmup: int, settle_s: float = 0.0):
 
 
 def _mean_ms(fn, steps: int, warmup: int, settle_s: float) -> float:
-    """Mean duration of fn(i) between events on the current stream, after settling and warmup."""
-    _settle(fn, settle_s)
-    for i in range(warmup):
+    """Mean GPU time of fn(i), replayed back to back from a HIP graph (see _graph_us): calls of
+    more than a millisecond one per replay, `steps` replays; shorter ones 16 per replay, so the
+    host's launch latency never enters."""
+    for i in range(max(1, warmup)):
         fn(i)
     torch.cuda.synchronize()
-    evs = [_events(2) for _ in range(steps)]
-    for i in range(steps):
-        evs[i][0].record()
-        fn(i)
-        evs[i][1].record()
+    e0, e1 = _events(2)
+    e0.record()
+    fn(0)
+    e1.record()
     torch.cuda.synchronize()
-    return float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    once_ms = e0.elapsed_time(e1)
+    if once_ms > 1.0:
+        return _graph_us(fn, 1, max(1, steps), settle_s) * 1e-3
+    return _graph_us(fn, 16, max(4, steps // 4), settle_s) * 1e-3
 
 
 def _rel_rms(got: torch.Tensor, want: torch.Tensor) -> float:
@@ -739,17 +816,7 @@ def bench_kv_fp8(nv, steps: int, warmup: int, settle_s: float = 0.0, rotate: int
     for name, fn in (("quantize", lambda i: nv.fp8_kv_quantize(ks[i % rotate], s, out=qs[i % rotate])),
                      ("dequantize", lambda i: nv.fp8_kv_dequantize(qs[i % rotate], s, torch.bfloat16,
                                                                  out=ys[i % rotate]))):
-        _settle(fn, settle_s)
-        for i in range(warmup):
-            fn(i)
-        torch.cuda.synchronize()
-        evs = [_events(2) for _ in range(steps)]
-        for i in range(steps):
-            evs[i][0].record()
-            fn(i)
-            evs[i][1].record()
-        torch.cuda.synchronize()
-        us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+        us = _mean_ms(fn, steps, warmup, settle_s) * 1e3
         gbs = 3.0 * n / (us * 1e-6) / 1e9
         out[name] = {"us": us, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
     return out
@@ -822,7 +889,7 @@ def main() -> int:
     ap.add_argument("--settle-s", type=float, default=1.0,
                     help="seconds of untimed steps before the warmup steps, for steady clocks")
     ap.add_argument("--workload", choices=["prefill", "decode", "fused", "nvfp4_out", "kv_fp8", "gdn_gates", "mxfp4",
-                                           "sweep", "swiglu"],
+                                           "sweep", "swiglu", "oracle"],
                     default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-step", action="store_true",
@@ -843,6 +910,10 @@ def main() -> int:
               f"(every GPU runs the same kernels on its own tokens); --gpus {args.gpus} is not "
               f"supported.", file=sys.stderr)
         return 2
+    if args.workload == "oracle":
+        # CPU only: the oracle on every config (no GPU is used).
+        print(json.dumps({"workload": "oracle", "results": oracle_configs()}))
+        return 0
     import nvfp4_w4a4_block_amd as nv
 
     copy_calibration(args.copy_calibration_mb)
