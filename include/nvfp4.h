@@ -38,7 +38,11 @@
  *
  * Conventions of every entry point:
  *   * Pointers are DEVICE pointers unless marked (host).  The caller owns all memory; the
- *     library never allocates device memory, never synchronises and keeps no state.
+ *     library never allocates device memory and never synchronises.  Its only state is set up
+ *     once per device by the first call that launches work there (kernel limits, the compute-
+ *     unit count, the address of nvfp4_quantize_no_alloc's static array), under std::call_once,
+ *     for the device the call's stream belongs to: first calls from several host threads at
+ *     once are safe.
  *   * Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = default stream)
  *     and is stream-ordered; the global scales never travel to the host.
  *   * Return value: an nvfp4_status.  Argument errors are detected on the host before any
