@@ -44,6 +44,24 @@ int make_segments(int num_segments, const int64_t* seg_n, SegmentTable& seg, int
   return NVFP4_OK;
 }
 
+// Arguments of the quantize entry points other than the workspace.
+int check_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, const uint8_t* codes,
+                   const uint8_t* scales, const float* global_scale, int mode) {
+  if (x_dtype != NVFP4_BF16 && x_dtype != NVFP4_F32) return NVFP4_ERR_INVALID_ARG;
+  if (mode != NVFP4_SCALE_PER_TENSOR && mode != NVFP4_SCALE_PER_ROW && mode != NVFP4_SCALE_GIVEN)
+    return NVFP4_ERR_INVALID_ARG;
+  if (rows < 0 || cols <= 0 || cols % 16 != 0 || ldx < cols) return NVFP4_ERR_INVALID_ARG;
+  if ((uint64_t)rows * (uint64_t)(cols / 16) >= (1ull << 31)) return NVFP4_ERR_UNSUPPORTED;
+  if ((rows > 0 || mode == NVFP4_SCALE_PER_TENSOR) && (!global_scale || !aligned(global_scale, 4)))
+    return NVFP4_ERR_INVALID_ARG;
+  const int64_t esize = x_dtype == NVFP4_BF16 ? 2 : 4;
+  if (rows > 0) {
+    if (!x || !codes || !scales) return NVFP4_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || (ldx * esize) % 16 != 0 || !aligned(codes, 8)) return NVFP4_ERR_INVALID_ARG;
+  }
+  return NVFP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -69,18 +87,8 @@ size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols, int mode) {
 int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, uint8_t* codes,
                    uint8_t* scales, float* global_scale, int mode, void* workspace, size_t workspace_bytes,
                    void* stream) {
-  if (x_dtype != NVFP4_BF16 && x_dtype != NVFP4_F32) return NVFP4_ERR_INVALID_ARG;
-  if (mode != NVFP4_SCALE_PER_TENSOR && mode != NVFP4_SCALE_PER_ROW && mode != NVFP4_SCALE_GIVEN)
-    return NVFP4_ERR_INVALID_ARG;
-  if (rows < 0 || cols <= 0 || cols % 16 != 0 || ldx < cols) return NVFP4_ERR_INVALID_ARG;
-  if ((uint64_t)rows * (uint64_t)(cols / 16) >= (1ull << 31)) return NVFP4_ERR_UNSUPPORTED;
-  if ((rows > 0 || mode == NVFP4_SCALE_PER_TENSOR) && (!global_scale || !aligned(global_scale, 4)))
-    return NVFP4_ERR_INVALID_ARG;
-  const int64_t esize = x_dtype == NVFP4_BF16 ? 2 : 4;
-  if (rows > 0) {
-    if (!x || !codes || !scales) return NVFP4_ERR_INVALID_ARG;
-    if (!aligned(x, 16) || (ldx * esize) % 16 != 0 || !aligned(codes, 8)) return NVFP4_ERR_INVALID_ARG;
-  }
+  const int st = check_quantize(x, x_dtype, rows, cols, ldx, codes, scales, global_scale, mode);
+  if (st != NVFP4_OK) return st;
   const size_t need = quantize_workspace_bytes(rows, cols, mode);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 4))) return NVFP4_ERR_WORKSPACE;
   return launch_quantize(x, x_dtype, rows, cols, ldx, codes, scales, global_scale, mode, workspace,
@@ -89,22 +97,12 @@ int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64
 
 int nvfp4_quantize_no_alloc(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, uint8_t* codes,
                             uint8_t* scales, float* global_scale, int mode, void* stream) {
-  if (x_dtype != NVFP4_BF16 && x_dtype != NVFP4_F32) return NVFP4_ERR_INVALID_ARG;
-  if (mode != NVFP4_SCALE_PER_TENSOR && mode != NVFP4_SCALE_PER_ROW && mode != NVFP4_SCALE_GIVEN)
-    return NVFP4_ERR_INVALID_ARG;
-  if (rows < 0 || cols <= 0 || cols % 16 != 0 || ldx < cols) return NVFP4_ERR_INVALID_ARG;
-  if ((uint64_t)rows * (uint64_t)(cols / 16) >= (1ull << 31)) return NVFP4_ERR_UNSUPPORTED;
-  if ((rows > 0 || mode == NVFP4_SCALE_PER_TENSOR) && (!global_scale || !aligned(global_scale, 4)))
-    return NVFP4_ERR_INVALID_ARG;
-  const int64_t esize = x_dtype == NVFP4_BF16 ? 2 : 4;
-  if (rows > 0) {
-    if (!x || !codes || !scales) return NVFP4_ERR_INVALID_ARG;
-    if (!aligned(x, 16) || (ldx * esize) % 16 != 0 || !aligned(codes, 8)) return NVFP4_ERR_INVALID_ARG;
-  }
+  int st = check_quantize(x, x_dtype, rows, cols, ldx, codes, scales, global_scale, mode);
+  if (st != NVFP4_OK) return st;
   if (quantize_workspace_bytes(rows, cols, mode) > quantize_scratch_bytes()) return NVFP4_ERR_WORKSPACE;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   DeviceInfo dev;
-  const int st = device_info(s, dev);
+  st = device_info(s, dev);
   if (st != NVFP4_OK) return st;
   return launch_quantize(x, x_dtype, rows, cols, ldx, codes, scales, global_scale, mode, dev.quant_scratch, s);
 }

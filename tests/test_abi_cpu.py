@@ -77,6 +77,21 @@ def test_quantize_argument_errors(nv):
     assert nv.lib.nvfp4_quantize_workspace_size(4096, 5120, 2) == 0
 
 
+def test_quantize_no_alloc_argument_errors(nv):
+    # The same host-side checks as nvfp4_quantize, without a workspace argument.
+    def qn(x=A16, dt=1, rows=4, cols=32, ldx=32, codes=A16, scales=A16, g=A16, mode=0):
+        return nv.lib.nvfp4_quantize_no_alloc(x, dt, rows, cols, ldx, codes, scales, g, mode, None)
+    assert qn(cols=24, ldx=24) == 1
+    assert qn(rows=-1) == 1
+    assert qn(ldx=16) == 1
+    assert qn(x=None) == 1
+    assert qn(g=None) == 1
+    assert qn(x=MIS) == 1
+    assert qn(dt=7) == 1
+    assert qn(mode=5) == 1
+    assert qn(rows=1 << 27, cols=1 << 10, ldx=1 << 10) == 2
+
+
 def g(nv, M=32, N=32, K=128, a=A16, sa=A16, ga=A16, pr=0, w=A16, sw=A16, gw=A16, y=A16, dt=1, ldy=32):
     return nv.lib.nvfp4_gemm(M, N, K, a, sa, ga, pr, w, sw, gw, y, dt, ldy, None, 0, None)
 
