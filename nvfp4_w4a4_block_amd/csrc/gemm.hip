@@ -1793,6 +1793,225 @@ __global__ __launch_bounds__(kDwThreads) void gemm_mx_decode_rows_kernel(GemmArg
   }
 }
 
+// ------------------------------------------------------------------ decode, one or two tokens
+
+// One token (batch-1 decode), K a multiple of 64, Y in fp32 or bf16: a matrix-vector product on
+// the vector ALUs instead of MFMA.  The MFMA decode kernels pad the token to 16 rows and the W
+// rows to 16-row groups and dequantize both operands in every workgroup (about 2.4 VALU
+// instructions per useful W value at the MLP down projection, 20 rows per CU); here a W value
+// costs half a converter instruction and half a dot2, and its block scale is applied once per 16
+// values:
+//   p_b  = sum over the block's 16 k of (E2M1(w_k) 2^8) t_k      (v_dot2_f32_f16, fp32)
+//   acc += p_b (E4M3(s_b) 2^-8)                                  (one fma per block)
+// with t_k = E2M1 E4M3 of the token, exact in fp16, dequantized once per workgroup into LDS.
+// Every product is exact in fp32 (11-bit significands).  The roundings -- at most two per dot2
+// inside a block's partial, one per block into the lane's sum, seven in the wave's reduction and
+// sixteen in the sum over the workgroup's wavefronts -- keep the error well inside 1e-4 sum |a w|.
+//
+// Workgroup b owns W rows [b R, b R + R), cut into items of 1 KB of codes (2048 values of a row,
+// the last item of a row shorter) and their 128 scale bytes; the R x (items per row) items are
+// shared out as 16 contiguous, equal ranges, one per wavefront, so every wavefront does the same
+// work whatever R is (a range may start and end inside a row).  Lane l multiplies the 16 bytes
+// at 16 l (32 values, two blocks) with scale bytes 2 l and 2 l + 1.  Items are copied straight
+// into a ring of kGvDepth slots private to the wavefront (one 1 KB copy for the codes, one 256 B
+// copy for the scales, lanes 32-63 repeating lanes 0-31), waited for with exact counts so that
+// kGvDepth - 1 items stay in flight across rows, and read from LDS one item ahead of the
+// products; copies past the range re-read its last item, unused.  The token's bytes are copied
+// into LDS the same way, before the ring's first copies, so those stay in flight while the token
+// is dequantized.  With 16 wavefronts per CU the latency of one wavefront's LDS reads and
+// dependent dot2 chain hides behind the others.  The token values sit in LDS zero-padded to whole
+// items (codes past a row's end multiply zeros) and swizzled so that the lanes' 64-byte reads of
+// a 32-value group fall in distinct banks.  A wavefront's sum over its part of a row is reduced
+// across its lanes in a fixed order and left in LDS in that row's slot for the wavefront (slots
+// of wavefronts that do not touch the row stay zero); the workgroup adds each row's 16 slots in
+// order and stores the result.
+constexpr int kGvThreads = 1024;
+constexpr int kGvWaves = kGvThreads / 64;
+constexpr int kGvDepth = 3;
+constexpr int kGvSlot = 1024 + 256;                       // codes, then scale bytes (x2)
+constexpr int kGvMaxLds = 160 * 1024;
+
+// Sum of v over the wavefront's 64 lanes in a fixed order, without LDS: within each row of 16
+// lanes, four DPP exchanges (neighbour in the pair, pair in the quad, quad in the half-row via
+// the half-row mirror, half in the row via the row mirror) leave every lane of the row holding
+// the same row sum; the four row sums are then read out and added pairwise.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));  // row_half_mirror
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, true));  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// Byte offset in the token's LDS values of piece j (8 values, 16 B) of 32-value group s.
+__device__ __forceinline__ uint32_t gv_tok_off(uint32_t s, int j) { return s * 64u + 16u * (j ^ ((s >> 1) & 3u)); }
+
+// LDS layout: the token's values (whole items), the token's raw codes (whole 1 KB copies) and
+// scale bytes (whole 256 B copies), the rings, the row slots.
+struct GvLayout {
+  int64_t raw_codes, raw_scales, rings, slots, bytes;
+  __host__ __device__ GvLayout(int64_t K, int64_t rows) {
+    const int64_t items = (K + 2047) / 2048;
+    raw_codes = items * 4096;
+    raw_scales = raw_codes + (K / 2 + 1023) / 1024 * 1024;
+    rings = raw_scales + (K / 16 + 255) / 256 * 256;
+    slots = rings + (int64_t)kGvWaves * kGvDepth * kGvSlot;
+    bytes = slots + rows * kGvWaves * 4;
+  }
+};
+
+__global__ __launch_bounds__(kGvThreads) void gemm_gemv_kernel(GemmArgs g, int rows_per_wg) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const uint32_t groups = (uint32_t)g.K / 32, kb = (uint32_t)g.K / 2, ks = (uint32_t)g.K / 16;
+  const int nch = (int)((groups + 63) / 64);            // items per row
+  const int r0 = blockIdx.x * rows_per_wg;
+  const int rows = min(r0 + rows_per_wg, g.N) - r0;
+  const GvLayout lay(g.K, rows);
+  uint8_t* ring = lds + lay.rings + wave * (kGvDepth * kGvSlot);
+  float* slots = reinterpret_cast<float*>(lds + lay.slots);   // [row][wave]
+
+  const int total = rows * nch;                         // item j = item j % nch of row j / nch
+  const int it0 = wave * total / kGvWaves, it1 = (wave + 1) * total / kGvWaves;
+  const int items = it1 - it0;
+
+  // The token's bytes into LDS: copy q (codes 1 KB at a time, then scale bytes 256 B at a time,
+  // lanes past the end re-reading the last piece into the padding) is wavefront q % 16's.
+  const int ncode = (int)((kb + 1023) / 1024), nscale = (int)((ks + 255) / 256);
+  for (int q = wave; q < ncode + nscale; q += kGvWaves) {
+    if (q < ncode)
+      copy16_to_lds(g.a_codes, min(1024u * q + 16u * lane, kb - 16u), lds + lay.raw_codes + 1024 * q);
+    else
+      copy4_to_lds(g.a_scales, min(256u * (q - ncode) + 4u * lane, ks - 4u), lds + lay.raw_scales + 256 * (q - ncode));
+  }
+
+  // Ring copies: the wavefront's items in order into slot t % kGvDepth; past it1 - 1 the last
+  // item again.
+  int cr = it0 / nch, cc = it0 - (it0 / nch) * nch, t_copy = 0, j_copy = it0;
+  auto copy_next = [&]() {
+    const size_t row = (size_t)(r0 + cr);
+    uint8_t* slot = ring + (t_copy % kGvDepth) * kGvSlot;
+    const uint32_t piece = min(64u * (uint32_t)cc + (uint32_t)lane, groups - 1);      // 16 B of codes
+    copy16_to_lds(g.w_codes + row * kb, 16u * piece, slot);
+    const uint32_t sbyte = min(128u * (uint32_t)cc + 4u * (uint32_t)(lane & 31), ks - 4u);   // 4 scale bytes
+    copy4_to_lds(g.w_scales + row * ks, sbyte, slot + 1024);
+    ++t_copy;
+    if (j_copy + 1 < it1) {
+      ++j_copy;
+      if (++cc == nch) {
+        cc = 0;
+        ++cr;
+      }
+    }
+  };
+  if (items > 0)
+    for (int d = 0; d < kGvDepth; ++d) copy_next();
+
+  // The row slots start at zero.
+  for (int t = threadIdx.x; t < rows * kGvWaves; t += kGvThreads) slots[t] = 0.0f;
+  // This wavefront's token copy is older than its 2 kGvDepth ring copies (none if it has no
+  // items: then the wait is for all of them, the token copy included).
+  if (items > 0)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kGvDepth));
+  else
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  asm volatile("" ::: "memory");
+  __syncthreads();
+  // The token's values, E2M1 * E4M3 in fp16 (exact), zeros past K.
+  for (uint32_t s = threadIdx.x; s < (uint32_t)nch * 64; s += kGvThreads) {
+    half8_t v[4] = {half8_t{}, half8_t{}, half8_t{}, half8_t{}};
+    if (s < groups) {
+      const uint4 c = *reinterpret_cast<const uint4*>(lds + lay.raw_codes + 16 * s);
+      const uint32_t sc = *reinterpret_cast<const uint16_t*>(lds + lay.raw_scales + 2 * s);
+      const half2_t p0 = scale_pair_f16(sc & 0xFFu), p1 = scale_pair_f16(sc >> 8);
+      v[0] = dequant8_f16(c.x, p0);
+      v[1] = dequant8_f16(c.y, p0);
+      v[2] = dequant8_f16(c.z, p1);
+      v[3] = dequant8_f16(c.w, p1);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<half8_t*>(lds + gv_tok_off(s, j)) = v[j];
+  }
+  // The W pointers' scalar loads must not stay pending into the loop, where their first use
+  // would wait for every LDS read as well: the empty statement takes them in scalar registers
+  // here, and the wait (LDS and scalar loads only) completes them.
+  asm volatile("" : : "s"(g.w_codes), "s"(g.w_scales));
+  __builtin_amdgcn_s_waitcnt(0xC07F);                   // lgkmcnt(0)
+  __syncthreads();
+
+  // Item i is read from LDS one item ahead: its codes, scale bytes and token values are in
+  // registers while item i - 1 is multiplied, so the LDS latency hides behind that work.
+  struct Operands {
+    uint4 wq;
+    uint32_t sc;
+    half8_t t[4];
+  };
+  auto read_item = [&](int i, int c, Operands& o) {
+    const uint8_t* slot = ring + (i % kGvDepth) * kGvSlot;
+    o.wq = *reinterpret_cast<const uint4*>(slot + 16 * lane);
+    o.sc = *reinterpret_cast<const uint16_t*>(slot + 1024 + 2 * lane);
+    const uint32_t st = (uint32_t)(64 * c + lane);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o.t[q] = *reinterpret_cast<const half8_t*>(lds + gv_tok_off(st, q));
+  };
+  float acc = 0.0f;
+  int jr = it0 / nch, jc = it0 - (it0 / nch) * nch;
+  Operands cur;
+  // Item 0's two copies are older than the 2 (kGvDepth - 1) of the items after it.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (kGvDepth - 1)));
+  asm volatile("" ::: "memory");
+  read_item(0, jc, cur);
+  for (int i = 0; i < items; ++i) {
+    // Item i + 1 (past the last one: a slot of unused copies, read and dropped).
+    const int cn = jc + 1 == nch ? 0 : jc + 1;
+    Operands nxt;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (kGvDepth - 2)));
+    asm volatile("" ::: "memory");
+    read_item(i + 1, cn, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float p = 0.0f;
+#pragma unroll
+      for (int q = 2 * b; q < 2 * b + 2; ++q) {
+        const uint32_t wd = q == 0 ? cur.wq.x : q == 1 ? cur.wq.y : q == 2 ? cur.wq.z : cur.wq.w;
+        const half2_t h[4] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 256.0f, 0),
+                              __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 256.0f, 1),
+                              __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 256.0f, 2),
+                              __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 256.0f, 3)};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) p = __builtin_amdgcn_fdot2(h[k], half2_t{cur.t[q][2 * k], cur.t[q][2 * k + 1]}, p, false);
+      }
+      acc = __builtin_fmaf(p, (float)scale_pair_f16((cur.sc >> (8 * b)) & 0xFFu)[0], acc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    copy_next();                                         // item i's slot, for item i + kGvDepth
+    if (jc + 1 == nch || i + 1 == items) {               // end of this wavefront's part of row jr
+      const float v = wave_sum_dpp(acc);
+      if (lane == 0) slots[jr * kGvWaves + wave] = v;
+      acc = 0.0f;
+    }
+    if (++jc == nch) {
+      jc = 0;
+      ++jr;
+    }
+    cur = nxt;
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));             // copies past the last item
+  asm volatile("" ::: "memory");
+  __syncthreads();
+  for (int t = threadIdx.x; t < rows; t += kGvThreads) {
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kGvWaves; ++w) v += slots[t * kGvWaves + w];
+    store_out(g, 0, r0 + t, (v * g.a_global[0]) * w_global_at(g, r0 + t));
+  }
+}
+
 // ------------------------------------------------------------------ plain kernel
 
 __device__ __forceinline__ float e2m1_value(uint32_t c) {
@@ -1951,6 +2170,9 @@ int gemm_device_setup() {
   for (const void* k : decode)
     if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kDlLds) != hipSuccess)
       return NVFP4_ERR_HIP;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_gemv_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kGvMaxLds) != hipSuccess)
+    return NVFP4_ERR_HIP;
   int st = set_decode_rows_lds<1>();
   if (st == NVFP4_OK) st = set_decode_rows_lds<2>();
   if (st == NVFP4_OK) st = set_decode_rows_lds<3>();
@@ -1990,7 +2212,19 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
   g.gate_beta = gates ? gates->beta : nullptr;
   g.swiglu = swiglu;
   const bool gated = gates != nullptr;
-  if (plain) {
+  int cus_gv = 0;
+  if (M == 1 && K % 64 == 0 && !qout && !swiglu && !gated) {
+    DeviceInfo dev;
+    const int st = device_info(stream, dev);
+    if (st != NVFP4_OK) return st;
+    cus_gv = dev.cus;
+  }
+  const int64_t gv_rows = cus_gv ? (N + cus_gv - 1) / cus_gv : 0;
+  if (cus_gv && GvLayout(K, gv_rows).bytes <= kGvMaxLds) {
+    // Batch-1 decode: one workgroup of about N / CUs rows per CU.
+    const unsigned grid = (unsigned)((N + gv_rows - 1) / gv_rows);
+    gemm_gemv_kernel<<<grid, kGvThreads, (size_t)GvLayout(K, gv_rows).bytes, stream>>>(g, (int)gv_rows);
+  } else if (plain) {
     const int64_t total = M * N;
     gemm_plain_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(g);
   } else if (M <= 16 && K % 256 == 0) {

@@ -213,6 +213,52 @@ def test_decode_balanced_rows(M, N, K):
     assert_gemm_close(y, Y, T, f"decode {M}x{N}x{K}")
 
 
+# Batch-1 decode (M = 1, K a multiple of 64) runs the matrix-vector kernel: a workgroup of 16
+# wavefronts per CU, each W row cut into 2048-value items, the workgroup's items shared out in
+# 16 equal ranges.  Shapes: one group of 32 values (K = 64, one short item), K not a multiple of
+# 128, items per row of 1, 3 and 16 (the token's copies then outnumber the wavefronts), N = 1
+# and 7 (wavefronts with no items, rows cut over many wavefronts), ragged last workgroups, and a
+# row count whose LDS slots no longer fit (N = 400003 at K = 64: the MFMA decode kernel).
+@pytest.mark.parametrize("N,K", [(1, 64), (7, 320), (300, 4160), (600, 32768), (70001, 128), (5120, 6208),
+                                 (400003, 64)])
+def test_gemv_batch1(N, K):
+    g = np.random.default_rng(N + K)
+
+    def operand(R):
+        codes = g.integers(0, 256, (R, K // 2), dtype=np.uint8)
+        scales = g.integers(0x10, 0x40, (R, K // 16), dtype=np.uint8)
+        gs = g.uniform(0.5, 2.0, 1).astype(np.float32)
+        return ref.NVFP4(codes, scales, gs, R, K)
+
+    oa, ow = operand(1), operand(N)
+    Y, T = ref.gemm(oa, ow)
+    a, w = to_device(oa), to_device(ow)
+    for dt in (torch.float32, torch.bfloat16):
+        assert_gemm_close(nv().gemm(a, w, dt), Y, T, f"gemv 1x{N}x{K} {dt}")
+
+
+def test_gemv_batch1_segments_and_pitch():
+    # Fused segments with their own global scales, and an output row pitch past N.
+    K, widths = 1088, (40, 8, 1000)
+    xg = to_gpu(workloads.activation(37, 0, 1, K))
+    a = nv().quantize(xg, "per_row")
+    oa = ref.quantize(xg.float().cpu().numpy(), ref.PER_ROW)
+    gq, oq = [], []
+    for i, n in enumerate(widths):
+        wg = to_gpu(workloads.weight(37, 10 + i, n, K, sigma=0.02 * (i + 1)))
+        gq.append(nv().quantize(wg))
+        oq.append(ref.quantize(wg.float().cpu().numpy()))
+    y = nv().gemm_fused_segments(a, torch.cat([q.codes for q in gq]), torch.cat([q.scales for q in gq]), widths,
+                                 torch.cat([q.global_scale for q in gq]), torch.float32)
+    Y, T = ref.fused_segments(oa, oq)
+    assert_gemm_close(y, Y, T, "gemv fused")
+    big = torch.full((1, 2000), 7.0, dtype=torch.float32, device=DEV)
+    nv().gemm(a, gq[2], torch.float32, out=big[:, :1000])
+    Y2, T2 = ref.gemm(oa, oq[2])
+    assert_gemm_close(big[:, :1000], Y2, T2, "gemv pitch")
+    assert torch.all(big[:, 1000:] == 7.0)
+
+
 def test_decode_balanced_rows_segments():
     M, K, widths = 4, 2048, (4000, 48, 3000)
     xg = to_gpu(workloads.activation(36, 0, M, K))
