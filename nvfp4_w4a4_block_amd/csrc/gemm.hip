@@ -1820,14 +1820,14 @@ __global__ __launch_bounds__(kDwThreads) void gemm_mx_decode_rows_kernel(GemmArg
 // into LDS the same way, before the ring's first copies, so those stay in flight while the token
 // is dequantized.  With 16 wavefronts per CU the latency of one wavefront's LDS reads and
 // dependent dot2 chain hides behind the others.  The token values sit in LDS zero-padded to whole
-// items (codes past a row's end multiply zeros) and swizzled so that the lanes' 64-byte reads of
-// a 32-value group fall in distinct banks.  A wavefront's sum over its part of a row is reduced
+// items (codes past a row's end multiply zeros), laid out so that one item's reads of them are
+// four 1 KB runs of consecutive LDS from one per-lane base.  A wavefront's sum over its part of a row is reduced
 // across its lanes in a fixed order and left in LDS in that row's slot for the wavefront (slots
 // of wavefronts that do not touch the row stay zero); the workgroup adds each row's 16 slots in
 // order and stores the result.
 constexpr int kGvThreads = 1024;
 constexpr int kGvWaves = kGvThreads / 64;
-constexpr int kGvDepth = 3;
+constexpr int kGvDepth = 4;
 constexpr int kGvSlot = 1024 + 256;                       // codes, then scale bytes (x2)
 constexpr int kGvMaxLds = 160 * 1024;
 
@@ -1847,9 +1847,6 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
-// Byte offset in the token's LDS values of piece j (8 values, 16 B) of 32-value group s.
-__device__ __forceinline__ uint32_t gv_tok_off(uint32_t s, int j) { return s * 64u + 16u * (j ^ ((s >> 1) & 3u)); }
-
 // LDS layout: the token's values (whole items), the token's raw codes (whole 1 KB copies) and
 // scale bytes (whole 256 B copies), the rings, the row slots.
 struct GvLayout {
@@ -1865,6 +1862,8 @@ struct GvLayout {
 };
 
 __global__ __launch_bounds__(kGvThreads) void gemm_gemv_kernel(GemmArgs g, int rows_per_wg) {
+  constexpr int D = kGvDepth;
+  static_assert(D % 2 == 0, "the unrolled steps alternate two operand sets");
   extern __shared__ __align__(16) uint8_t lds[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const uint32_t groups = (uint32_t)g.K / 32, kb = (uint32_t)g.K / 2, ks = (uint32_t)g.K / 16;
@@ -1872,7 +1871,7 @@ __global__ __launch_bounds__(kGvThreads) void gemm_gemv_kernel(GemmArgs g, int r
   const int r0 = blockIdx.x * rows_per_wg;
   const int rows = min(r0 + rows_per_wg, g.N) - r0;
   const GvLayout lay(g.K, rows);
-  uint8_t* ring = lds + lay.rings + wave * (kGvDepth * kGvSlot);
+  uint8_t* ring = lds + lay.rings + wave * (D * kGvSlot);
   float* slots = reinterpret_cast<float*>(lds + lay.slots);   // [row][wave]
 
   const int total = rows * nch;                         // item j = item j % nch of row j / nch
@@ -1889,39 +1888,43 @@ __global__ __launch_bounds__(kGvThreads) void gemm_gemv_kernel(GemmArgs g, int r
       copy4_to_lds(g.a_scales, min(256u * (q - ncode) + 4u * lane, ks - 4u), lds + lay.raw_scales + 256 * (q - ncode));
   }
 
-  // Ring copies: the wavefront's items in order into slot t % kGvDepth; past it1 - 1 the last
-  // item again.
-  int cr = it0 / nch, cc = it0 - (it0 / nch) * nch, t_copy = 0, j_copy = it0;
-  auto copy_next = [&]() {
-    const size_t row = (size_t)(r0 + cr);
-    uint8_t* slot = ring + (t_copy % kGvDepth) * kGvSlot;
-    const uint32_t piece = min(64u * (uint32_t)cc + (uint32_t)lane, groups - 1);      // 16 B of codes
-    copy16_to_lds(g.w_codes + row * kb, 16u * piece, slot);
-    const uint32_t sbyte = min(128u * (uint32_t)cc + 4u * (uint32_t)(lane & 31), ks - 4u);   // 4 scale bytes
-    copy4_to_lds(g.w_scales + row * ks, sbyte, slot + 1024);
-    ++t_copy;
+  // Ring copies: the wavefront's items in order, item t into slot t % D; past it1 - 1 the last
+  // item again.  The copy position advances through W's rows by pointer (rows are contiguous).
+  const int r_first = it0 / nch;
+  int cc = it0 - r_first * nch, j_copy = it0;
+  const uint8_t* cp_codes = g.w_codes + (size_t)(r0 + r_first) * kb;
+  const uint8_t* cp_scales = g.w_scales + (size_t)(r0 + r_first) * ks;
+  const uint32_t lane16 = 16u * (uint32_t)lane, lane4 = 4u * (uint32_t)(lane & 31);
+  auto copy_next = [&](int u) {
+    copy16_to_lds(cp_codes, min(lane16 + 1024u * (uint32_t)cc, kb - 16u), ring + u * kGvSlot);
+    copy4_to_lds(cp_scales, min(lane4 + 128u * (uint32_t)cc, ks - 4u), ring + u * kGvSlot + 1024);
     if (j_copy + 1 < it1) {
       ++j_copy;
       if (++cc == nch) {
         cc = 0;
-        ++cr;
+        cp_codes += kb;
+        cp_scales += ks;
       }
     }
   };
-  if (items > 0)
-    for (int d = 0; d < kGvDepth; ++d) copy_next();
+  if (items > 0) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) copy_next(u);
+  }
 
   // The row slots start at zero.
   for (int t = threadIdx.x; t < rows * kGvWaves; t += kGvThreads) slots[t] = 0.0f;
-  // This wavefront's token copy is older than its 2 kGvDepth ring copies (none if it has no
-  // items: then the wait is for all of them, the token copy included).
+  // This wavefront's token copies are older than its 2 D ring copies (none if it has no items:
+  // then the wait is for all of them).
   if (items > 0)
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kGvDepth));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * D));
   else
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   asm volatile("" ::: "memory");
   __syncthreads();
-  // The token's values, E2M1 * E4M3 in fp16 (exact), zeros past K.
+  // The token's values, E2M1 * E4M3 in fp16 (exact), zeros past K.  32-value group s = 64 c + l
+  // sits as four 16 B pieces at c 4096 + q 1024 + 16 l (q = 0..3), so that a wavefront reading
+  // piece q of groups 64 c .. 64 c + 63 reads 1 KB of consecutive LDS.
   for (uint32_t s = threadIdx.x; s < (uint32_t)nch * 64; s += kGvThreads) {
     half8_t v[4] = {half8_t{}, half8_t{}, half8_t{}, half8_t{}};
     if (s < groups) {
@@ -1933,8 +1936,9 @@ __global__ __launch_bounds__(kGvThreads) void gemm_gemv_kernel(GemmArgs g, int r
       v[2] = dequant8_f16(c.z, p1);
       v[3] = dequant8_f16(c.w, p1);
     }
+    uint8_t* dst = lds + (s >> 6) * 4096 + 16 * (s & 63);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<half8_t*>(lds + gv_tok_off(s, j)) = v[j];
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<half8_t*>(dst + 1024 * q) = v[q];
   }
   // The W pointers' scalar loads must not stay pending into the loop, where their first use
   // would wait for every LDS read as well: the empty statement takes them in scalar registers
@@ -1944,62 +1948,68 @@ __global__ __launch_bounds__(kGvThreads) void gemm_gemv_kernel(GemmArgs g, int r
   __syncthreads();
 
   // Item i is read from LDS one item ahead: its codes, scale bytes and token values are in
-  // registers while item i - 1 is multiplied, so the LDS latency hides behind that work.
+  // registers while item i - 1 is multiplied, so the LDS latency hides behind that work.  The
+  // loop is unrolled D times, so ring slots are fixed offsets and the two operand sets
+  // alternate without copies.
   struct Operands {
     uint4 wq;
     uint32_t sc;
     half8_t t[4];
   };
-  auto read_item = [&](int i, int c, Operands& o) {
-    const uint8_t* slot = ring + (i % kGvDepth) * kGvSlot;
-    o.wq = *reinterpret_cast<const uint4*>(slot + 16 * lane);
+  auto read_item = [&](int u, int c, Operands& o) {
+    const uint8_t* slot = ring + u * kGvSlot;
+    o.wq = *reinterpret_cast<const uint4*>(slot + lane16);
     o.sc = *reinterpret_cast<const uint16_t*>(slot + 1024 + 2 * lane);
-    const uint32_t st = (uint32_t)(64 * c + lane);
+    const uint8_t* tok = lds + c * 4096 + lane16;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) o.t[q] = *reinterpret_cast<const half8_t*>(lds + gv_tok_off(st, q));
+    for (int q = 0; q < 4; ++q) o.t[q] = *reinterpret_cast<const half8_t*>(tok + 1024 * q);
   };
   float acc = 0.0f;
-  int jr = it0 / nch, jc = it0 - (it0 / nch) * nch;
-  Operands cur;
-  // Item 0's two copies are older than the 2 (kGvDepth - 1) of the items after it.
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (kGvDepth - 1)));
+  int jr = r_first, jc = it0 - r_first * nch;
+  Operands op[2];
+  // Item 0's two copies are older than the 2 (D - 1) of the items after it.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (D - 1)));
   asm volatile("" ::: "memory");
-  read_item(0, jc, cur);
-  for (int i = 0; i < items; ++i) {
-    // Item i + 1 (past the last one: a slot of unused copies, read and dropped).
-    const int cn = jc + 1 == nch ? 0 : jc + 1;
-    Operands nxt;
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (kGvDepth - 2)));
-    asm volatile("" ::: "memory");
-    read_item(i + 1, cn, nxt);
-    __builtin_amdgcn_sched_barrier(0);
+  read_item(0, jc, op[0]);
+  for (int i0 = 0; i0 < items; i0 += D) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      float p = 0.0f;
+    for (int u = 0; u < D; ++u) {
+      if (i0 + u < items) {
+        Operands& cur = op[u & 1];
+        // Item i + 1 (past the last one: a slot of unused copies, read and dropped).
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (D - 2)));
+        asm volatile("" ::: "memory");
+        read_item((u + 1) % D, jc + 1 == nch ? 0 : jc + 1, op[(u + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int q = 2 * b; q < 2 * b + 2; ++q) {
-        const uint32_t wd = q == 0 ? cur.wq.x : q == 1 ? cur.wq.y : q == 2 ? cur.wq.z : cur.wq.w;
-        const half2_t h[4] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 256.0f, 0),
-                              __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 256.0f, 1),
-                              __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 256.0f, 2),
-                              __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 256.0f, 3)};
+        for (int b = 0; b < 2; ++b) {
+          float p = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) p = __builtin_amdgcn_fdot2(h[k], half2_t{cur.t[q][2 * k], cur.t[q][2 * k + 1]}, p, false);
+          for (int q = 2 * b; q < 2 * b + 2; ++q) {
+            const uint32_t wd = q == 0 ? cur.wq.x : q == 1 ? cur.wq.y : q == 2 ? cur.wq.z : cur.wq.w;
+            const half2_t h[4] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 256.0f, 0),
+                                  __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 256.0f, 1),
+                                  __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 256.0f, 2),
+                                  __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 256.0f, 3)};
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              p = __builtin_amdgcn_fdot2(h[k], half2_t{cur.t[q][2 * k], cur.t[q][2 * k + 1]}, p, false);
+          }
+          acc = __builtin_fmaf(p, (float)scale_pair_f16((cur.sc >> (8 * b)) & 0xFFu)[0], acc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        copy_next(u);                                    // item i's slot, for item i + D
+        if (jc + 1 == nch || i0 + u + 1 == items) {      // end of this wavefront's part of row jr
+          const float v = wave_sum_dpp(acc);
+          if (lane == 0) slots[jr * kGvWaves + wave] = v;
+          acc = 0.0f;
+        }
+        if (++jc == nch) {
+          jc = 0;
+          ++jr;
+        }
       }
-      acc = __builtin_fmaf(p, (float)scale_pair_f16((cur.sc >> (8 * b)) & 0xFFu)[0], acc);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    copy_next();                                         // item i's slot, for item i + kGvDepth
-    if (jc + 1 == nch || i + 1 == items) {               // end of this wavefront's part of row jr
-      const float v = wave_sum_dpp(acc);
-      if (lane == 0) slots[jr * kGvWaves + wave] = v;
-      acc = 0.0f;
-    }
-    if (++jc == nch) {
-      jc = 0;
-      ++jr;
-    }
-    cur = nxt;
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));             // copies past the last item
   asm volatile("" ::: "memory");
@@ -2219,6 +2229,9 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
     if (st != NVFP4_OK) return st;
     cus_gv = dev.cus;
   }
+  // Past one round of 32-row workgroups with whole 256-wide stages the balanced MFMA kernel
+  // streams W faster than this one; below it the matrix-vector kernel beats the K-split kernel.
+  if (cus_gv && N > (int64_t)kDecodeRows * cus_gv && K % 256 == 0) cus_gv = 0;
   const int64_t gv_rows = cus_gv ? (N + cus_gv - 1) / cus_gv : 0;
   if (cus_gv && GvLayout(K, gv_rows).bytes <= kGvMaxLds) {
     // Batch-1 decode: one workgroup of about N / CUs rows per CU.

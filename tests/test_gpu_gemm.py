@@ -213,9 +213,9 @@ def test_decode_balanced_rows(M, N, K):
     assert_gemm_close(y, Y, T, f"decode {M}x{N}x{K}")
 
 
-# Batch-1 decode (M = 1, K a multiple of 64) runs the matrix-vector kernel: a workgroup of 16
-# wavefronts per CU, each W row cut into 2048-value items, the workgroup's items shared out in
-# 16 equal ranges.  Shapes: one group of 32 values (K = 64, one short item), K not a multiple of
+# Batch-1 decode (M = 1, K a multiple of 64, N up to one round of 32-row workgroups or K not a
+# multiple of 256) runs the matrix-vector kernel: a workgroup of 16 wavefronts per CU, each W row
+# cut into 2048-value items, the workgroup's items shared out in 16 equal ranges.  Shapes: one group of 32 values (K = 64, one short item), K not a multiple of
 # 128, items per row of 1, 3 and 16 (the token's copies then outnumber the wavefronts), N = 1
 # and 7 (wavefronts with no items, rows cut over many wavefronts), ragged last workgroups, and a
 # row count whose LDS slots no longer fit (N = 400003 at K = 64: the MFMA decode kernel).
