@@ -497,6 +497,15 @@ def _bench_decode_shape(nv, d, steps: int, warmup: int, settle_s: float, rotate:
                          "gemm_gbs": round(gb / (g_ms * 1e-3) / 1e9, 1),
                          "gemm_frac_hbm": round(gb / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "quant_gbs": round(_bytes_quantize(M, d.K) / (q_ms * 1e-3) / 1e9, 1)}
+        if M == 1:
+            # The same step as one call: the token quantized inside the GEMM launch.
+            def fused(i):
+                nv.decode_linear(x, ws[i % rotate], out=y, a_out=a)
+
+            f_ms = _graph_us(fused, reps, max(4, steps // 5), settle_s) * 1e-3
+            fb = wbytes + _bytes_quantize(1, d.K) + ybytes
+            out["M=1"].update({"step_fused_us": round(f_ms * 1e3, 2),
+                               "step_fused_frac_hbm": round(fb / (f_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
     return out
 
 

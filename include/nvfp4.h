@@ -149,6 +149,34 @@ int nvfp4_gemm(int64_t M, int64_t N, int64_t K,
                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Batch-1 decode of one W4A4 linear layer in one call: the token's activation row is quantized
+ * to the 4-bit block format and multiplied with W, as every linear layer of the hybrid model
+ * runs at decode ("Why Gated DeltaNet Survives 4-Bit Quantization", "The deep dive": 4-bit
+ * weights and activations).  The result is that of
+ *   nvfp4_quantize(x, x_dtype, 1, K, K, a_codes, a_scales, a_global, mode, ...)
+ *   nvfp4_gemm(1, N, K, a_codes, a_scales, a_global, 0, w_codes, w_scales, w_global, y, y_dtype, N, ...)
+ * on the same stream: the token's NVFP4 bytes are written to a_codes / a_scales (and its global
+ * scale to a_global, except in NVFP4_SCALE_GIVEN mode, where a_global is read), bit for bit those
+ * of nvfp4_quantize, and Y[1, N] to y.  Y is bit for bit that of nvfp4_gemm except where the one
+ * launch below runs and nvfp4_gemm takes an MFMA kernel for the shape (bf16 input, K a multiple
+ * of 256, N above 32 x the CU count): there both are within nvfp4_gemm's rounding bound of the
+ * exact product, accumulated in a different order.
+ * With one row NVFP4_SCALE_PER_TENSOR and NVFP4_SCALE_PER_ROW are the same scale; neither needs a
+ * workspace here.  For bf16 input with K a multiple of 64 whose working set fits the kernel's
+ * 160 KB of LDS (the token twice, as bf16 and as fp16 values, plus the weight copy rings: K up to
+ * 18432 for N up to 32512 on 256 CUs) it is one launch that quantizes the token inside the GEMM
+ * kernel, with no separate quantize launch; other inputs run the two calls above internally.
+ *   N >= 0 (zero: only the quantization), K > 0 and a multiple of 16.
+ *   x             device [K] of x_dtype, 16-byte aligned.
+ *   a_codes       out [K/2], a_scales out [K/16], both 16-byte aligned; a_global device [1].
+ *   w_codes, w_scales, w_global, y_dtype as in nvfp4_gemm; y device [N] of y_dtype.
+ */
+int nvfp4_decode_linear(int64_t N, int64_t K, const void* x, int x_dtype, int mode,
+                        uint8_t* a_codes, uint8_t* a_scales, float* a_global,
+                        const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                        void* y, int y_dtype, void* stream);
+
+/*
  * The fused-module GEMM, the repair of the global-scale mismatch the paper abstract reports
  * (modules calibrated one by one, each with its own global scale, served by a kernel that fuses
  * them into one GEMM); "Quantizing All Layers Reveals Recurrent Memory Is Robust" ("Block

@@ -38,7 +38,7 @@ import torch
 
 __all__ = [
     "NVFP4Tensor", "NVFP4Error", "quantize", "gemm", "gemm_fused_segments", "gemm_nvfp4_out", "gemm_fused_gdn_gates", "MXFP4Tensor", "to_mxfp4", "mxfp4_gemm",
-    "fp8_kv_quantize", "fp8_kv_dequantize", "interleave_gate_up", "gemm_swiglu",
+    "fp8_kv_quantize", "fp8_kv_dequantize", "interleave_gate_up", "gemm_swiglu", "decode_linear",
     "library_path", "lib",
     "PER_TENSOR", "PER_ROW", "GIVEN", "MAX_SEGMENTS", "EXPORTED_SYMBOLS",
 ]
@@ -54,7 +54,8 @@ EXPORTED_SYMBOLS = (
     "nvfp4_quantize", "nvfp4_quantize_workspace_size", "nvfp4_quantize_no_alloc", "nvfp4_gemm", "nvfp4_gemm_fused_segments",
     "nvfp4_gemm_nvfp4_out", "nvfp4_gemm_fused_gdn_gates", "nvfp4_to_mxfp4", "nvfp4_mxfp4_gemm",
     "nvfp4_gemm_workspace_size", "nvfp4_fp8_kv_quantize", "nvfp4_fp8_kv_dequantize",
-    "nvfp4_interleave_gate_up", "nvfp4_gemm_swiglu", "nvfp4_status_string", "nvfp4_version",
+    "nvfp4_interleave_gate_up", "nvfp4_gemm_swiglu", "nvfp4_decode_linear", "nvfp4_status_string",
+    "nvfp4_version",
 )
 
 
@@ -75,6 +76,8 @@ def _load() -> ctypes.CDLL:
     L.nvfp4_quantize_workspace_size.restype = sz
     L.nvfp4_gemm.argtypes = [i64, i64, i64, p, p, p, i32, p, p, p, p, i32, i64, p, sz, p]
     L.nvfp4_gemm.restype = i32
+    L.nvfp4_decode_linear.argtypes = [i64, i64, p, i32, i32, p, p, p, p, p, p, p, i32, p]
+    L.nvfp4_decode_linear.restype = i32
     L.nvfp4_gemm_fused_segments.argtypes = [i64, i64, p, p, p, i32, i32, p, p, p, p, p, i32, i64, p, sz, p]
     L.nvfp4_gemm_fused_segments.restype = i32
     L.nvfp4_gemm_nvfp4_out.argtypes = [i64, i64, p, p, p, i32, i32, p, p, p, p, p, p, p, p]
@@ -275,6 +278,47 @@ def gemm(a: NVFP4Tensor, w: NVFP4Tensor, out_dtype: torch.dtype = torch.bfloat16
                         y.stride(0) if M > 0 else N, _ptr(ws), ws_bytes, _stream(dev))
     _check(st, "nvfp4_gemm")
     return y
+
+
+def decode_linear(x: torch.Tensor, w: NVFP4Tensor, mode: str = "per_tensor",
+                  global_scale: torch.Tensor | None = None, out_dtype: torch.dtype = torch.bfloat16,
+                  out: torch.Tensor | None = None, a_out: NVFP4Tensor | None = None):
+    """Batch-1 decode of one linear layer: quantize the token x [1, K] (bf16 or fp32) and
+    multiply with W [N, K] in one call.  Returns (y [1, N], the token as NVFP4); the same bits as
+    ``quantize(x, mode, global_scale)`` followed by ``gemm``.  mode: "per_tensor" or "per_row"
+    (the same scale for one row) or "given" (``global_scale``: one fp32 element)."""
+    _require(isinstance(x, torch.Tensor) and x.dim() == 2 and x.shape[0] == 1, "x must be [1, K]")
+    _require(x.dtype in (torch.bfloat16, torch.float32), "x must be bf16 or fp32")
+    _require(x.is_contiguous(), "x must be contiguous")
+    _require(mode in _MODES, f"mode must be one of {sorted(_MODES)}")
+    _require_operand(w, "w")
+    K, N, dev = x.shape[1], w.rows, x.device
+    _require(w.cols == K, "K mismatch")
+    _require(w.codes.device == dev, "x and w must be on one device")
+    _require_f32(w.global_scale, 1, "w.global_scale (one per tensor)", dev)
+    m = _MODES[mode]
+    if a_out is None:
+        if m == GIVEN:
+            _require(global_scale is not None, "given mode needs global_scale")
+            g = global_scale
+        else:
+            g = torch.empty((1,), dtype=torch.float32, device=dev)
+        a_out = NVFP4Tensor(torch.empty((1, K // 2), dtype=torch.uint8, device=dev),
+                            torch.empty((1, K // 16), dtype=torch.uint8, device=dev), g)
+    elif m == GIVEN and global_scale is not None:
+        a_out.global_scale = global_scale
+    _require_bytes(a_out.codes, (1, K // 2), "a_out.codes", dev)
+    _require_bytes(a_out.scales, (1, K // 16), "a_out.scales", dev)
+    _require_f32(a_out.global_scale, 1, "a_out.global_scale", dev)
+    y = _out_tensor(1, N, out_dtype, dev, out)
+    _require(y.is_contiguous(), "out must be contiguous")
+    _on_gpu(dev)
+    st = lib.nvfp4_decode_linear(N, K, _ptr(x), _BF16 if x.dtype == torch.bfloat16 else _F32, m,
+                                 _ptr(a_out.codes), _ptr(a_out.scales), _ptr(a_out.global_scale),
+                                 _ptr(w.codes), _ptr(w.scales), _ptr(w.global_scale), _ptr(y),
+                                 _y_dtype(out_dtype), _stream(dev))
+    _check(st, "nvfp4_decode_linear")
+    return y, a_out
 
 
 def gemm_fused_segments(a: NVFP4Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,

@@ -130,6 +130,35 @@ int nvfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const ui
                      y, y_dtype, ldy, workspace, static_cast<hipStream_t>(stream));
 }
 
+int nvfp4_decode_linear(int64_t N, int64_t K, const void* x, int x_dtype, int mode, uint8_t* a_codes,
+                        uint8_t* a_scales, float* a_global, const uint8_t* w_codes, const uint8_t* w_scales,
+                        const float* w_global, void* y, int y_dtype, void* stream) {
+  int st = check_quantize(x, x_dtype, 1, K, K, a_codes, a_scales, a_global, mode);
+  if (st != NVFP4_OK) return st;
+  if (N < 0 || !aligned(a_codes, 16) || !aligned(a_scales, 16)) return NVFP4_ERR_INVALID_ARG;
+  if (N > 0) {
+    st = check_gemm_common(1, N, K, a_codes, a_scales, a_global, 0, w_codes, w_scales, y, y_dtype, N);
+    if (st != NVFP4_OK) return st;
+    if (!w_global || !aligned(w_global, 4)) return NVFP4_ERR_INVALID_ARG;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N > 0 && x_dtype == NVFP4_BF16) {
+    st = launch_decode_linear(N, K, static_cast<const uint16_t*>(x), mode == NVFP4_SCALE_GIVEN, a_codes, a_scales,
+                              a_global, w_codes, w_scales, w_global, y, y_dtype, s);
+    if (st != NVFP4_ERR_UNSUPPORTED) return st;
+  }
+  // One row: the per-row scale is the per-tensor scale, without the per-tensor mode's workspace.
+  st = launch_quantize(x, x_dtype, 1, K, K, a_codes, a_scales, a_global,
+                       mode == NVFP4_SCALE_GIVEN ? NVFP4_SCALE_GIVEN : NVFP4_SCALE_PER_ROW, nullptr, s);
+  if (st != NVFP4_OK || N == 0) return st;
+  SegmentTable seg{};
+  seg.count = 1;
+  seg.bound[0] = 0;
+  seg.bound[1] = (int32_t)N;
+  return launch_gemm(1, N, K, a_codes, a_scales, a_global, 0, w_codes, w_scales, w_global, seg, y, y_dtype, N,
+                     nullptr, s);
+}
+
 int nvfp4_gemm_fused_segments(int64_t M, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
                               const float* a_global, int a_global_per_row, int num_segments,
                               const int64_t* seg_n, const uint8_t* w_codes, const uint8_t* w_scales,

@@ -1847,21 +1847,37 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
-// LDS layout: the token's values (whole items), the token's raw codes (whole 1 KB copies) and
-// scale bytes (whole 256 B copies), the rings, the row slots.
+// LDS layout: the token's values (whole items); the token's raw bytes: its codes (whole 1 KB
+// copies) and scale bytes (whole 256 B copies), or with the quantization fused in its bf16 values
+// (whole 1 KB copies); the rings; the row slots; with the quantization fused, one word per
+// wavefront for the row maximum.
 struct GvLayout {
-  int64_t raw_codes, raw_scales, rings, slots, bytes;
-  __host__ __device__ GvLayout(int64_t K, int64_t rows) {
+  int64_t raw_codes, raw_scales, rings, slots, red, bytes;
+  __host__ __device__ GvLayout(int64_t K, int64_t rows, bool quant) {
     const int64_t items = (K + 2047) / 2048;
     raw_codes = items * 4096;
-    raw_scales = raw_codes + (K / 2 + 1023) / 1024 * 1024;
-    rings = raw_scales + (K / 16 + 255) / 256 * 256;
+    raw_scales = raw_codes + (quant ? (2 * K + 1023) / 1024 * 1024 : (K / 2 + 1023) / 1024 * 1024);
+    rings = raw_scales + (quant ? 0 : (K / 16 + 255) / 256 * 256);
     slots = rings + (int64_t)kGvWaves * kGvDepth * kGvSlot;
-    bytes = slots + rows * kGvWaves * 4;
+    red = slots + rows * kGvWaves * 4;
+    bytes = red + (quant ? kGvWaves * 4 : 0);
   }
 };
 
-__global__ __launch_bounds__(kGvThreads) void gemm_gemv_kernel(GemmArgs g, int rows_per_wg) {
+// The token as one bf16 row, quantized inside the kernel (every workgroup computes the same
+// bytes; workgroup 0 writes them out): codes [K/2], scale bytes [K/16] and the global scale, which
+// is read instead of computed when `given` is set.
+struct GvQuant {
+  const uint8_t* x;
+  uint8_t* codes;
+  uint8_t* scales;
+  float* global;
+  int32_t given;
+};
+constexpr int kGvQuantBlocks = 2;   // 16-value blocks per thread: K up to 2 * 1024 * 16
+
+template <bool Q>
+__global__ __launch_bounds__(kGvThreads) void gemm_gemv_kernel(GemmArgs g, int rows_per_wg, GvQuant q) {
   constexpr int D = kGvDepth;
   static_assert(D % 2 == 0, "the unrolled steps alternate two operand sets");
   extern __shared__ __align__(16) uint8_t lds[];
@@ -1870,7 +1886,7 @@ __global__ __launch_bounds__(kGvThreads) void gemm_gemv_kernel(GemmArgs g, int r
   const int nch = (int)((groups + 63) / 64);            // items per row
   const int r0 = blockIdx.x * rows_per_wg;
   const int rows = min(r0 + rows_per_wg, g.N) - r0;
-  const GvLayout lay(g.K, rows);
+  const GvLayout lay(g.K, rows, Q);
   uint8_t* ring = lds + lay.rings + wave * (D * kGvSlot);
   float* slots = reinterpret_cast<float*>(lds + lay.slots);   // [row][wave]
 
@@ -1878,14 +1894,21 @@ __global__ __launch_bounds__(kGvThreads) void gemm_gemv_kernel(GemmArgs g, int r
   const int it0 = wave * total / kGvWaves, it1 = (wave + 1) * total / kGvWaves;
   const int items = it1 - it0;
 
-  // The token's bytes into LDS: copy q (codes 1 KB at a time, then scale bytes 256 B at a time,
-  // lanes past the end re-reading the last piece into the padding) is wavefront q % 16's.
-  const int ncode = (int)((kb + 1023) / 1024), nscale = (int)((ks + 255) / 256);
-  for (int q = wave; q < ncode + nscale; q += kGvWaves) {
-    if (q < ncode)
-      copy16_to_lds(g.a_codes, min(1024u * q + 16u * lane, kb - 16u), lds + lay.raw_codes + 1024 * q);
-    else
-      copy4_to_lds(g.a_scales, min(256u * (q - ncode) + 4u * lane, ks - 4u), lds + lay.raw_scales + 256 * (q - ncode));
+  // The token's bytes into LDS: copy c (codes 1 KB at a time, then scale bytes 256 B at a time;
+  // with the quantization fused, bf16 values 1 KB at a time; lanes past the end re-reading the
+  // last piece into the padding) is wavefront c % 16's.
+  if constexpr (Q) {
+    const uint32_t xb = 2u * (uint32_t)g.K;
+    for (int c = wave; c < (int)((xb + 1023) / 1024); c += kGvWaves)
+      copy16_to_lds(q.x, min(1024u * c + 16u * lane, xb - 16u), lds + lay.raw_codes + 1024 * c);
+  } else {
+    const int ncode = (int)((kb + 1023) / 1024), nscale = (int)((ks + 255) / 256);
+    for (int c = wave; c < ncode + nscale; c += kGvWaves) {
+      if (c < ncode)
+        copy16_to_lds(g.a_codes, min(1024u * c + 16u * lane, kb - 16u), lds + lay.raw_codes + 1024 * c);
+      else
+        copy4_to_lds(g.a_scales, min(256u * (c - ncode) + 4u * lane, ks - 4u), lds + lay.raw_scales + 256 * (c - ncode));
+    }
   }
 
   // Ring copies: the wavefront's items in order, item t into slot t % D; past it1 - 1 the last
@@ -1925,20 +1948,83 @@ __global__ __launch_bounds__(kGvThreads) void gemm_gemv_kernel(GemmArgs g, int r
   // The token's values, E2M1 * E4M3 in fp16 (exact), zeros past K.  32-value group s = 64 c + l
   // sits as four 16 B pieces at c 4096 + q 1024 + 16 l (q = 0..3), so that a wavefront reading
   // piece q of groups 64 c .. 64 c + 63 reads 1 KB of consecutive LDS.
-  for (uint32_t s = threadIdx.x; s < (uint32_t)nch * 64; s += kGvThreads) {
-    half8_t v[4] = {half8_t{}, half8_t{}, half8_t{}, half8_t{}};
-    if (s < groups) {
-      const uint4 c = *reinterpret_cast<const uint4*>(lds + lay.raw_codes + 16 * s);
-      const uint32_t sc = *reinterpret_cast<const uint16_t*>(lds + lay.raw_scales + 2 * s);
-      const half2_t p0 = scale_pair_f16(sc & 0xFFu), p1 = scale_pair_f16(sc >> 8);
-      v[0] = dequant8_f16(c.x, p0);
-      v[1] = dequant8_f16(c.y, p0);
-      v[2] = dequant8_f16(c.z, p1);
-      v[3] = dequant8_f16(c.w, p1);
-    }
-    uint8_t* dst = lds + (s >> 6) * 4096 + 16 * (s & 63);
+  float a_g;                                            // the token's global scale
+  if constexpr (Q) {
+    // Quantize the bf16 row as the quantizer's per-row mode does: s_g = fl32(max |x| / 2688)
+    // from the integer max of the magnitude bits (NaN propagates), or the given scale, then
+    // encode_block per 16 values.  Block b = 16 values = pieces 2 (b & 1), 2 (b & 1) + 1 of
+    // group b >> 1.
+    const uint32_t bpr = (uint32_t)g.K / 16, bpad = (uint32_t)nch * 128;
+    float v[kGvQuantBlocks][16];
+    uint32_t m = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) *reinterpret_cast<half8_t*>(dst + 1024 * q) = v[q];
+    for (int j = 0; j < kGvQuantBlocks; ++j) {
+      const uint32_t b = threadIdx.x + j * kGvThreads;
+      if (b < bpr) {
+        const uint4 w0 = *reinterpret_cast<const uint4*>(lds + lay.raw_codes + 32 * b);
+        const uint4 w1 = *reinterpret_cast<const uint4*>(lds + lay.raw_codes + 32 * b + 16);
+        widen(w0, v[j], (const uint16_t*)nullptr);
+        widen(w1, v[j] + 8, (const uint16_t*)nullptr);
+        m = max(m, max(max_abs_bits(w0, (const uint16_t*)nullptr), max_abs_bits(w1, (const uint16_t*)nullptr)));
+      }
+    }
+    if (q.given) {
+      // A scalar load waited for in the same statement: a vector load here would be counted
+      // with the ring's copies, and waiting for it would drain them.
+      uint32_t bits;
+      asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(bits) : "s"(q.global) : "memory");
+      a_g = __uint_as_float(bits);
+    } else {
+      uint32_t* red = reinterpret_cast<uint32_t*>(lds + lay.red);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+      if (lane == 0) red[wave] = m;
+      __syncthreads();
+      m = red[0];
+#pragma unroll
+      for (int w = 1; w < kGvWaves; ++w) m = max(m, red[w]);
+      a_g = __uint_as_float(m) / kGlobalDivisor;
+      if (blockIdx.x == 0 && threadIdx.x == 0) q.global[0] = a_g;
+    }
+#pragma unroll
+    for (int j = 0; j < kGvQuantBlocks; ++j) {
+      const uint32_t b = threadIdx.x + j * kGvThreads;
+      if (b < bpad) {
+        half8_t lo8 = half8_t{}, hi8 = half8_t{};
+        if (b < bpr) {
+          uint32_t sb, lo, hi;
+          encode_block(v[j], a_g, sb, lo, hi);
+          if (blockIdx.x == 0) {
+            *reinterpret_cast<uint2*>(q.codes + 8 * (size_t)b) = make_uint2(lo, hi);
+            q.scales[b] = (uint8_t)sb;
+          }
+          const half2_t sp = scale_pair_f16(sb);
+          lo8 = dequant8_f16(lo, sp);
+          hi8 = dequant8_f16(hi, sp);
+        }
+        const uint32_t gs = b >> 1;
+        uint8_t* dst = lds + (gs >> 6) * 4096 + 2048 * (b & 1) + 16 * (gs & 63);
+        *reinterpret_cast<half8_t*>(dst) = lo8;
+        *reinterpret_cast<half8_t*>(dst + 1024) = hi8;
+      }
+    }
+  } else {
+    for (uint32_t s = threadIdx.x; s < (uint32_t)nch * 64; s += kGvThreads) {
+      half8_t v[4] = {half8_t{}, half8_t{}, half8_t{}, half8_t{}};
+      if (s < groups) {
+        const uint4 c = *reinterpret_cast<const uint4*>(lds + lay.raw_codes + 16 * s);
+        const uint32_t sc = *reinterpret_cast<const uint16_t*>(lds + lay.raw_scales + 2 * s);
+        const half2_t p0 = scale_pair_f16(sc & 0xFFu), p1 = scale_pair_f16(sc >> 8);
+        v[0] = dequant8_f16(c.x, p0);
+        v[1] = dequant8_f16(c.y, p0);
+        v[2] = dequant8_f16(c.z, p1);
+        v[3] = dequant8_f16(c.w, p1);
+      }
+      uint8_t* dst = lds + (s >> 6) * 4096 + 16 * (s & 63);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<half8_t*>(dst + 1024 * j) = v[j];
+    }
+    a_g = 0.0f;
   }
   // The W pointers' scalar loads must not stay pending into the loop, where their first use
   // would wait for every LDS read as well: the empty statement takes them in scalar registers
@@ -2018,7 +2104,7 @@ __global__ __launch_bounds__(kGvThreads) void gemm_gemv_kernel(GemmArgs g, int r
     float v = 0.0f;
 #pragma unroll
     for (int w = 0; w < kGvWaves; ++w) v += slots[t * kGvWaves + w];
-    store_out(g, 0, r0 + t, (v * g.a_global[0]) * w_global_at(g, r0 + t));
+    store_out(g, 0, r0 + t, (v * (Q ? a_g : g.a_global[0])) * w_global_at(g, r0 + t));
   }
 }
 
@@ -2180,8 +2266,10 @@ int gemm_device_setup() {
   for (const void* k : decode)
     if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kDlLds) != hipSuccess)
       return NVFP4_ERR_HIP;
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_gemv_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          kGvMaxLds) != hipSuccess)
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_gemv_kernel<false>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kGvMaxLds) != hipSuccess ||
+      hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_gemv_kernel<true>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kGvMaxLds) != hipSuccess)
     return NVFP4_ERR_HIP;
   int st = set_decode_rows_lds<1>();
   if (st == NVFP4_OK) st = set_decode_rows_lds<2>();
@@ -2196,6 +2284,28 @@ int gemm_device_setup() {
                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
     return NVFP4_ERR_HIP;
   return NVFP4_OK;
+}
+
+int launch_decode_linear(int64_t N, int64_t K, const uint16_t* x, bool given, uint8_t* a_codes, uint8_t* a_scales,
+                         float* a_global, const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                         void* y, int y_dtype, hipStream_t stream) {
+  if (N == 0) return NVFP4_OK;
+  if (K % 64 != 0 || (K + 2047) / 2048 * 128 > (int64_t)kGvQuantBlocks * kGvThreads) return NVFP4_ERR_UNSUPPORTED;
+  DeviceInfo dev;
+  const int st = device_info(stream, dev);
+  if (st != NVFP4_OK) return st;
+  const int64_t rows = (N + dev.cus - 1) / dev.cus;
+  const GvLayout lay(K, rows, true);
+  if (lay.bytes > kGvMaxLds) return NVFP4_ERR_UNSUPPORTED;
+  SegmentTable seg{};
+  seg.count = 1;
+  seg.bound[0] = 0;
+  seg.bound[1] = (int32_t)N;
+  const GemmArgs g = gemm_args(1, N, K, a_codes, a_scales, a_global, 0, w_codes, w_scales, w_global, seg, y,
+                               y_dtype, N);
+  const GvQuant q{reinterpret_cast<const uint8_t*>(x), a_codes, a_scales, a_global, given ? 1 : 0};
+  gemm_gemv_kernel<true><<<(unsigned)((N + rows - 1) / rows), kGvThreads, (size_t)lay.bytes, stream>>>(g, (int)rows, q);
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
 int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
@@ -2233,10 +2343,11 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
   // streams W faster than this one; below it the matrix-vector kernel beats the K-split kernel.
   if (cus_gv && N > (int64_t)kDecodeRows * cus_gv && K % 256 == 0) cus_gv = 0;
   const int64_t gv_rows = cus_gv ? (N + cus_gv - 1) / cus_gv : 0;
-  if (cus_gv && GvLayout(K, gv_rows).bytes <= kGvMaxLds) {
+  if (cus_gv && GvLayout(K, gv_rows, false).bytes <= kGvMaxLds) {
     // Batch-1 decode: one workgroup of about N / CUs rows per CU.
     const unsigned grid = (unsigned)((N + gv_rows - 1) / gv_rows);
-    gemm_gemv_kernel<<<grid, kGvThreads, (size_t)GvLayout(K, gv_rows).bytes, stream>>>(g, (int)gv_rows);
+    gemm_gemv_kernel<false><<<grid, kGvThreads, (size_t)GvLayout(K, gv_rows, false).bytes, stream>>>(
+        g, (int)gv_rows, GvQuant{});
   } else if (plain) {
     const int64_t total = M * N;
     gemm_plain_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(g);

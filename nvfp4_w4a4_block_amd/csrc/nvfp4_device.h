@@ -49,6 +49,38 @@ __device__ __forceinline__ float div_rn(float x, float d, float r) {
   return __builtin_fmaf(e, r, q);
 }
 
+// 16 B of input as fp32 values.
+__device__ __forceinline__ void widen(const uint4& w, float* v, const uint16_t*) {
+  uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(a[i] << 16);
+    v[2 * i + 1] = __uint_as_float(a[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void widen(const uint4& w, float* v, const float*) {
+  v[0] = __uint_as_float(w.x);
+  v[1] = __uint_as_float(w.y);
+  v[2] = __uint_as_float(w.z);
+  v[3] = __uint_as_float(w.w);
+}
+
+// Largest |x| bit pattern of 16 B of input, as an fp32 bit pattern.  Integer max of the
+// magnitude bits orders NaN above +inf above every finite value, so NaN propagates.
+__device__ __forceinline__ uint32_t max_abs_bits(const uint4& w, const uint16_t*) {
+  uint32_t m = 0;
+  uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t lo = (a[i] & 0x7FFFu), hi = (a[i] >> 16) & 0x7FFFu;
+    m = max(m, max(lo, hi));
+  }
+  return m << 16;
+}
+__device__ __forceinline__ uint32_t max_abs_bits(const uint4& w, const float*) {
+  return max(max(w.x & 0x7FFFFFFFu, w.y & 0x7FFFFFFFu), max(w.z & 0x7FFFFFFFu, w.w & 0x7FFFFFFFu));
+}
+
 // Encode one 16-element block (values v[0..15] as fp32) under global scale sg.
 // Outputs the E4M3 scale byte and the 16 codes packed into two dwords (element 2i in the
 // low nibble of byte i).  Arithmetic: binary32, round to nearest even, no contraction.

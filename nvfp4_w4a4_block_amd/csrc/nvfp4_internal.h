@@ -97,6 +97,16 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
                 const QuantOut* qout = nullptr, const GateOut* gates = nullptr, bool swiglu = false);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+// Batch-1 decode with the token's quantization fused in (per-row, which at one row is also
+// per-tensor; or under the given global scale in a_global): one launch that writes the token's
+// NVFP4 bytes to a_codes/a_scales (and a_global unless given) and Y = that token times W, the
+// same bits as launch_quantize followed by launch_gemm wherever launch_gemm also takes the
+// matrix-vector kernel.  bf16 input; NVFP4_ERR_UNSUPPORTED for a shape the kernel does not take
+// (K % 64 != 0, K > 32768, or its LDS would not fit: about K <= 18432).
+int launch_decode_linear(int64_t N, int64_t K, const uint16_t* x, bool given, uint8_t* a_codes, uint8_t* a_scales,
+                         float* a_global, const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                         void* y, int y_dtype, hipStream_t stream);
+
 // MXFP4 operands (E2M1 codes [rows, K/2] as NVFP4, E8M0 scale bytes [rows, K/32]), the same
 // tiling with scaled FP4 MFMAs; K % 256 == 0 and K < 2^24 (NVFP4_ERR_UNSUPPORTED otherwise).
 int launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,

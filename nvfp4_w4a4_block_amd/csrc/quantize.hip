@@ -25,38 +25,6 @@ constexpr int kThreads = 256;
 constexpr int kWideThreads = 1024;       // per-row workgroups when there are fewer rows than CUs
 constexpr int kMaxPartials = 1024;        // pass-1 workgroups (4 partials per pass-2 thread)
 
-// 16 B of input as fp32 values.
-__device__ __forceinline__ void widen(const uint4& w, float* v, const uint16_t*) {
-  uint32_t a[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(a[i] << 16);
-    v[2 * i + 1] = __uint_as_float(a[i] & 0xFFFF0000u);
-  }
-}
-__device__ __forceinline__ void widen(const uint4& w, float* v, const float*) {
-  v[0] = __uint_as_float(w.x);
-  v[1] = __uint_as_float(w.y);
-  v[2] = __uint_as_float(w.z);
-  v[3] = __uint_as_float(w.w);
-}
-
-// Largest |x| bit pattern of 16 B of input, as an fp32 bit pattern.  Integer max of the
-// magnitude bits orders NaN above +inf above every finite value, so NaN propagates.
-__device__ __forceinline__ uint32_t max_abs_bits(const uint4& w, const uint16_t*) {
-  uint32_t m = 0;
-  uint32_t a[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t lo = (a[i] & 0x7FFFu), hi = (a[i] >> 16) & 0x7FFFu;
-    m = max(m, max(lo, hi));
-  }
-  return m << 16;
-}
-__device__ __forceinline__ uint32_t max_abs_bits(const uint4& w, const float*) {
-  return max(max(w.x & 0x7FFFFFFFu, w.y & 0x7FFFFFFFu), max(w.z & 0x7FFFFFFFu, w.w & 0x7FFFFFFFu));
-}
-
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));

@@ -110,6 +110,17 @@ def test_gemm_argument_errors(nv):
     assert g(nv, M=0) == 0 and g(nv, N=0, ldy=0) == 0     # empty products are no-ops
 
 
+def test_decode_linear_argument_errors(nv):
+    def d(N=32, K=128, x=A16, dt=1, mode=0, c=A16, s=A16, gl=A16, w=A16, sw=A16, gw=A16, y=A16, ydt=1):
+        return nv.lib.nvfp4_decode_linear(N, K, x, dt, mode, c, s, gl, w, sw, gw, y, ydt, None)
+    assert d(K=24) == 1 and d(K=0) == 1 and d(N=-1) == 1
+    assert d(x=None) == 1 and d(x=MIS) == 1
+    assert d(c=None) == 1 and d(c=A16 + 8) == 1 and d(s=A16 + 4) == 1   # codes, scales 16-byte aligned
+    assert d(gl=None) == 1
+    assert d(w=None) == 1 and d(sw=MIS) == 1 and d(gw=None) == 1 and d(y=None) == 1
+    assert d(dt=7) == 1 and d(ydt=3) == 1 and d(mode=5) == 1
+
+
 def test_fused_argument_errors(nv):
     widths = (ctypes.c_int64 * 3)(16, 0, 16)
     f = nv.lib.nvfp4_gemm_fused_segments

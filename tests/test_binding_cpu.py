@@ -124,3 +124,26 @@ def test_fp8_kv_checked(nv):
         nv.fp8_kv_quantize(x, f32(1))
     with pytest.raises(ValueError, match="GPU"):
         nv.fp8_kv_dequantize(u8(64), f32(1))
+
+
+def test_decode_linear_checked(nv):
+    x = torch.zeros((1, 64), dtype=torch.bfloat16)
+    w = operand(nv, 8, 64)
+    with pytest.raises(ValueError, match="GPU"):          # well-formed, but on the CPU
+        nv.decode_linear(x, w)
+    with pytest.raises(ValueError, match=r"\[1, K\]"):
+        nv.decode_linear(torch.zeros((2, 64), dtype=torch.bfloat16), w)
+    with pytest.raises(ValueError, match="bf16 or fp32"):
+        nv.decode_linear(torch.zeros((1, 64), dtype=torch.float16), w)
+    with pytest.raises(ValueError, match="K mismatch"):
+        nv.decode_linear(x, operand(nv, 8, 128))
+    with pytest.raises(ValueError, match="mode"):
+        nv.decode_linear(x, w, "per_column")
+    with pytest.raises(ValueError, match="global_scale"):
+        nv.decode_linear(x, w, "given")
+    with pytest.raises(ValueError, match="w.global_scale"):
+        nv.decode_linear(x, operand(nv, 8, 64, gs=8))
+    with pytest.raises(ValueError, match="a_out.codes"):
+        nv.decode_linear(x, w, a_out=nv.NVFP4Tensor(u8(1, 16), u8(1, 4), f32(1)))
+    with pytest.raises(ValueError, match="a_out.global_scale"):
+        nv.decode_linear(x, w, a_out=nv.NVFP4Tensor(u8(1, 32), u8(1, 4), f32(2)))
