@@ -172,3 +172,29 @@ def test_graph_mxfp4_decode(N, K):
         return ae.codes, ae.scales, nv().mxfp4_gemm(ae, w.codes, w.scales, (N,), w.global_scale, torch.float32)
 
     _replay_and_compare(g, x, M, K, (am.codes, am.scales, y), eager)
+
+
+def test_graph_batch1_decode():
+    # Batch 1: the matrix-vector kernel as two calls, and the one-call entry point that quantizes
+    # the token inside the GEMM launch, captured together.
+    N, K = 3000, 4160
+    w = nv().quantize(to_gpu(workloads.weight(204, 1, N, K)))
+    x = torch.empty((1, K), dtype=torch.bfloat16, device=DEV)
+    _fill(x, 299, 1, K)
+    a = nv().quantize(x)
+    y = nv().gemm(a, w, torch.float32)
+    y1, a1 = nv().decode_linear(x, w, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        nv().quantize(x, out=a)
+        nv().gemm(a, w, torch.float32, out=y)
+        nv().decode_linear(x, w, out_dtype=torch.float32, out=y1, a_out=a1)
+
+    def eager():
+        ae = nv().quantize(x)
+        ye = nv().gemm(ae, w, torch.float32)
+        yf, af = nv().decode_linear(x, w, out_dtype=torch.float32)
+        return ae.codes, ae.global_scale, ye, af.codes, af.scales, af.global_scale, yf
+
+    _replay_and_compare(g, x, 1, K, (a.codes, a.global_scale, y, a1.codes, a1.scales, a1.global_scale, y1), eager)
