@@ -1814,8 +1814,9 @@ __global__ __launch_bounds__(kDwThreads) void gemm_mx_decode_rows_kernel(GemmArg
 // work whatever R is (a range may start and end inside a row).  Lane l multiplies the 16 bytes
 // at 16 l (32 values, two blocks) with scale bytes 2 l and 2 l + 1.  Items are copied straight
 // into a ring of kGvDepth slots private to the wavefront (one 1 KB copy for the codes, one 256 B
-// copy for the scales, lanes 32-63 repeating lanes 0-31), waited for with exact counts so that
-// kGvDepth - 1 items stay in flight across rows, and read from LDS one item ahead of the
+// copy for the scales, lanes 32-63 repeating lanes 0-31), waited for with exact counts (which
+// rest on the wavefront's loads completing in issue order, 16-byte and 4-byte copies alike) so
+// that kGvDepth - 1 items stay in flight across rows, and read from LDS one item ahead of the
 // products; copies past the range re-read its last item, unused.  The token's bytes are copied
 // into LDS the same way, before the ring's first copies, so those stay in flight while the token
 // is dequantized.  With 16 wavefronts per CU the latency of one wavefront's LDS reads and
