@@ -16,7 +16,9 @@
  *   7. a lossy variant: NVFP4 re-encoded to MXFP4 and multiplied with gfx950's native scaled
  *      FP4 matrix instructions;
  *   8. the gated MLP input projection: the fused gate+up GEMM with its SwiGLU activation in
- *      the same launch, the result optionally leaving as NVFP4 for the down projection.
+ *      the same launch, the result optionally leaving as NVFP4 for the down projection;
+ *   9. batch-1 decode of one linear layer in one launch: 1 and 2 with the token's quantization
+ *      inside the GEMM kernel.
  *
  * Sources: the element format (E2M1 values, one E4M3 scale per 16-element block) is from
  * "NVFP4 W4A4 Quantization Compresses 27B Hybrid Models" (thevalue.engineering), section
