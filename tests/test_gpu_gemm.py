@@ -252,11 +252,12 @@ def test_gemv_batch1_segments_and_pitch():
                                  torch.cat([q.global_scale for q in gq]), torch.float32)
     Y, T = ref.fused_segments(oa, oq)
     assert_gemm_close(y, Y, T, "gemv fused")
-    big = torch.full((1, 2000), 7.0, dtype=torch.float32, device=DEV)
-    nv().gemm(a, gq[2], torch.float32, out=big[:, :1000])
     Y2, T2 = ref.gemm(oa, oq[2])
-    assert_gemm_close(big[:, :1000], Y2, T2, "gemv pitch")
-    assert torch.all(big[:, 1000:] == 7.0)
+    for dt in (torch.float32, torch.bfloat16):
+        big = torch.full((1, 2000), 7.0, dtype=dt, device=DEV)
+        nv().gemm(a, gq[2], dt, out=big[:, :1000])
+        assert_gemm_close(big[:, :1000], Y2, T2, f"gemv pitch {dt}")
+        assert torch.all(big[:, 1000:] == 7.0)
 
 
 def test_decode_balanced_rows_segments():

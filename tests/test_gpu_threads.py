@@ -1,5 +1,5 @@
 """Concurrent first calls: several host threads of a fresh process make their first
-quantize + GEMM calls at the same moment, each on its own stream, so the library's once-per-
+quantize + GEMM calls (and a one-call batch-1 decode) at the same moment, each on its own stream, so the library's once-per-
 device set-up (kernel LDS limits, the compute-unit count, the static scratch address) runs
 while other threads are already calling in.  Every thread's results must equal, bit for bit,
 those of the same calls made afterwards by one thread.  The workers run in a child process so
@@ -36,7 +36,9 @@ def step(i):
     y = nv.gemm(a, q, torch.float32)                         # prefill kernel (M = 512)
     ad = nv.quantize(xd[i], "per_row")
     yd = nv.gemm(ad, q, torch.float32)                      # decode kernel (M = 4)
-    return [a.codes, a.scales, a.global_scale, q.codes, q.scales, y, ad.codes, ad.scales, yd]
+    y1, a1 = nv.decode_linear(xd[i][:1], q, out_dtype=torch.float32)   # batch 1, one launch
+    return [a.codes, a.scales, a.global_scale, q.codes, q.scales, y, ad.codes, ad.scales, yd,
+            a1.codes, a1.scales, a1.global_scale, y1]
 
 results = [None] * NT
 errors = []
