@@ -319,3 +319,27 @@ def test_deterministic():
     p = workloads.PREFILL
     a, w, _, _ = _quant_pair(p.x(512), p.w()[:1024])
     assert torch.equal(nv().gemm(a, w), nv().gemm(a, w))
+
+
+def test_batch1_per_row_flag_at_the_abi():
+    # One token: a per-row global scale and a per-tensor one are the same number, and the C ABI
+    # accepts either flag; both calls must give the same bits (the binding always passes 0 here).
+    N, K = 3000, 2048
+    g = np.random.default_rng(5)
+    ow = ref.NVFP4(g.integers(0, 256, (N, K // 2), dtype=np.uint8), g.integers(0x10, 0x40, (N, K // 16), dtype=np.uint8),
+                   np.array([0.75], np.float32), N, K)
+    oa = ref.NVFP4(g.integers(0, 256, (1, K // 2), dtype=np.uint8), g.integers(0x10, 0x40, (1, K // 16), dtype=np.uint8),
+                   np.array([1.25], np.float32), 1, K)
+    a, w = to_device(oa), to_device(ow)
+    ys = []
+    for per_row in (0, 1):
+        y = torch.empty((1, N), dtype=torch.float32, device=DEV)
+        st = nv().lib.nvfp4_gemm(1, N, K, a.codes.data_ptr(), a.scales.data_ptr(), a.global_scale.data_ptr(), per_row,
+                                 w.codes.data_ptr(), w.scales.data_ptr(), w.global_scale.data_ptr(), y.data_ptr(), 0, N,
+                                 None, 0, torch.cuda.current_stream(DEV).cuda_stream)
+        assert st == 0
+        ys.append(y)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ys[1])
+    Y, T = ref.gemm(oa, ow)
+    assert_gemm_close(ys[0], Y, T, "batch-1 per-row flag")
