@@ -75,6 +75,132 @@ def check_m0(asm: str) -> int:
     return writes
 
 
+def lds_reads_in_flight_at_copies(asm: str) -> dict:
+    """For each kernel of a gfx950 assembly listing that issues direct-to-LDS copies
+    (global_load_lds): the largest number of LDS reads that may still be in flight when such a
+    copy is issued, over every path through the kernel's branches.  A copy lands in LDS
+    asynchronously, so a read of the bytes it overwrites must be complete before it is issued.
+
+    Model: LDS instructions complete in issue order; scalar memory loads also count in lgkmcnt
+    but complete in any order, so `s_waitcnt lgkmcnt(N)` is taken to retire them first (the
+    case that leaves the most LDS reads in flight) and then the oldest LDS operations until at
+    most N remain.  Only the newest 64 operations are tracked: a wait keeps at most its
+    newest 15 (the counter is 4 bits wide), so older ones never change a result.  Returns
+    {kernel symbol: count}."""
+    import re
+    result = {}
+    funcs, cur = [], None
+    for raw in asm.splitlines():
+        m = re.match(r"^([A-Za-z_][\w.$]*):", raw)
+        if m:
+            cur = [m.group(1), []]
+            funcs.append(cur)
+            continue
+        if cur is None:
+            continue
+        if raw.startswith(".Lfunc_end"):
+            cur = None
+            continue
+        line = raw.split(";")[0].strip()
+        if line:
+            cur[1].append(line)
+    for name, lines in funcs:
+        if not any(l.startswith("global_load_lds") for l in lines):
+            continue
+        # basic blocks: a label starts one, a branch or s_endpgm ends one
+        blocks, labels, blk = [], {}, []
+        for l in lines:
+            lm = re.match(r"^(\.L\w+):", l)
+            if lm:
+                if blk:
+                    blocks.append(blk)
+                    blk = []
+                labels[lm.group(1)] = len(blocks)
+                continue
+            if l.startswith("."):
+                continue
+            blk.append(l)
+            if l.startswith(("s_branch", "s_cbranch", "s_endpgm", "s_setpc")):
+                blocks.append(blk)
+                blk = []
+        if blk:
+            blocks.append(blk)
+        # successors of block i: a branch target (a label maps to the block that follows it)
+        # and, unless the block ends in an unconditional branch or the end of the program, the
+        # next block
+        def succ(i):
+            last = blocks[i][-1] if blocks[i] else ""
+            op = last.split()[0] if last else ""
+            out = []
+            if op in ("s_endpgm", "s_setpc_b64"):
+                return out
+            if op.startswith(("s_branch", "s_cbranch")):
+                tgt = last.split()[-1]
+                if tgt not in labels:
+                    raise RuntimeError(f"{name}: branch to unknown label {tgt}")
+                out.append(labels[tgt])
+                if op == "s_branch":
+                    return [t for t in out if t < len(blocks)]
+            if i + 1 < len(blocks):
+                out.append(i + 1)
+            return [t for t in out if t < len(blocks)]
+
+        def step(q, l):
+            op = l.split()[0]
+            if op.startswith("ds_"):
+                return q + ("r" if op.startswith("ds_read") else "o",)
+            if op.startswith(("s_load", "s_buffer_load", "s_memtime", "s_memrealtime", "s_sendmsg")):
+                return q + ("s",)
+            if op == "s_waitcnt":
+                m = re.search(r"lgkmcnt\((\d+)\)", l)
+                if m:
+                    n = int(m.group(1))
+                    q = list(q)
+                    while len(q) > n:
+                        if "s" in q:
+                            q.remove("s")
+                        else:
+                            q.pop(0)
+                    return tuple(q)
+            return q
+
+        # every (block, operations in flight at its entry) reachable from the kernel's entry
+        seen = {(0, ())}
+        work, worst = [(0, ())], 0
+        while work:
+            i, q = work.pop()
+            for l in blocks[i]:
+                if l.startswith("global_load_lds"):
+                    worst = max(worst, q.count("r"))
+                q = step(q, l)[-64:]
+            for t in succ(i):
+                if (t, q) not in seen:
+                    seen.add((t, q))
+                    if len(seen) > 100000:
+                        raise RuntimeError(f"{name}: too many paths to follow")
+                    work.append((t, q))
+        result[name] = worst
+    return result
+
+
+# LDS reads allowed in flight at a direct-to-LDS copy, per kernel: none, except where a kernel
+# reads the next ring slot ahead while it refills another one (the batch-1 kernel's next item:
+# one 16-byte code read, one scale read and four token reads).
+LDS_READ_AHEAD = {"gemm_gemv_kernel": 6}
+
+
+def check_lds_refills(asm: str) -> dict:
+    """Raise RuntimeError if any kernel may issue a direct-to-LDS copy while more LDS reads
+    are in flight than LDS_READ_AHEAD allows it; returns the per-kernel counts."""
+    found = lds_reads_in_flight_at_copies(asm)
+    for fn, n in found.items():
+        allowed = next((v for k, v in LDS_READ_AHEAD.items() if k in fn), 0)
+        if n > allowed:
+            raise RuntimeError(f"{fn}: a direct-to-LDS copy may be issued with {n} LDS reads in flight "
+                               f"(at most {allowed} allowed)")
+    return found
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source to an object in parallel (each carries its own gfx950 code
     object), then link the shared library."""
@@ -101,7 +227,9 @@ def build(verbose: bool = False) -> str:
         if verbose and err.strip():
             print(err, file=sys.stderr)
     with open(gemm_s) as f:
-        check_m0(f.read())
+        text = f.read()
+    check_m0(text)
+    check_lds_refills(text)
     for lib, o in ((LIB, objs), (CALIB_LIB, calib_objs)):
         tmp = lib + ".tmp"
         res = _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *o, "-o", tmp], verbose)

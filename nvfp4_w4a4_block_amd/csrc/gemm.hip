@@ -2085,6 +2085,11 @@ __global__ __launch_bounds__(kGvThreads) void gemm_gemv_kernel(GemmArgs g, int r
           acc = __builtin_fmaf(p, (float)scale_pair_f16((cur.sc >> (8 * b)) & 0xFFu)[0], acc);
         }
         __builtin_amdgcn_sched_barrier(0);
+        // The refill below overwrites the slot that item i was read from.  Those reads must be
+        // complete first; the sum above consumes every value they loaded, so taking it as an
+        // operand here places the copy after the compiler's own wait for them (without it the
+        // compiler may issue the copy ahead of that wait and of the arithmetic).
+        asm volatile("" : : "v"(acc) : "memory");
         copy_next(u);                                    // item i's slot, for item i + D
         if (jc + 1 == nch || i0 + u + 1 == items) {      // end of this wavefront's part of row jr
           const float v = wave_sum_dpp(acc);

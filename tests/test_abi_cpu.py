@@ -155,22 +155,67 @@ def test_fastdiv_host_logic(tmp_path):
     assert r.returncode == 0 and r.stdout.strip() == "0", r.stdout
 
 
-def test_m0_is_only_set_for_lds_copies(tmp_path):
+@pytest.fixture(scope="module")
+def gemm_asm(tmp_path_factory):
+    """The GEMM source's generated gfx950 device assembly."""
+    from nvfp4_w4a4_block_amd import build as b
+    flags = [f for f in b.HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
+    out = tmp_path_factory.mktemp("asm") / "gemm.s"
+    r = subprocess.run([b.hipcc(), *flags, "--cuda-device-only", "-S", "-I", os.path.join(ROOT, "include"),
+                        os.path.join(b.CSRC, "gemm.hip"), "-o", str(out)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return out.read_text()
+
+
+def test_m0_is_only_set_for_lds_copies(gemm_asm):
     """The GEMM's direct-to-LDS copies set M0 in inline assembly, which the compiler cannot be
     told about.  Check on the generated gfx950 assembly that every M0 write is one of those
     copies (immediately followed by its global_load_lds) and that nothing else reads M0."""
     from nvfp4_w4a4_block_amd import build as b
-    flags = [f for f in b.HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
-    out = tmp_path / "gemm.s"
-    r = subprocess.run([b.hipcc(), *flags, "--cuda-device-only", "-S", "-I", os.path.join(ROOT, "include"),
-                        os.path.join(b.CSRC, "gemm.hip"), "-o", str(out)], capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr[-2000:]
-    assert b.check_m0(out.read_text()) > 0
+    assert b.check_m0(gemm_asm) > 0
     # the check rejects a stray M0 use and a copy without its own M0 write
     with pytest.raises(RuntimeError):
         b.check_m0("s_mov_b32 m0, s4\nglobal_load_lds_dwordx4 v1, off\ns_add_u32 s0, m0, 1\n")
     with pytest.raises(RuntimeError):
         b.check_m0("s_mov_b32 m0, s4\nglobal_load_lds_dwordx4 v1, off\nglobal_load_lds_dwordx4 v2, off\n")
+
+
+def _kernel(name, body):
+    return f"{name}:\n" + "\n".join("\t" + l if not l.startswith(".LBB") else l for l in body) + "\n.Lfunc_end0:\n"
+
+
+def test_lds_refills_wait_for_reads(gemm_asm):
+    """A direct-to-LDS copy writes LDS when its data arrives, so an LDS read of the bytes it
+    overwrites must be complete before the copy is issued.  On the generated assembly, over
+    every path through each kernel's branches: no copy is issued with an LDS read in flight,
+    except the batch-1 kernel's read-ahead of its next item (6 reads, from another ring slot)."""
+    from nvfp4_w4a4_block_amd import build as b
+    found = b.check_lds_refills(gemm_asm)
+    gemv = {k: v for k, v in found.items() if "gemm_gemv_kernel" in k}
+    assert len(gemv) == 2 and all(v == 6 for v in gemv.values()), gemv
+    others = {k: v for k, v in found.items() if k not in gemv}
+    assert len(others) >= 10 and not any(others.values()), others
+
+    count = lambda body: b.lds_reads_in_flight_at_copies(_kernel("k", body))["k"]
+    copy = "global_load_lds_dword v2, s[0:1]"
+    # straight line: a pending read counts, a wait retires it
+    assert count(["ds_read_b32 v0, v1", copy, "s_endpgm"]) == 1
+    assert count(["ds_read_b32 v0, v1", "s_waitcnt lgkmcnt(0)", copy, "s_endpgm"]) == 0
+    # LDS operations retire in order: lgkmcnt(1) leaves only the newest in flight
+    assert count(["ds_read_b32 v0, v1", "ds_read_b32 v3, v1", "s_waitcnt lgkmcnt(1)", copy, "s_endpgm"]) == 1
+    assert count(["ds_read_b32 v0, v1", "ds_write_b32 v1, v0", "s_waitcnt lgkmcnt(1)", copy, "s_endpgm"]) == 0
+    # a scalar load may complete first, so it does not stand in for the read
+    assert count(["ds_read_b32 v0, v1", "s_load_dword s4, s[0:1], 0x0", "s_waitcnt lgkmcnt(1)", copy,
+                  "s_endpgm"]) == 1
+    # a branch that skips the wait, and a read carried round a loop to the copy at its top
+    assert count(["ds_read_b32 v0, v1", "s_cbranch_scc1 .LBB0_2", "s_waitcnt lgkmcnt(0)", ".LBB0_2:", copy,
+                  "s_endpgm"]) == 1
+    assert count([".LBB0_1:", copy, "ds_read_b32 v0, v1", "s_cbranch_scc1 .LBB0_1", "s_endpgm"]) >= 1
+    assert count([".LBB0_1:", copy, "ds_read_b32 v0, v1", "s_waitcnt lgkmcnt(0)", "s_cbranch_scc1 .LBB0_1",
+                  "s_endpgm"]) == 0
+    with pytest.raises(RuntimeError):
+        b.check_lds_refills(_kernel("k", ["ds_read_b32 v0, v1", copy, "s_endpgm"]))
+    b.check_lds_refills(_kernel("gemm_gemv_kernel_x", ["ds_read_b32 v0, v1", copy, "s_endpgm"]))
 
 
 def test_nvfp4_out_argument_errors(nv):
