@@ -215,8 +215,8 @@ int nvfp4_gemm_fused_segments(int64_t M, int64_t K,
  * scale is given (a calibrated, static scale): a dynamic per-tensor scale would need the
  * whole output before the first block could be encoded.  Format and encoding as for
  * nvfp4_quantize (sources in the file header).
- *   N = sum of seg_n, a multiple of 16; K a multiple of 128, and for M > 16 a multiple of
- *   256 below 2^24 (other shapes: NVFP4_ERR_UNSUPPORTED).
+ *   N = sum of seg_n, a multiple of 16; K a multiple of 128 below 2^24, and for M > 16 a
+ *   multiple of 256 (other shapes: NVFP4_ERR_UNSUPPORTED).
  *   y_global      device [1], in: finite and > 0.
  *   y_codes       out [M, N/2], 16-byte aligned; y_scales out [M, N/16], 16-byte aligned.
  *   Other arguments as in nvfp4_gemm_fused_segments (one segment: a plain GEMM).
@@ -337,8 +337,8 @@ int nvfp4_interleave_gate_up(int64_t F, int64_t K,
  * h_codes is given: each 16-element block of a row encoded exactly as nvfp4_quantize in
  * NVFP4_SCALE_GIVEN mode encodes it under h_global[0] (a calibrated, static scale).  At least
  * one of the two outputs is required.
- *   F > 0, a multiple of 16 (hidden width); K a multiple of 128, and for M > 16 a multiple of
- *   256 below 2^24 (other shapes: NVFP4_ERR_UNSUPPORTED); M * F < 2^31.
+ *   F > 0, a multiple of 16 (hidden width); K a multiple of 128 below 2^24, and for M > 16 a
+ *   multiple of 256 (other shapes: NVFP4_ERR_UNSUPPORTED); M * F < 2^31.
  *   w_codes [2F, K/2], w_scales [2F, K/16]: the interleaved layout of nvfp4_interleave_gate_up.
  *   w_globals device [2] = {gate, up}.
  *   h       out [M, F] of h_dtype, row pitch ldh >= F elements, or NULL.

@@ -2320,7 +2320,11 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
                 hipStream_t stream, const QuantOut* qout, const GateOut* gates, bool swiglu) {
   (void)workspace;
   if (M == 0 || N == 0) return NVFP4_OK;
-  const bool plain = K % 128 != 0 || (M > 16 && (K % BK != 0 || K >= (1 << 24)));
+  // The tiled and decode kernels address a row of W or A with 32-bit per-lane offsets from a
+  // per-tile base (row index times the row pitch, up to 96 rows at once; 24-bit multiplies in
+  // the prefill tiles): K below 2^24 keeps every such offset in range.  Larger K, and K that
+  // is not a multiple of 128 (or of 256 past 16 tokens), take the plain kernel.
+  const bool plain = K % 128 != 0 || K >= (1 << 24) || (M > 16 && K % BK != 0);
   if ((qout || swiglu) && (plain || N % 16 != 0)) return NVFP4_ERR_UNSUPPORTED;
   if ((qout || swiglu) && gates) return NVFP4_ERR_INVALID_ARG;
   if (swiglu && N % 32 != 0) return NVFP4_ERR_INVALID_ARG;

@@ -230,6 +230,7 @@ def test_nvfp4_out_argument_errors(nv):
     assert call(gy=None) == 1 and call(yc=None) == 1 and call(ys=A16 + 8) == 1
     assert call(K=272) == 2                        # K not a multiple of 128: no kernel takes it
     assert call(M=32, K=384) == 2                  # M > 16 needs K % 256 == 0
+    assert call(M=1, K=1 << 24) == 2 and call(M=32, K=1 << 24) == 2   # K >= 2^24: only the plain kernel
     assert call(M=0) == 0                          # empty product: a no-op
 
 

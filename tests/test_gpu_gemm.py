@@ -292,6 +292,20 @@ def test_decode_fused_segments():
     assert_gemm_close(y, Y, T, "decode fused")
 
 
+@pytest.mark.parametrize("M", [1, 4])
+def test_long_k_at_decode(M):
+    """K = 2^24 with few tokens: the tiled and decode kernels address rows with 32-bit offsets
+    that are only guaranteed below 2^24, so these shapes run the plain kernel."""
+    K, N = 1 << 24, 3
+    rng = np.random.default_rng(24 + M)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    w = rng.standard_normal((N, K), dtype=np.float32)
+    a, q, oa, ow = _quant_pair(x, w)
+    y = nv().gemm(a, q, torch.float32)
+    Y, T = ref.gemm(oa, ow)
+    assert_gemm_close(y, Y, T, f"K = 2^24, M = {M}")
+
+
 def test_decode_deterministic():
     d = workloads.DECODE
     a, w, _, _ = _quant_pair(d.x(16), d.w()[:512])
