@@ -198,7 +198,7 @@ def quantize(x: torch.Tensor, mode: str = "per_tensor", global_scale: torch.Tens
     of one element)."""
     _require(isinstance(x, torch.Tensor) and x.dim() == 2, "x must be a 2-D tensor")
     _require(x.dtype in (torch.bfloat16, torch.float32), "x must be bf16 or fp32")
-    _require(x.stride(1) == 1, "x must be row-contiguous")
+    _require(x.stride(1) == 1 or x.shape[0] == 0, "x must be row-contiguous")   # (no rows: no data)
     _require(mode in _MODES, f"mode must be one of {sorted(_MODES)}")
     m = _MODES[mode]
     rows, cols = x.shape

@@ -2,6 +2,7 @@
 ValueError before the library is called.  The binding checks shapes, dtypes, contiguity and
 global-scale counts first and GPU residency last, so these cases run on CPU tensors; a call
 whose only fault is that its tensors live on the CPU fails the residency check."""
+import numpy as np
 import pytest
 import torch
 
@@ -43,6 +44,12 @@ def test_quantize_out_checked(nv):
         nv.quantize(x, "per_column")
     with pytest.raises(ValueError, match="GPU"):          # well-formed, but on the CPU
         nv.quantize(x)
+    with pytest.raises(ValueError, match="row-contiguous"):
+        nv.quantize(torch.zeros((8, 128), dtype=torch.bfloat16)[:, ::2])
+    # no rows: no data, so any strides pass the layout checks (torch gives (0, 0) for an empty
+    # array made from numpy); only the residency check remains
+    with pytest.raises(ValueError, match="GPU"):
+        nv.quantize(torch.from_numpy(np.zeros((0, 64), np.float32)))
 
 
 def test_gemm_operands_checked(nv):

@@ -64,3 +64,68 @@ def test_random_shape(M, K, widths, mode, out_dtype, seed):
                                      widths, torch.cat([q.global_scale for q in gq]), out_dtype)
     Y, T = ref.fused_segments(oa, oq)
     assert_gemm_close(y, Y, T, f"M={M} K={K} widths={widths} {mode}")
+
+
+def _quant_cases():
+    rng = np.random.default_rng(7)
+    cases = []
+    for i in range(40):
+        rows = int(rng.choice([0, 1, 2, 3, 17, 255, 256, 257, 1000, int(rng.integers(1, 3000))]))
+        cols = 16 * int(rng.integers(1, 400))
+        pad = 0 if rng.random() < 0.5 else 8 * int(rng.integers(1, 40))      # row stride - width, elements
+        fp32 = bool(rng.random() < 0.3)
+        mode = str(rng.choice(["per_tensor", "per_row", "given"]))
+        cases.append(pytest.param(rows, cols, pad, fp32, mode, i, id=f"{rows}x{cols}+{pad}-{'f32' if fp32 else 'bf16'}-{mode}"))
+    return cases
+
+
+@pytest.mark.parametrize("rows,cols,pad,fp32,mode,seed", _quant_cases())
+def test_random_quantize(rows, cols, pad, fp32, mode, seed):
+    """Quantizer bytes (codes, scale bytes, global scales) bitwise against the oracle over random
+    shapes, row strides wider than the rows, both input types and every scale mode."""
+    # (the stride cols + pad is a multiple of 8 elements: 16-byte rows for both input types)
+    x = workloads.activation(1000 + seed, 0, max(rows, 1), cols + pad)[:rows] * np.float32(1 + seed % 5)
+    full = to_gpu(x, bf16=not fp32)
+    xg = full[:, :cols]
+    src = xg.float().cpu().numpy()
+    if mode == "given":
+        g = torch.tensor([np.float32(0.0123 * (1 + seed % 7))], dtype=torch.float32, device=xg.device)
+        got = nv().quantize(xg, "given", global_scale=g)
+        want = ref.quantize(src, ref.GIVEN, given=float(g.item()))
+    else:
+        got = nv().quantize(xg, mode)
+        want = ref.quantize(src, ref.PER_ROW if mode == "per_row" else ref.PER_TENSOR)
+    assert_quant_equal(got, want, what=f"{rows}x{cols} stride {cols + pad}")
+
+
+def _decode_linear_cases():
+    rng = np.random.default_rng(11)
+    cases = []
+    for i in range(24):
+        K = 64 * int(rng.integers(1, 288))                   # up to the one-call kernel's LDS limit
+        N = int(rng.choice([1, 3, int(rng.integers(1, 9000)), int(rng.integers(1, 300))]))
+        mode = "per_tensor" if rng.random() < 0.7 else "given"
+        cases.append(pytest.param(N, K, mode, i, id=f"{N}x{K}-{mode}"))
+    return cases
+
+
+@pytest.mark.parametrize("N,K,mode,seed", _decode_linear_cases())
+def test_random_decode_linear(N, K, mode, seed):
+    """The one-call batch-1 decode over random shapes: the token's bytes bitwise against the
+    oracle's quantization of the bf16 row, Y against the oracle's product within the bound."""
+    xg = to_gpu(workloads.activation(2000 + seed, 0, 1, K))
+    wg = to_gpu(workloads.weight(2000 + seed, 1, N, K, sigma=0.03))
+    w = nv().quantize(wg)
+    ow = ref.quantize(wg.float().cpu().numpy())
+    src = xg.float().cpu().numpy()
+    if mode == "given":
+        gs = np.float32(0.004 * (1 + seed % 3))
+        y, a = nv().decode_linear(xg, w, mode="given", global_scale=torch.tensor([gs], device=xg.device),
+                                  out_dtype=torch.float32)
+        oa = ref.quantize(src, ref.GIVEN, given=float(gs))
+    else:
+        y, a = nv().decode_linear(xg, w, mode="per_tensor", out_dtype=torch.float32)
+        oa = ref.quantize(src, ref.PER_ROW)
+    assert_quant_equal(a, oa, what="token")
+    Y, T = ref.gemm(oa, ow)
+    assert_gemm_close(y, Y, T, f"decode_linear N={N} K={K}")
