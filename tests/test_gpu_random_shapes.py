@@ -129,3 +129,52 @@ def test_random_decode_linear(N, K, mode, seed):
     assert_quant_equal(a, oa, what="token")
     Y, T = ref.gemm(oa, ow)
     assert_gemm_close(y, Y, T, f"decode_linear N={N} K={K}")
+
+
+def _epilogue_shape(rng):
+    """M, K for the fused epilogues: up to 16 tokens K a multiple of 128 (K-split or balanced
+    decode kernel at K % 256 == 0, the register decode kernel otherwise), past 16 a multiple of
+    256 (prefill tiles)."""
+    M = int(rng.choice([1, int(rng.integers(2, 17)), int(rng.integers(17, 400))]))
+    K = 128 * int(rng.integers(1, 24)) if M <= 16 else 256 * int(rng.integers(1, 12))
+    return M, K
+
+
+def _nvfp4_out_cases():
+    rng = np.random.default_rng(17)
+    cases = []
+    for i in range(16):
+        M, K = _epilogue_shape(rng)
+        nseg = int(rng.integers(1, 4))
+        widths = tuple(16 * int(rng.integers(1, 160)) for _ in range(nseg))
+        mode = "per_row" if rng.random() < 0.5 else "per_tensor"
+        cases.append(pytest.param(M, K, widths, mode, 300 + i, id=f"{M}x{K}-{'-'.join(map(str, widths))}-{mode}"))
+    return cases
+
+
+@pytest.mark.parametrize("M,K,widths,a_mode,seed", _nvfp4_out_cases())
+def test_random_nvfp4_out(M, K, widths, a_mode, seed):
+    """GEMM with NVFP4 output over random shapes: the fp32 values within the GEMM bound, then the
+    codes and scale bytes bitwise against the oracle's encoding of them."""
+    from tests.test_gpu_nvfp4_out import _check
+    _check(M, K, widths, a_mode, seed=seed)
+
+
+def _swiglu_cases():
+    rng = np.random.default_rng(19)
+    cases = []
+    for i in range(16):
+        M, K = _epilogue_shape(rng)
+        F = 16 * int(rng.integers(1, 300))
+        h = torch.bfloat16 if rng.random() < 0.5 else torch.float32
+        mode = ref.PER_ROW if rng.random() < 0.5 else ref.PER_TENSOR
+        cases.append(pytest.param(M, F, K, mode, h, 400 + i, id=f"{M}x{F}x{K}-{mode}-{str(h)[6:]}"))
+    return cases
+
+
+@pytest.mark.parametrize("M,F,K,a_mode,h_dtype,seed", _swiglu_cases())
+def test_random_swiglu(M, F, K, a_mode, h_dtype, seed):
+    """The SwiGLU GEMM over random shapes: h within its derived bound, NVFP4 h bitwise."""
+    from tests.test_gpu_swiglu import _check, _workload_operands
+    oa, og, ou = _workload_operands(seed, M, F, K, a_mode)
+    _check(oa, og, ou, h_dtype, what=f"swiglu {M}x{F}x{K}")
