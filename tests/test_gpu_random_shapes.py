@@ -5,7 +5,9 @@ the K-split and balanced decode kernels (M <= 16, K % 256 == 0, N on either side
 32-row workgroups) and the prefill tiles with their peeled 128 x 128 tails.  Each case is a
 fused launch of 1-4 modules with their own global scales (one module: the plain GEMM), per-
 tensor or per-row activation scales and fp32 or bf16 output, checked element by element against
-the oracle's fused GEMM with the per-element bound of the other parity tests."""
+the oracle's fused GEMM with the per-element bound of the other parity tests.  The other entry
+points (quantizer, one-call batch-1 decode, NVFP4-output, SwiGLU and GDN-gate epilogues, the
+MXFP4 variant) get their own random sweeps, checked as their fixed-shape tests check them."""
 import numpy as np
 import pytest
 import torch
@@ -178,3 +180,48 @@ def test_random_swiglu(M, F, K, a_mode, h_dtype, seed):
     from tests.test_gpu_swiglu import _check, _workload_operands
     oa, og, ou = _workload_operands(seed, M, F, K, a_mode)
     _check(oa, og, ou, h_dtype, what=f"swiglu {M}x{F}x{K}")
+
+
+def _gdn_cases():
+    rng = np.random.default_rng(23)
+    cases = []
+    for i in range(12):
+        M, K = _epilogue_shape(rng)
+        H = int(rng.integers(1, 65))
+        lead = tuple(int(rng.integers(1, 600)) for _ in range(int(rng.integers(1, 4))))
+        mode = "per_row" if rng.random() < 0.5 else "per_tensor"
+        out = torch.bfloat16 if rng.random() < 0.5 else torch.float32
+        cases.append(pytest.param(M, K, lead + (H, H), mode, out, 500 + i,
+                                  id=f"{M}x{K}-{'-'.join(map(str, lead))}-H{H}-{mode}"))
+    return cases
+
+
+@pytest.mark.parametrize("M,K,widths,a_mode,out_dtype,seed", _gdn_cases())
+def test_random_gdn_gates(M, K, widths, a_mode, out_dtype, seed):
+    """The fused GDN projection with its gate epilogue over random shapes and head counts: Y
+    within the GEMM bound and bitwise equal to the fused GEMM, the gates within their bound."""
+    from tests.test_gpu_gdn_gates import _run
+    _run(M, K, widths, seed, a_mode, out_dtype=out_dtype)
+
+
+def _mx_cases():
+    rng = np.random.default_rng(29)
+    cases = []
+    for i in range(12):
+        M = int(rng.choice([1, int(rng.integers(2, 17)), int(rng.integers(17, 400))]))
+        N = int(rng.integers(1, 1200))
+        K = 256 * int(rng.integers(1, 12))
+        out = torch.bfloat16 if rng.random() < 0.5 else torch.float32
+        cases.append(pytest.param(M, N, K, out, 600 + i, id=f"{M}x{N}x{K}-{str(out)[6:]}"))
+    return cases
+
+
+@pytest.mark.parametrize("M,N,K,out_dtype,seed", _mx_cases())
+def test_random_mxfp4(M, N, K, out_dtype, seed):
+    """The lossy MXFP4 variant over random shapes: re-encoding bitwise against the oracle, the
+    GEMM within the bound against the oracle's product of the re-encoded operands."""
+    from tests.test_gpu_mxfp4 import _mx_pair
+    ma, mw, oma, omw, _, _ = _mx_pair(M, N, K, seed)
+    y = nv().mxfp4_gemm(ma, mw.codes, mw.scales, (N,), mw.global_scale, out_dtype)
+    Y, T = ref.mx_gemm(oma, omw)
+    assert_gemm_close(y, Y, T, f"mx {M}x{N}x{K}")
