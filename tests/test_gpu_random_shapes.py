@@ -59,13 +59,20 @@ def test_random_shape(M, K, widths, mode, out_dtype, seed):
         gq.append(nv().quantize(wg))
         oq.append(ref.quantize(wg.float().cpu().numpy()))
         assert_quant_equal(gq[-1], oq[-1], what=f"W{i}")
+    # Half the cases write Y into a wider buffer (row pitch N + 8j elements, so both aligned and
+    # unaligned rows) whose other columns must keep their sentinel.
+    N = sum(widths)
+    pitch = N if seed % 2 else N + 8 * (1 + seed % 7)
+    big = torch.full((M, pitch), 7.0, dtype=out_dtype, device=xg.device)
+    out = big[:, :N]
     if len(widths) == 1:
-        y = nv().gemm(a, gq[0], out_dtype)
+        y = nv().gemm(a, gq[0], out_dtype, out=out)
     else:
         y = nv().gemm_fused_segments(a, torch.cat([q.codes for q in gq]), torch.cat([q.scales for q in gq]),
-                                     widths, torch.cat([q.global_scale for q in gq]), out_dtype)
+                                     widths, torch.cat([q.global_scale for q in gq]), out_dtype, out=out)
     Y, T = ref.fused_segments(oa, oq)
-    assert_gemm_close(y, Y, T, f"M={M} K={K} widths={widths} {mode}")
+    assert_gemm_close(y, Y, T, f"M={M} K={K} widths={widths} {mode} pitch {pitch}")
+    assert bool((big[:, N:] == 7.0).all()), "columns past N were written"
 
 
 def _quant_cases():
