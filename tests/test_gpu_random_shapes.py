@@ -97,14 +97,26 @@ def test_random_quantize(rows, cols, pad, fp32, mode, seed):
     full = to_gpu(x, bf16=not fp32)
     xg = full[:, :cols]
     src = xg.float().cpu().numpy()
+    # Outputs are the fronts of larger buffers holding a sentinel, which must survive.
+    guard = 64
+    cbuf = torch.full((rows * cols // 2 + guard,), 0xA5, dtype=torch.uint8, device=xg.device)
+    sbuf = torch.full((rows * cols // 16 + guard,), 0x5A, dtype=torch.uint8, device=xg.device)
+    ng = rows if mode == "per_row" else 1
+    gbuf = torch.full((ng + guard,), -3.0, dtype=torch.float32, device=xg.device)
+    out = nv().NVFP4Tensor(cbuf[:rows * cols // 2].view(rows, cols // 2), sbuf[:rows * cols // 16].view(rows, cols // 16),
+                           gbuf[:ng])
     if mode == "given":
         g = torch.tensor([np.float32(0.0123 * (1 + seed % 7))], dtype=torch.float32, device=xg.device)
-        got = nv().quantize(xg, "given", global_scale=g)
+        gbuf[0] = g[0]
+        got = nv().quantize(xg, "given", global_scale=gbuf[:1], out=out)
         want = ref.quantize(src, ref.GIVEN, given=float(g.item()))
     else:
-        got = nv().quantize(xg, mode)
+        got = nv().quantize(xg, mode, out=out)
         want = ref.quantize(src, ref.PER_ROW if mode == "per_row" else ref.PER_TENSOR)
     assert_quant_equal(got, want, what=f"{rows}x{cols} stride {cols + pad}")
+    assert bool((cbuf[rows * cols // 2:] == 0xA5).all()) and bool((sbuf[rows * cols // 16:] == 0x5A).all()), \
+        "bytes past the codes or scale bytes were written"
+    assert bool((gbuf[ng:] == -3.0).all()), "floats past the global scales were written"
 
 
 def _decode_linear_cases():
