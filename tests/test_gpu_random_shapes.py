@@ -139,17 +139,29 @@ def test_random_decode_linear(N, K, mode, seed):
     w = nv().quantize(wg)
     ow = ref.quantize(wg.float().cpu().numpy())
     src = xg.float().cpu().numpy()
+    # Y and the token's bytes go to the fronts of larger buffers holding a sentinel.
+    dev, guard = xg.device, 64
+    ybuf = torch.full((N + guard,), -7.0, dtype=torch.float32, device=dev)
+    cbuf = torch.full((K // 2 + guard,), 0xA5, dtype=torch.uint8, device=dev)
+    sbuf = torch.full((K // 16 + guard,), 0x5A, dtype=torch.uint8, device=dev)
+    gbuf = torch.full((1 + guard,), -3.0, dtype=torch.float32, device=dev)
+    a_out = nv().NVFP4Tensor(cbuf[:K // 2].view(1, K // 2), sbuf[:K // 16].view(1, K // 16), gbuf[:1])
     if mode == "given":
         gs = np.float32(0.004 * (1 + seed % 3))
-        y, a = nv().decode_linear(xg, w, mode="given", global_scale=torch.tensor([gs], device=xg.device),
-                                  out_dtype=torch.float32)
+        gbuf[0] = float(gs)
+        y, a = nv().decode_linear(xg, w, mode="given", global_scale=gbuf[:1], out_dtype=torch.float32,
+                                  out=ybuf[:N].view(1, N), a_out=a_out)
         oa = ref.quantize(src, ref.GIVEN, given=float(gs))
     else:
-        y, a = nv().decode_linear(xg, w, mode="per_tensor", out_dtype=torch.float32)
+        y, a = nv().decode_linear(xg, w, mode="per_tensor", out_dtype=torch.float32, out=ybuf[:N].view(1, N),
+                                  a_out=a_out)
         oa = ref.quantize(src, ref.PER_ROW)
     assert_quant_equal(a, oa, what="token")
     Y, T = ref.gemm(oa, ow)
     assert_gemm_close(y, Y, T, f"decode_linear N={N} K={K}")
+    assert bool((ybuf[N:] == -7.0).all()), "floats past Y were written"
+    assert bool((cbuf[K // 2:] == 0xA5).all()) and bool((sbuf[K // 16:] == 0x5A).all()), "token bytes overran"
+    assert bool((gbuf[1:] == -3.0).all()), "floats past the token's global scale were written"
 
 
 def _epilogue_shape(rng):
