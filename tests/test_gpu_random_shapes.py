@@ -256,3 +256,68 @@ def test_random_mxfp4(M, N, K, out_dtype, seed):
     y = nv().mxfp4_gemm(ma, mw.codes, mw.scales, (N,), mw.global_scale, out_dtype)
     Y, T = ref.mx_gemm(oma, omw)
     assert_gemm_close(y, Y, T, f"mx {M}x{N}x{K}")
+
+
+def _guarded(shape, dtype, fill, dev, guard=64):
+    """A tensor of `shape` at the front of a buffer whose `guard` trailing elements hold `fill`."""
+    n = int(np.prod(shape))
+    buf = torch.full((n + guard,), fill, dtype=dtype, device=dev)
+    return buf, buf[:n].view(*shape)
+
+
+def _tail_intact(buf, n, fill):
+    return bool((buf[n:] == fill).all())
+
+
+def _bounds_cases():
+    rng = np.random.default_rng(31)
+    cases = []
+    for i in range(12):
+        M, K = _epilogue_shape(rng)
+        widths = tuple(16 * int(rng.integers(1, 120)) for _ in range(int(rng.integers(1, 4))))
+        cases.append(pytest.param(M, K, widths, 700 + i, id=f"{M}x{K}-{'-'.join(map(str, widths))}"))
+    return cases
+
+
+@pytest.mark.parametrize("M,K,widths,seed", _bounds_cases())
+def test_random_epilogue_writes_stay_in_bounds(M, K, widths, seed):
+    """The NVFP4-output, SwiGLU and GDN-gate epilogues write their outputs into the fronts of
+    larger buffers holding a sentinel: every element past each output must survive (the values
+    are checked by the sweeps above)."""
+    dev = torch.device("cuda:0")
+    a = nv().quantize(to_gpu(workloads.activation(seed, 0, M, K)), "per_row" if seed % 2 else "per_tensor")
+    qs = [nv().quantize(to_gpu(workloads.weight(seed, 1 + i, n, K))) for i, n in enumerate(widths)]
+    wc, ws = torch.cat([q.codes for q in qs]), torch.cat([q.scales for q in qs])
+    wg = torch.cat([q.global_scale for q in qs])
+    N = sum(widths)
+    # NVFP4 output
+    cb, c = _guarded((M, N // 2), torch.uint8, 0xA5, dev)
+    sb, s = _guarded((M, N // 16), torch.uint8, 0x5A, dev)
+    yg = torch.tensor([0.01], dtype=torch.float32, device=dev)
+    nv().gemm_nvfp4_out(a, wc, ws, widths, wg, yg, out=nv().NVFP4Tensor(c, s, yg))
+    assert _tail_intact(cb, M * N // 2, 0xA5) and _tail_intact(sb, M * N // 16, 0x5A), "NVFP4 output overran"
+    # SwiGLU on the first module as gate and up (F = its width)
+    F = widths[0]
+    gcodes, gscales = nv().interleave_gate_up(qs[0], qs[0])
+    hb, h = _guarded((M, F), torch.float32, -7.0, dev)
+    hcb, hc = _guarded((M, F // 2), torch.uint8, 0xA5, dev)
+    hsb, hs = _guarded((M, F // 16), torch.uint8, 0x5A, dev)
+    nv().gemm_swiglu(a, gcodes, gscales, torch.cat([qs[0].global_scale, qs[0].global_scale]),
+                     h_dtype=torch.float32, h_global=yg, out=h, q_out=nv().NVFP4Tensor(hc, hs, yg))
+    assert _tail_intact(hb, M * F, -7.0), "SwiGLU h overran"
+    assert _tail_intact(hcb, M * F // 2, 0xA5) and _tail_intact(hsb, M * F // 16, 0x5A), "NVFP4 h overran"
+    # GDN gates on the modules plus two gate segments of H heads
+    H = 1 + seed % 40
+    gq = [nv().quantize(to_gpu(workloads.weight(seed, 10 + j, H, K, sigma=0.05))) for j in range(2)]
+    gw = tuple(widths) + (H, H)
+    gc2 = torch.cat([wc] + [q.codes for q in gq])
+    gs2 = torch.cat([ws] + [q.scales for q in gq])
+    gg2 = torch.cat([wg] + [q.global_scale for q in gq])
+    a_log = torch.linspace(-1.0, 1.0, H, device=dev)
+    dt = torch.linspace(-0.5, 0.5, H, device=dev)
+    yb, y = _guarded((M, N + 2 * H), torch.float32, -7.0, dev)
+    gb, g = _guarded((M, H), torch.float32, -7.0, dev)
+    bb, beta = _guarded((M, H), torch.float32, -7.0, dev)
+    nv().gemm_fused_gdn_gates(a, gc2, gs2, gw, gg2, a_log, dt, torch.float32, out=y, g_out=g, beta_out=beta)
+    assert _tail_intact(yb, M * (N + 2 * H), -7.0), "fused output overran"
+    assert _tail_intact(gb, M * H, -7.0) and _tail_intact(bb, M * H, -7.0), "gate outputs overran"
