@@ -974,7 +974,8 @@ def main() -> int:
     print("[bench] decode (config: X[M x K] bf16 per-token quantize + GEMM, M in {1, 4, 16})", file=sys.stderr,
           flush=True)
     decode = bench_decode(nv, args.steps, args.warmup, min(args.settle_s, 0.3))
-    decode["down"]["kernel"] = "M = 1: matrix-vector kernel; M = 4, 16: K-split decode kernel (N <= 32 x CUs)"
+    decode["down"]["kernel"] = ("M = 1: matrix-vector kernel; M = 4: K-split decode kernel on 4x4x4 MFMAs; "
+                                "M = 16: K-split decode kernel on 16x16x32 MFMAs (N <= 32 x CUs)")
     decode["up"]["kernel"] = "balanced-rows decode kernel (N > 32 x CUs)"
     print("[bench] quantize modes", file=sys.stderr, flush=True)
     qmodes = bench_quantize_modes(nv, args.steps, min(args.settle_s, 0.3))

@@ -1272,6 +1272,144 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(GemmArg
   decode_epilogue<GATES>(g, red, reinterpret_cast<float*>(lds), wave, lane, n0, n_end);
 }
 
+// M <= 4 tokens and at most 20 rows per workgroup: the K-split scheme above (the same LDS
+// rings, copies and waits), multiplied with the 16-block 4 x 4 x 4 fp16 MFMA instead of
+// 16 x 16 x 32, so that no padding row is dequantized: the workgroup's rows go in NG groups of 4
+// (4 NG >= rows) and the tokens in one group of 4.  Block b of an instruction takes K elements
+// [16b + 4f, 16b + 4f + 4) of the stage (f = 0..3 over four instructions), so lane 4b + i
+// dequantizes exactly one 16-element block (8 B of codes, one scale byte) of W row 4g + i per
+// group and stage, and lane 4b + j one block of token j, which serves all NG groups.  A and W
+// take the same K order, so every dot product is unchanged.  D of block b sits in lane 4b + j,
+// register i (W row i, token j); the 16 blocks' partial sums are added once after the loop: two
+// DPP rotations within each row of 16 lanes, then the four row sums through LDS, in a fixed
+// order.  This instruction issues far less work per cycle than 16 x 16 x 32, so it pays only
+// while the dequantization it saves dominates: more tokens or rows take gemm_decode_lds_kernel.
+template <int NG, bool GATES>
+__global__ __launch_bounds__(kDecodeThreads) void gemm_decode_q4_kernel(GemmArgs g, int rows_per_wg) {
+  constexpr int NT = 1;
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int i8 = lane >> 3;
+  const int n0 = blockIdx.x * rows_per_wg;              // rows [n0, n_end), at most 4 NG <= 32
+  const int n_end = min(n0 + rows_per_wg, g.N);
+  const uint32_t kb = (uint32_t)g.K / 2, ks = (uint32_t)g.K / 16;
+  const int nst = g.K / 256;
+  const int s0 = wave * nst / kDecodeWaves, cnt = (wave + 1) * nst / kDecodeWaves - s0;
+  uint8_t* region = lds + wave * kDlWaveBytes;
+
+  // Copies exactly as in gemm_decode_lds_kernel: chunks 0-3 hold W rows 0-31, chunks 4-5 token
+  // rows 0-15 (rows past the workgroup's last row or past M load that last row).
+  uint32_t row_codes[kDlChunks], row_scales[kDlChunks];
+#pragma unroll
+  for (int c = 0; c < kDlChunks; ++c) {
+    const int r = c < 4 ? min(8 * c + i8, n_end - 1 - n0) : min(8 * (c - 4) + i8, g.M - 1);
+    row_codes[c] = (uint32_t)r * kb;
+    row_scales[c] = (uint32_t)r * ks;
+  }
+  const uint8_t* wcb = g.w_codes + (size_t)n0 * kb;
+  const uint8_t* wsb = g.w_scales + (size_t)n0 * ks;
+  const uint32_t last_piece = ks - 16;
+  auto copy_codes = [&](int t) {
+    const uint32_t col = (uint32_t)(s0 + min(t, cnt - 1)) * 128;
+    uint8_t* dst = region + (t % kDlDepth) * kDlStageBytes;
+#pragma unroll
+    for (int c = 0; c < kDlChunks; ++c)
+      dl_copy_chunk(c < 4 ? wcb : g.a_codes, row_codes[c], col, lane, dst + c * 1024);
+  };
+  auto copy_scales = [&](int b) {
+    const uint32_t col = (uint32_t)(s0 + 8 * b) * 16;
+    uint8_t* dst = region + kDlDepth * kDlStageBytes + (b & 1) * kDlScaleBytes;
+    const uint32_t p16 = (uint32_t)(((lane & 7) ^ i8) * 16);
+#pragma unroll
+    for (int c = 0; c < kDlChunks; ++c)
+      copy16_to_lds(c < 4 ? wsb : g.a_scales, row_scales[c] + min(col + p16, last_piece), dst + c * 1024);
+  };
+
+  // Lane 4b + i: block b of the stage (16 B piece b / 2 of a row, its half b % 2), row i of a
+  // group.  Row r of the ring (W rows 0-31, then token m as row 32 + m) is row r % 8 of chunk
+  // r / 8.
+  const int bq = lane >> 2, iq = lane & 3;
+  const int piece = bq >> 1, half_off = (bq & 1) * 8;
+  f32x4_t acc[NG][NT];
+#pragma unroll
+  for (int a = 0; a < NG; ++a)
+#pragma unroll
+    for (int b = 0; b < NT; ++b) acc[a][b] = f32x4_t{};
+  if (cnt > 0) {
+    copy_scales(0);
+#pragma unroll
+    for (int t = 0; t < kDlDepth; ++t) copy_codes(t);
+    for (int t = 0; t < cnt; ++t) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDlChunks * (kDlDepth - 1)));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      const uint8_t* cs = region + (t % kDlDepth) * kDlStageBytes;
+      const uint8_t* ss = region + kDlDepth * kDlStageBytes + ((t >> 3) & 1) * kDlScaleBytes;
+      const int q = t & 7;
+      // The lane's block of ring row r, dequantized: fragment f holds its K elements [4f, 4f + 4).
+      auto block_frags = [&](int r, half4_t (&f)[4]) {
+        const uint2 c = *reinterpret_cast<const uint2*>(cs + (r >> 3) * 1024 + dl_slot(r & 7, piece) + half_off);
+        uint32_t u = (uint32_t)ss[(r >> 3) * 1024 + dl_slot(r & 7, q) + bq] << 7;   // E4M3 * 2^-8 as fp16
+        u |= u << 16;
+        const half2_t sc = __builtin_bit_cast(half2_t, u);
+        const half8_t lo = dequant8_f16(c.x, sc), hi = dequant8_f16(c.y, sc);
+        f[0] = __builtin_shufflevector(lo, lo, 0, 1, 2, 3);
+        f[1] = __builtin_shufflevector(lo, lo, 4, 5, 6, 7);
+        f[2] = __builtin_shufflevector(hi, hi, 0, 1, 2, 3);
+        f[3] = __builtin_shufflevector(hi, hi, 4, 5, 6, 7);
+      };
+      half4_t tf[NT][4];
+#pragma unroll
+      for (int b = 0; b < NT; ++b) block_frags(32 + 4 * b + iq, tf[b]);
+#pragma unroll
+      for (int a = 0; a < NG; ++a) {
+        half4_t wf[4];
+        block_frags(4 * a + iq, wf);
+#pragma unroll
+        for (int b = 0; b < NT; ++b)
+#pragma unroll
+          for (int f = 0; f < 4; ++f) acc[a][b] = __builtin_amdgcn_mfma_f32_4x4x4f16(wf[f], tf[b][f], acc[a][b], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      copy_codes(t + kDlDepth);
+      if (((t + kDlDepth) & 7) == 0) copy_scales((t + kDlDepth) >> 3);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  asm volatile("" ::: "memory");
+  // Sum over the blocks within each row of 16 lanes (lanes 4b + j, b = 4R .. 4R + 3): after the
+  // rotations by 4 and 8 every lane of row R holds that row's sum for its token j.  Lanes 16R + j
+  // (j < 4) leave the row sums in this wavefront's ring region: part[(a NT + b) 4 + i][4R + j].
+  float* part = reinterpret_cast<float*>(region);
+#pragma unroll
+  for (int a = 0; a < NG; ++a)
+#pragma unroll
+    for (int b = 0; b < NT; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = acc[a][b][i];
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, true));   // row_ror:4
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, true));   // row_ror:8
+        if ((lane & 15) < 4) part[((a * NT + b) * 4 + i) * 16 + (lane >> 4) * 4 + (lane & 3)] = v;
+      }
+  __syncthreads();
+  // The wavefront's 16 x 16 tiles in the layout the epilogue reads (W row n of group G, token m
+  // in lane n + 16 (m / 4), register m % 4): lane l takes n = l % 16 and token group l / 16.
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(lds + kDlRedOffset);
+#pragma unroll
+  for (int G = 0; G < 2; ++G) {
+    const int r = 16 * G + (lane & 15), tg = lane >> 4;
+    const int a = r >> 2, i = r & 3;
+    f32x4_t s = f32x4_t{};
+    if (a < NG && tg < NT) {
+      const f32x4_t* p = reinterpret_cast<const f32x4_t*>(part + ((a * NT + tg) * 4 + i) * 16);
+      s = ((p[0] + p[1]) + p[2]) + p[3];
+    }
+    red[(wave * 2 + G) * 64 + lane] = s;
+  }
+  decode_epilogue<GATES>(g, red, reinterpret_cast<float*>(lds), wave, lane, n0, n_end);
+}
+
 // M <= 16 tokens on MXFP4 operands with K a multiple of 512: the K-split scheme above (each
 // wavefront copies and multiplies its own contiguous range of 256-wide stages through a
 // private LDS ring: W rows 0-31 in chunks 0-3, token rows 0-15 in chunks 4-5), with the
@@ -2268,10 +2406,15 @@ int gemm_device_setup() {
       return NVFP4_ERR_HIP;
   const void* decode[] = {reinterpret_cast<const void*>(gemm_decode_lds_kernel<false>),
                           reinterpret_cast<const void*>(gemm_decode_lds_kernel<true>),
+                          reinterpret_cast<const void*>(gemm_decode_q4_kernel<4, false>),
+                          reinterpret_cast<const void*>(gemm_decode_q4_kernel<4, true>),
+                          reinterpret_cast<const void*>(gemm_decode_q4_kernel<5, false>),
+                          reinterpret_cast<const void*>(gemm_decode_q4_kernel<5, true>),
                           reinterpret_cast<const void*>(gemm_mx_decode_lds_kernel)};
   for (const void* k : decode)
     if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kDlLds) != hipSuccess)
       return NVFP4_ERR_HIP;
+
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_gemv_kernel<false>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kGvMaxLds) != hipSuccess ||
       hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_gemv_kernel<true>),
@@ -2378,7 +2521,15 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
       const int64_t share = (N + cus - 1) / cus;
       const int r = unit > 1 ? kDecodeRows : (int)std::min<int64_t>(kDecodeRows, std::max<int64_t>(16, share));
       const unsigned grid = (unsigned)((N + r - 1) / r);
-      if (gated)
+      // Up to 4 tokens and 20 rows (four or five 4-row groups) the 4 x 4 x 4 kernel dequantizes
+      // no padding and is the faster (at the MLP down projection, 5120 x 17408: 13.5-13.9
+      // against 15.6-16.0 us at M = 2-4); past that its instruction rate costs more than the
+      // padding it saves.
+      if (M <= 4 && r <= 16)
+        (gated ? gemm_decode_q4_kernel<4, true> : gemm_decode_q4_kernel<4, false>)<<<grid, kDecodeThreads, kDlLds, stream>>>(g, r);
+      else if (M <= 4 && r <= 20)
+        (gated ? gemm_decode_q4_kernel<5, true> : gemm_decode_q4_kernel<5, false>)<<<grid, kDecodeThreads, kDlLds, stream>>>(g, r);
+      else if (gated)
         gemm_decode_lds_kernel<true><<<grid, kDecodeThreads, kDlLds, stream>>>(g, r);
       else
         gemm_decode_lds_kernel<false><<<grid, kDecodeThreads, kDlLds, stream>>>(g, r);

@@ -2,7 +2,8 @@
 pick: the batch-1 matrix-vector kernel (M = 1, K % 64 == 0), the plain kernel (K % 128 != 0,
 or more than 16 tokens with K % 256 != 0), the register decode kernel (M <= 16, K % 256 != 0),
 the K-split and balanced decode kernels (M <= 16, K % 256 == 0, N on either side of one round of
-32-row workgroups) and the prefill tiles with their peeled 128 x 128 tails.  Each case is a
+32-row workgroups; the K-split kernel on 4 x 4 x 4 MFMAs for up to 4 tokens and N <= 20 x CUs) and
+the prefill tiles with their peeled 128 x 128 tails.  Each case is a
 fused launch of 1-4 modules with their own global scales (one module: the plain GEMM), per-
 tensor or per-row activation scales and fp32 or bf16 output, checked element by element against
 the oracle's fused GEMM with the per-element bound of the other parity tests.  The other entry
@@ -31,6 +32,8 @@ def _cases():
         ("K-split decode", (2, 16), (1, 900), [256, 512, 1280, 2304]),
         ("balanced decode", (1, 16), (8193, 9400), [256, 512]),
         ("prefill tiles", (17, 300), (1, 700), [256, 512, 768]),
+        # up to 4 tokens and N <= 20 x CUs: the K-split kernel on 4 x 4 x 4 MFMAs
+        ("small-batch decode", (2, 4), (1, 5120), [256, 512, 1280, 2304]),
     ]
     for name, (m0, m1), (n0, n1), ks in classes:
         for _ in range(10):

@@ -8,9 +8,10 @@ through all 127 bytes, so every output element is the product of exactly one A b
 W byte: a byte that a kernel decoded wrongly (a subnormal flushed to zero, say) changes whole
 output rows or columns by far more than the tolerance 1e-4 * sum_k |a_k w_k| (plus half a bf16
 ulp for bf16 output).  Every pair of bytes meets in every kernel family: the prefill kernel's
-256 x 256 tiles and its peeled 128 x 128 tiles, the K-split, balanced (three to five row groups,
-and the SwiGLU pairs) and register decode kernels, the plain kernel; fp32 and bf16 output, and
-the NVFP4-output, GDN gate and SwiGLU epilogues.
+256 x 256 tiles and its peeled 128 x 128 tiles, the K-split decode kernel on 16 x 16 x 32 MFMAs
+and on 4 x 4 x 4 MFMAs (up to 4 tokens, four or five 4-row groups), the balanced (three to five
+row groups, and the SwiGLU pairs) and register decode kernels, the plain kernel; fp32 and bf16
+output, and the NVFP4-output, GDN gate and SwiGLU epilogues.
 
 Codes are seeded random bytes and the same bytes go to the GPU and the oracle.  With K = 256
 every partial sum is an integer multiple of 2^(e-8) below 2^24 units, so the kernel's fp32
@@ -85,6 +86,19 @@ def test_decode_kernels_every_byte(N, K):
         _check_store(oa, ow, f"decode N={N} K={K} launch {j}")
 
 
+# Up to 4 tokens with at most 20 rows per workgroup (N <= 20 x CUs): the K-split kernel on
+# 4 x 4 x 4 MFMAs, with four row groups (N = 1000: 16 rows per workgroup on 256 CUs) and five
+# (N = 4700: 19 rows, so the last group holds three real rows).  3 and 4 tokens per launch.
+@pytest.mark.parametrize("N,M", [(1000, 4), (4700, 3)])
+def test_small_batch_decode_every_byte(N, M):
+    K = 256
+    ow = _operand(70 + N, N, K, 3, [1.25])
+    oas = [_a_operand(71 + N + j, M, K, M * j, True) for j in range((NBYTES + M - 1) // M)]
+    _assert_all_pairs(oas, ow)
+    for j, oa in enumerate(oas):
+        _check_store(oa, ow, f"small-batch decode N={N} M={M} launch {j}")
+
+
 @pytest.mark.parametrize("M", [16, 127])
 def test_plain_kernel_every_byte(M):
     # K % 128 != 0: the plain kernel, for decode-sized and larger M.
@@ -140,7 +154,7 @@ def _check_gates(oa, ows, what):
     assert_gates_close(g, beta, Y, T, H, a_log, dt, g_o, beta_o, what)
 
 
-@pytest.mark.parametrize("M", [200, 16])
+@pytest.mark.parametrize("M", [200, 16, 4])
 def test_gates_every_byte(M):
     # Three segments: 381 plain columns, then the two 127-wide gate projections; each gate
     # column has its own byte, so every byte reaches both gate functions.
