@@ -1272,18 +1272,18 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(GemmArg
   decode_epilogue<GATES>(g, red, reinterpret_cast<float*>(lds), wave, lane, n0, n_end);
 }
 
-// M <= 4 tokens and at most 20 rows per workgroup: the K-split scheme above (the same LDS
-// rings, copies and waits), multiplied with the 16-block 4 x 4 x 4 fp16 MFMA instead of
-// 16 x 16 x 32, so that no padding row is dequantized: the workgroup's rows go in NG groups of 4
-// (4 NG >= rows) and the tokens in one group of 4.  Block b of an instruction takes K elements
-// [16b + 4f, 16b + 4f + 4) of the stage (f = 0..3 over four instructions), so lane 4b + i
-// dequantizes exactly one 16-element block (8 B of codes, one scale byte) of W row 4g + i per
-// group and stage, and lane 4b + j one block of token j, which serves all NG groups.  A and W
-// take the same K order, so every dot product is unchanged.  D of block b sits in lane 4b + j,
-// register i (W row i, token j); the 16 blocks' partial sums are added once after the loop: two
-// DPP rotations within each row of 16 lanes, then the four row sums through LDS, in a fixed
-// order.  This instruction issues far less work per cycle than 16 x 16 x 32, so it pays only
-// while the dequantization it saves dominates: more tokens or rows take gemm_decode_lds_kernel.
+// M <= 4 tokens and at most 20 rows per workgroup: the K-split scheme above (the same LDS ring
+// layout and copies, minus the chunks of padding rows), multiplied with the 16-block 4 x 4 x 4 fp16
+// MFMA instead of 16 x 16 x 32, so that no padding row is dequantized: the workgroup's rows go in
+// NG groups of 4 (4 NG >= rows) and the tokens in one group of 4.  Block b of an instruction takes
+// K elements [16b + 4f, 16b + 4f + 4) of the stage (f = 0..3 over four instructions), so lane 4b +
+// i dequantizes exactly one 16-element block (8 B of codes, one scale byte) of W row 4g + i per
+// group and stage, and lane 4b + j one block of token j, which serves all NG groups.  A and W take
+// the same K order, so every dot product is unchanged.  D of block b sits in lane 4b + j, register
+// i (W row i, token j); the 16 blocks' partial sums are added once after the loop: two DPP
+// rotations within each row of 16 lanes, then the four row sums through LDS, in a fixed order.
+// This instruction issues far less work per cycle than 16 x 16 x 32, so it pays only while the
+// dequantization it saves dominates: more tokens or rows take gemm_decode_lds_kernel.
 template <int NG, bool GATES>
 __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_q4_kernel(GemmArgs g, int rows_per_wg) {
   constexpr int NT = 1;
@@ -1297,12 +1297,16 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_q4_kernel(GemmArgs
   const int s0 = wave * nst / kDecodeWaves, cnt = (wave + 1) * nst / kDecodeWaves - s0;
   uint8_t* region = lds + wave * kDlWaveBytes;
 
-  // Copies exactly as in gemm_decode_lds_kernel: chunks 0-3 hold W rows 0-31, chunks 4-5 token
-  // rows 0-15 (rows past the workgroup's last row or past M load that last row).
-  uint32_t row_codes[kDlChunks], row_scales[kDlChunks];
+  // The ring layout of gemm_decode_lds_kernel (chunk c of a stage at c KB: W rows 8c .. 8c + 7
+  // for c < 4, token rows 0-7 in chunk 4), but only the chunks this kernel reads are copied: the
+  // W chunks of rows 0 .. 4 NG - 1 and token chunk 4 (rows past the workgroup's last row or
+  // past M load that last row).  NC copies per stage and per scale block.
+  constexpr int kWChunks = (4 * NG + 7) / 8, NC = kWChunks + 1;
+  auto chunk_of = [](int c) { return c < kWChunks ? c : 4; };
+  uint32_t row_codes[NC], row_scales[NC];
 #pragma unroll
-  for (int c = 0; c < kDlChunks; ++c) {
-    const int r = c < 4 ? min(8 * c + i8, n_end - 1 - n0) : min(8 * (c - 4) + i8, g.M - 1);
+  for (int c = 0; c < NC; ++c) {
+    const int r = c < kWChunks ? min(8 * c + i8, n_end - 1 - n0) : min(i8, g.M - 1);
     row_codes[c] = (uint32_t)r * kb;
     row_scales[c] = (uint32_t)r * ks;
   }
@@ -1313,16 +1317,17 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_q4_kernel(GemmArgs
     const uint32_t col = (uint32_t)(s0 + min(t, cnt - 1)) * 128;
     uint8_t* dst = region + (t % kDlDepth) * kDlStageBytes;
 #pragma unroll
-    for (int c = 0; c < kDlChunks; ++c)
-      dl_copy_chunk(c < 4 ? wcb : g.a_codes, row_codes[c], col, lane, dst + c * 1024);
+    for (int c = 0; c < NC; ++c)
+      dl_copy_chunk(c < kWChunks ? wcb : g.a_codes, row_codes[c], col, lane, dst + chunk_of(c) * 1024);
   };
   auto copy_scales = [&](int b) {
     const uint32_t col = (uint32_t)(s0 + 8 * b) * 16;
     uint8_t* dst = region + kDlDepth * kDlStageBytes + (b & 1) * kDlScaleBytes;
     const uint32_t p16 = (uint32_t)(((lane & 7) ^ i8) * 16);
 #pragma unroll
-    for (int c = 0; c < kDlChunks; ++c)
-      copy16_to_lds(c < 4 ? wsb : g.a_scales, row_scales[c] + min(col + p16, last_piece), dst + c * 1024);
+    for (int c = 0; c < NC; ++c)
+      copy16_to_lds(c < kWChunks ? wsb : g.a_scales, row_scales[c] + min(col + p16, last_piece),
+                    dst + chunk_of(c) * 1024);
   };
 
   // Lane 4b + i: block b of the stage (16 B piece b / 2 of a row, its half b % 2), row i of a
@@ -1340,7 +1345,9 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_q4_kernel(GemmArgs
 #pragma unroll
     for (int t = 0; t < kDlDepth; ++t) copy_codes(t);
     for (int t = 0; t < cnt; ++t) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDlChunks * (kDlDepth - 1)));
+      // Stage t's copies and its scale block are older than the NC (kDlDepth - 1) copies of the
+      // next stages.
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(NC * (kDlDepth - 1)));
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       const uint8_t* cs = region + (t % kDlDepth) * kDlStageBytes;
@@ -2522,9 +2529,9 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
       const int r = unit > 1 ? kDecodeRows : (int)std::min<int64_t>(kDecodeRows, std::max<int64_t>(16, share));
       const unsigned grid = (unsigned)((N + r - 1) / r);
       // Up to 4 tokens and 20 rows (four or five 4-row groups) the 4 x 4 x 4 kernel dequantizes
-      // no padding and is the faster (at the MLP down projection, 5120 x 17408: 13.5-13.9
-      // against 15.6-16.0 us at M = 2-4); past that its instruction rate costs more than the
-      // padding it saves.
+      // no padding and copies no padding chunk, and is the faster (at the MLP down projection,
+      // 5120 x 17408: 12.6-12.9 against 15.6-16.0 us at M = 2-4); past that its instruction
+      // rate costs more than the padding it saves.
       if (M <= 4 && r <= 16)
         (gated ? gemm_decode_q4_kernel<4, true> : gemm_decode_q4_kernel<4, false>)<<<grid, kDecodeThreads, kDlLds, stream>>>(g, r);
       else if (M <= 4 && r <= 20)
