@@ -1191,7 +1191,7 @@ __device__ __forceinline__ void dl_copy_chunk(const uint8_t* base, uint32_t row_
   copy16_to_lds(base, row_off + col + p * 16, dst);
 }
 
-template <bool GATES>
+template <int WC, int TC, bool GATES>
 __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(GemmArgs g, int rows_per_wg) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -1203,11 +1203,17 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(GemmArg
   const int s0 = wave * nst / kDecodeWaves, cnt = (wave + 1) * nst / kDecodeWaves - s0;
   uint8_t* region = lds + wave * kDlWaveBytes;
 
-  // Per-lane row offsets of the rows this lane copies (row i8 of each chunk), clamped.
-  uint32_t row_codes[kDlChunks], row_scales[kDlChunks];
+  // Only the chunks that hold real rows are copied: W chunks 0 .. WC - 1 (WC = ceil(rows / 8))
+  // and token chunks 4 .. 3 + TC (TC = ceil(M / 8)), NC copies per stage and per scale block.
+  // The multiplies below read every chunk; what a chunk that is not copied holds reaches only
+  // the outputs of padding rows and tokens, which are never stored.  Per-lane row offsets of the
+  // rows this lane copies (row i8 of each chunk), clamped.
+  constexpr int NC = WC + TC;
+  auto chunk_of = [](int c) { return c < WC ? c : 4 + (c - WC); };
+  uint32_t row_codes[NC], row_scales[NC];
 #pragma unroll
-  for (int c = 0; c < kDlChunks; ++c) {
-    const int r = c < 4 ? min(8 * c + i8, n_end - 1 - n0) : min(8 * (c - 4) + i8, g.M - 1);
+  for (int c = 0; c < NC; ++c) {
+    const int r = c < WC ? min(8 * c + i8, n_end - 1 - n0) : min(8 * (c - WC) + i8, g.M - 1);
     row_codes[c] = (uint32_t)r * kb;
     row_scales[c] = (uint32_t)r * ks;
   }
@@ -1218,16 +1224,17 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(GemmArg
     const uint32_t col = (uint32_t)(s0 + min(t, cnt - 1)) * 128;
     uint8_t* dst = region + (t % kDlDepth) * kDlStageBytes;
 #pragma unroll
-    for (int c = 0; c < kDlChunks; ++c)
-      dl_copy_chunk(c < 4 ? wcb : g.a_codes, row_codes[c], col, lane, dst + c * 1024);
+    for (int c = 0; c < NC; ++c)
+      dl_copy_chunk(c < WC ? wcb : g.a_codes, row_codes[c], col, lane, dst + chunk_of(c) * 1024);
   };
   auto copy_scales = [&](int b) {     // scale bytes of stages 8b .. 8b + 7 of this wavefront
     const uint32_t col = (uint32_t)(s0 + 8 * b) * 16;
     uint8_t* dst = region + kDlDepth * kDlStageBytes + (b & 1) * kDlScaleBytes;
     const uint32_t p16 = (uint32_t)(((lane & 7) ^ i8) * 16);
 #pragma unroll
-    for (int c = 0; c < kDlChunks; ++c)   // pieces past the row's end (never read) clamped in bounds
-      copy16_to_lds(c < 4 ? wsb : g.a_scales, row_scales[c] + min(col + p16, last_piece), dst + c * 1024);
+    for (int c = 0; c < NC; ++c)   // pieces past the row's end (never read) clamped in bounds
+      copy16_to_lds(c < WC ? wsb : g.a_scales, row_scales[c] + min(col + p16, last_piece),
+                    dst + chunk_of(c) * 1024);
   };
 
   f32x4_t acc0 = f32x4_t{}, acc1 = f32x4_t{};
@@ -1237,9 +1244,9 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(GemmArg
     for (int t = 0; t < kDlDepth; ++t) copy_codes(t);
     const int iw = rr & 7;
     for (int t = 0; t < cnt; ++t) {
-      // Stage t's copies (and its scale block) are older than the 6 (kDlDepth - 1) copies of
+      // Stage t's copies (and its scale block) are older than the NC (kDlDepth - 1) copies of
       // the next stages: at most that many may still be in flight.
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDlChunks * (kDlDepth - 1)));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(NC * (kDlDepth - 1)));
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       const uint8_t* cs = region + (t % kDlDepth) * kDlStageBytes;
@@ -1415,6 +1422,20 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_q4_kernel(GemmArgs
     red[(wave * 2 + G) * 64 + lane] = s;
   }
   decode_epilogue<GATES>(g, red, reinterpret_cast<float*>(lds), wave, lane, n0, n_end);
+}
+
+// The instantiation of gemm_decode_lds_kernel that copies WC W chunks (2 to 4: 16 to 32 rows) and
+// TC token chunks (1 or 2: up to 8 or 16 tokens).
+typedef void (*DecodeLdsKernel)(GemmArgs, int);
+DecodeLdsKernel decode_lds_kernel(bool gated, int wc, int tc) {
+  static constexpr DecodeLdsKernel k[2][3][2] = {
+      {{gemm_decode_lds_kernel<2, 1, false>, gemm_decode_lds_kernel<2, 2, false>},
+       {gemm_decode_lds_kernel<3, 1, false>, gemm_decode_lds_kernel<3, 2, false>},
+       {gemm_decode_lds_kernel<4, 1, false>, gemm_decode_lds_kernel<4, 2, false>}},
+      {{gemm_decode_lds_kernel<2, 1, true>, gemm_decode_lds_kernel<2, 2, true>},
+       {gemm_decode_lds_kernel<3, 1, true>, gemm_decode_lds_kernel<3, 2, true>},
+       {gemm_decode_lds_kernel<4, 1, true>, gemm_decode_lds_kernel<4, 2, true>}}};
+  return k[gated][wc - 2][tc - 1];
 }
 
 // M <= 16 tokens on MXFP4 operands with K a multiple of 512: the K-split scheme above (each
@@ -2411,9 +2432,13 @@ int gemm_device_setup() {
   for (const void* k : tiles)
     if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kPrefillLds) != hipSuccess)
       return NVFP4_ERR_HIP;
-  const void* decode[] = {reinterpret_cast<const void*>(gemm_decode_lds_kernel<false>),
-                          reinterpret_cast<const void*>(gemm_decode_lds_kernel<true>),
-                          reinterpret_cast<const void*>(gemm_decode_q4_kernel<4, false>),
+  for (int gated = 0; gated < 2; ++gated)
+    for (int wc = 2; wc <= 4; ++wc)
+      for (int tc = 1; tc <= 2; ++tc)
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(decode_lds_kernel(gated, wc, tc)),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kDlLds) != hipSuccess)
+          return NVFP4_ERR_HIP;
+  const void* decode[] = {reinterpret_cast<const void*>(gemm_decode_q4_kernel<4, false>),
                           reinterpret_cast<const void*>(gemm_decode_q4_kernel<4, true>),
                           reinterpret_cast<const void*>(gemm_decode_q4_kernel<5, false>),
                           reinterpret_cast<const void*>(gemm_decode_q4_kernel<5, true>),
@@ -2536,10 +2561,8 @@ int launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const u
         (gated ? gemm_decode_q4_kernel<4, true> : gemm_decode_q4_kernel<4, false>)<<<grid, kDecodeThreads, kDlLds, stream>>>(g, r);
       else if (M <= 4 && r <= 20)
         (gated ? gemm_decode_q4_kernel<5, true> : gemm_decode_q4_kernel<5, false>)<<<grid, kDecodeThreads, kDlLds, stream>>>(g, r);
-      else if (gated)
-        gemm_decode_lds_kernel<true><<<grid, kDecodeThreads, kDlLds, stream>>>(g, r);
       else
-        gemm_decode_lds_kernel<false><<<grid, kDecodeThreads, kDlLds, stream>>>(g, r);
+        decode_lds_kernel(gated, (r + 7) / 8, M <= 8 ? 1 : 2)<<<grid, kDecodeThreads, kDlLds, stream>>>(g, r);
     } else {
       if (swiglu && groups % 2 != 0) return NVFP4_ERR_UNSUPPORTED;   // not reached: rows % 32 == 0
       switch (groups) {

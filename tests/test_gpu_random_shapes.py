@@ -34,6 +34,8 @@ def _cases():
         ("prefill tiles", (17, 300), (1, 700), [256, 512, 768]),
         # up to 4 tokens and N <= 20 x CUs: the K-split kernel on 4 x 4 x 4 MFMAs
         ("small-batch decode", (2, 4), (1, 5120), [256, 512, 1280, 2304]),
+        # 5 to 8 tokens: the 16 x 16 x 32 K-split kernel copying one token chunk
+        ("mid-batch decode", (5, 8), (1, 8192), [256, 512, 1280]),
     ]
     for name, (m0, m1), (n0, n1), ks in classes:
         for _ in range(10):

@@ -89,7 +89,9 @@ def test_decode_kernels_every_byte(N, K):
 # Up to 4 tokens with at most 20 rows per workgroup (N <= 20 x CUs): the K-split kernel on
 # 4 x 4 x 4 MFMAs, with four row groups (N = 1000: 16 rows per workgroup on 256 CUs) and five
 # (N = 4700: 19 rows, so the last group holds three real rows).  3 and 4 tokens per launch.
-@pytest.mark.parametrize("N,M", [(1000, 4), (4700, 3)])
+# 5 to 8 tokens: the 16 x 16 x 32 K-split kernel copying one token chunk, with three W chunks
+# (N = 6000: 24 rows per workgroup on 256 CUs) and four (N = 8000: 32 rows).
+@pytest.mark.parametrize("N,M", [(1000, 4), (4700, 3), (6000, 8), (8000, 6)])
 def test_small_batch_decode_every_byte(N, M):
     K = 256
     ow = _operand(70 + N, N, K, 3, [1.25])
