@@ -55,6 +55,39 @@ def test_decode(M, a_mode):
     assert_gemm_close(y, Y, T, f"decode M={M}")
 
 
+def _raw_values(t):
+    """E2M1(code) * E4M3(scale) per element, without the global scale (exact in binary32)."""
+    v = ref.e2m1_decode(ref.unpack_codes(t.codes)).astype(np.float32)
+    return v * np.repeat(ref.e4m3_decode(t.scales).astype(np.float32), 16, axis=1)
+
+
+# Decode where the kernels' fp32 accumulation rounds: 1 % of the token's channels x50 and weight
+# blocks scaled by 2^((k / 16) mod 7), so the block scales of a row span six binades more than the
+# Gaussian cases, where every partial sum is exactly representable in fp32.  The shapes reach the
+# 4 x 4 x 4 kernel (M <= 4, five and four row groups on 256 CUs) and the 16 x 16 x 32 K-split
+# kernel copying one token chunk (M = 6, 8) and two (M = 16).
+@pytest.mark.parametrize("M,N,K", [(4, 5120, 17408), (3, 4700, 4096), (8, 6000, 2560), (6, 8000, 1280),
+                                   (16, 5120, 4096)])
+def test_decode_inexact_accumulation(M, N, K):
+    x = workloads.activation(77, M, M, K, outlier_frac=0.01)
+    gain = np.exp2((np.arange(K) // 16) % 7).astype(np.float32)
+    w = workloads.weight(77, 1, N, K) * gain[None, :]
+    a, q, oa, ow = _quant_pair(x, w, "per_row")
+    # Precondition, on the host: a sequential fp32 sum of these operands differs from the exact
+    # sum somewhere, so exactness of the accumulation cannot hide an ordering or reduction error.
+    ra, rw = _raw_values(oa), _raw_values(ow)
+    cols = np.arange(0, N, max(1, N // 64))
+    acc = np.zeros((M, cols.size), np.float32)
+    for k in range(K):
+        acc += ra[:, k:k + 1] * rw[cols, k][None, :]
+    exact = ra.astype(np.float64) @ rw[cols].astype(np.float64).T
+    assert np.any(acc.astype(np.float64) != exact), "the fp32 accumulation is exact for these operands"
+    for out_dtype in (torch.float32, torch.bfloat16):
+        y = nv().gemm(a, q, out_dtype)
+        Y, T = ref.gemm(oa, ow)
+        assert_gemm_close(y, Y, T, f"inexact decode M={M} N={N} K={K} {out_dtype}")
+
+
 @pytest.fixture(scope="module")
 def decode_up_weight():
     """The MLP up projection's weight at decode (17408 x 5120), quantized on the GPU and by the
