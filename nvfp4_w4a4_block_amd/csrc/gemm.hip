@@ -1447,6 +1447,7 @@ DecodeLdsKernel decode_lds_kernel(bool gated, int wc, int tc) {
 // 16-byte aligned.  Lane (r, h) multiplies MX block 4h + c of the stage in chunk c for W row r
 // and token row r mod 16 (lanes 16-31 read the same LDS rows as 0-15; their outputs are not
 // stored), with the stage's scale dword at byte 4h of its 8.
+template <int WC, int TC>
 __global__ __launch_bounds__(kDecodeThreads) void gemm_mx_decode_lds_kernel(GemmArgs g, int rows_per_wg) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -1458,10 +1459,16 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_mx_decode_lds_kernel(Gemm
   const int s0 = 2 * (wave * pairs / kDecodeWaves), cnt = 2 * ((wave + 1) * pairs / kDecodeWaves) - s0;
   uint8_t* region = lds + wave * kDlWaveBytes;
 
-  uint32_t row_codes[kDlChunks], row_scales[kDlChunks];
+  // As in gemm_decode_lds_kernel, only the chunks that hold real rows are copied: W chunks
+  // 0 .. WC - 1 and token chunks 4 .. 3 + TC, NC copies per stage and per scale block; the
+  // multiplies read every chunk, and what an uncopied chunk holds reaches only outputs that are
+  // never stored.
+  constexpr int NC = WC + TC;
+  auto chunk_of = [](int c) { return c < WC ? c : 4 + (c - WC); };
+  uint32_t row_codes[NC], row_scales[NC];
 #pragma unroll
-  for (int c = 0; c < kDlChunks; ++c) {
-    const int rw = c < 4 ? min(8 * c + i8, n_end - 1 - n0) : min(8 * (c - 4) + i8, g.M - 1);
+  for (int c = 0; c < NC; ++c) {
+    const int rw = c < WC ? min(8 * c + i8, n_end - 1 - n0) : min(8 * (c - WC) + i8, g.M - 1);
     row_codes[c] = (uint32_t)rw * kb;
     row_scales[c] = (uint32_t)rw * kx;
   }
@@ -1472,16 +1479,17 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_mx_decode_lds_kernel(Gemm
     const uint32_t col = (uint32_t)(s0 + min(t, cnt - 1)) * 128;
     uint8_t* dst = region + (t % kDlDepth) * kDlStageBytes;
 #pragma unroll
-    for (int c = 0; c < kDlChunks; ++c)
-      dl_copy_chunk(c < 4 ? wcb : g.a_codes, row_codes[c], col, lane, dst + c * 1024);
+    for (int c = 0; c < NC; ++c)
+      dl_copy_chunk(c < WC ? wcb : g.a_codes, row_codes[c], col, lane, dst + chunk_of(c) * 1024);
   };
   auto copy_scales = [&](int b) {     // scale bytes of stages 16b .. 16b + 15 of this wavefront
     const uint32_t col = (uint32_t)(s0 + 16 * b) * 8;
     uint8_t* dst = region + kDlDepth * kDlStageBytes + (b & 1) * kDlScaleBytes;
     const uint32_t p16 = (uint32_t)(((lane & 7) ^ i8) * 16);
 #pragma unroll
-    for (int c = 0; c < kDlChunks; ++c)   // pieces past the row's end (never read) clamped in bounds
-      copy16_to_lds(c < 4 ? wxb : g.a_scales, row_scales[c] + min(col + p16, last_piece), dst + c * 1024);
+    for (int c = 0; c < NC; ++c)   // pieces past the row's end (never read) clamped in bounds
+      copy16_to_lds(c < WC ? wxb : g.a_scales, row_scales[c] + min(col + p16, last_piece),
+                    dst + chunk_of(c) * 1024);
   };
 
   f32x16_t acc = f32x16_t{};
@@ -1491,9 +1499,9 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_mx_decode_lds_kernel(Gemm
     for (int t = 0; t < kDlDepth; ++t) copy_codes(t);
     const int iw = r & 7, wch = r >> 3, ach = 4 + ((r & 15) >> 3);
     for (int t = 0; t < cnt; ++t) {
-      // Stage t's copies (and its scale block) are older than the copies of the next
-      // kDlDepth - 1 stages: at most that many may still be in flight.
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDlChunks * (kDlDepth - 1)));
+      // Stage t's copies (and its scale block) are older than the NC (kDlDepth - 1) copies of
+      // the next stages: at most that many may still be in flight.
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(NC * (kDlDepth - 1)));
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       const uint8_t* cs = region + (t % kDlDepth) * kDlStageBytes;
@@ -1542,6 +1550,16 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_mx_decode_lds_kernel(Gemm
       }
     }
   }
+}
+
+// The instantiation of gemm_mx_decode_lds_kernel that copies WC W chunks (2 to 4) and TC token
+// chunks (1 or 2).
+DecodeLdsKernel mx_decode_lds_kernel(int wc, int tc) {
+  static constexpr DecodeLdsKernel k[3][2] = {
+      {gemm_mx_decode_lds_kernel<2, 1>, gemm_mx_decode_lds_kernel<2, 2>},
+      {gemm_mx_decode_lds_kernel<3, 1>, gemm_mx_decode_lds_kernel<3, 2>},
+      {gemm_mx_decode_lds_kernel<4, 1>, gemm_mx_decode_lds_kernel<4, 2>}};
+  return k[wc - 2][tc - 1];
 }
 
 // ------------------------------------------------------------------ decode, balanced rows
@@ -2432,17 +2450,17 @@ int gemm_device_setup() {
   for (const void* k : tiles)
     if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kPrefillLds) != hipSuccess)
       return NVFP4_ERR_HIP;
-  for (int gated = 0; gated < 2; ++gated)
-    for (int wc = 2; wc <= 4; ++wc)
-      for (int tc = 1; tc <= 2; ++tc)
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(decode_lds_kernel(gated, wc, tc)),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kDlLds) != hipSuccess)
+  for (int wc = 2; wc <= 4; ++wc)
+    for (int tc = 1; tc <= 2; ++tc)
+      for (const DecodeLdsKernel k : {decode_lds_kernel(false, wc, tc), decode_lds_kernel(true, wc, tc),
+                                      mx_decode_lds_kernel(wc, tc)})
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kDlLds) != hipSuccess)
           return NVFP4_ERR_HIP;
   const void* decode[] = {reinterpret_cast<const void*>(gemm_decode_q4_kernel<4, false>),
                           reinterpret_cast<const void*>(gemm_decode_q4_kernel<4, true>),
                           reinterpret_cast<const void*>(gemm_decode_q4_kernel<5, false>),
-                          reinterpret_cast<const void*>(gemm_decode_q4_kernel<5, true>),
-                          reinterpret_cast<const void*>(gemm_mx_decode_lds_kernel)};
+                          reinterpret_cast<const void*>(gemm_decode_q4_kernel<5, true>)};
   for (const void* k : decode)
     if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kDlLds) != hipSuccess)
       return NVFP4_ERR_HIP;
@@ -2631,7 +2649,7 @@ int launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, cons
     // whole extra workgroup in a short last round.
     const int64_t rounds = (N + 32 * cus - 1) / (32 * cus);
     const int r = (int)std::min<int64_t>(32, std::max<int64_t>(16, (N + cus * rounds - 1) / (cus * rounds)));
-    gemm_mx_decode_lds_kernel<<<(unsigned)((N + r - 1) / r), kDecodeThreads, kDlLds, stream>>>(g, r);
+    mx_decode_lds_kernel((r + 7) / 8, M <= 8 ? 1 : 2)<<<(unsigned)((N + r - 1) / r), kDecodeThreads, kDlLds, stream>>>(g, r);
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
   }
   if (M <= 16) {
